@@ -1,0 +1,173 @@
+/*
+ * pa_verify.h — C ABI of libpa_verify.so: paged attention for the verify step
+ * of speculative decoding on MI355X (gfx950).
+ *
+ * What the operation computes.  A batch holds num_seqs sequences.  Sequence s
+ * brings T_s = subsequence_begins[s+1] - subsequence_begins[s] new query
+ * tokens (1 <= T_s <= 4) on top of past_len L_s = past_lens[s] cached tokens.
+ * The paged KV cache already holds all L_s + T_s tokens of the sequence.  New
+ * token i (0-based within its sequence) attends to cache positions
+ * [lo_i, L_s + i + 1), with lo_i = 0 for a full-causal layer and
+ * lo_i = max(0, L_s + i + 1 - W) for a sliding-window layer of window W
+ * (the window counts the token itself).  Per query head h the result is
+ *
+ *     out[n, h, :] = sum_t softmax_t(scale * <q[n, h, :], k_t>) * v_t
+ *
+ * over those positions, where KV head floor(h / (Hq / Hkv)) serves q head h.
+ *
+ * Sources (cited by page title and section):
+ *  - The per-token key limit past_len + i + 1, the op metadata (past_lens,
+ *    subsequence_begins, max_context_len, one block table per sequence) and a
+ *    u8 KV cache with f16 compute: OpenVINO issue #38153 "[GPU] PagedAttention
+ *    with 2-4 query tokens per sequence (speculative decoding verify) is ~8x
+ *    slower than single-token decode", sections "Performance issue
+ *    description" and "Step-by-step reproduction".
+ *  - The KV scan split into segments reduced in parallel, and segment buffers
+ *    that must be sized per query token, not per sequence: the vLLM article
+ *    "speculative decoding net loss" (dual-radeon-vllm), passages on the
+ *    use_3d gate, the segment-buffer geometry and vllm#45450.
+ *  - The sliding window of 1024 and page size 64 of the SWA-hybrid model:
+ *    SGLang discussion #36314 "FROZEN_KV_MTP slower than no-spec on Gemma 4
+ *    (SWA hybrid)", sections "Environment" and "Observation 3".
+ *  - Graph replay must stay intact (no allocation, no host sync in a call):
+ *    the same vLLM article, torch-profiler trace passage (hipGraphLaunch).
+ *
+ * Memory layouts (all row-major, contiguous, caller-owned device memory):
+ *  q, out        [num_tokens, Hq, D]            f16 or bf16 (out dtype == q dtype)
+ *  k_cache       [num_blocks, Hkv, block_size, D]     one page tile per (block, head)
+ *  v_cache       [num_blocks, Hkv, D, block_size]     V pages are stored d-major
+ *                (transposed) so that the PV contraction over keys reads
+ *                keys contiguously; see DESIGN notes in the library source.
+ *  k_scale_zp,   [num_blocks, Hkv, block_size, 2]     f16 (scale, zero_point) per
+ *  v_scale_zp    token per KV head, u8 variant only; dequant = (u - zp) * scale
+ *  block_tables  [num_seqs, max_blocks_per_seq] int32 physical block ids
+ *  past_lens     [num_seqs] int32
+ *  subsequence_begins [num_seqs + 1] int32, cumulative, [0] == 0,
+ *                [num_seqs] == num_tokens
+ *
+ * Ownership and behaviour.  The library never allocates, frees or retains a
+ * pointer past the call and never synchronises (except pa_verify_read_status).
+ * A forward call enqueues exactly two kernels (segment kernel, then combine
+ * kernel) on params->stream, so it can be captured in a HIP graph.  Calls are
+ * stateless and thread-safe; calls that share one workspace must be ordered
+ * on one stream.  No C++ exception crosses this ABI.
+ *
+ * Errors.  Host-checkable problems return a nonzero pa_status before anything
+ * is enqueued and leave `out` untouched.  Problems that only the device can see
+ * (T_s outside [1,4], L_s < 0, L_s + T_s > max_context_len, a physical block id
+ * outside [0, num_blocks), non-monotone subsequence_begins) set the sticky
+ * device status word PA_ERR_DEVICE_CONTRACT in the workspace and make the
+ * affected sequence's output rows NaN; pa_verify_read_status reports it.
+ */
+#ifndef PA_VERIFY_H
+#define PA_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,      /* null pointer, non-positive size, inconsistent sizes */
+  PA_ERR_UNSUPPORTED = 2,      /* valid but not built: D, block_size, group size, dtype combo */
+  PA_ERR_WORKSPACE = 3,        /* workspace missing or smaller than pa_verify_workspace_bytes */
+  PA_ERR_HIP = 4,              /* a HIP runtime call or kernel launch failed */
+  PA_ERR_DEVICE_CONTRACT = 5   /* device-side metadata violated the contract (see above) */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F16 = 0,
+  PA_BF16 = 1,
+  PA_U8 = 2   /* KV only: asymmetric per-token per-KV-head u8 with f16 scale and zero point */
+} pa_dtype;
+
+/* Sizes and options of one call.  Supported: head_dim in {64, 128, 256},
+ * block_size in {16, 32, 64}, group size Hq/Hkv in {1, 2, 4, 8} with
+ * group * max T_s <= 16 enforced per sequence on the device, dtype pairs
+ * (q, kv) = (f16, f16), (bf16, bf16), (f16, u8), (bf16, u8). */
+typedef struct pa_verify_params {
+  int32_t num_seqs;            /* sequences in the batch, >= 1 */
+  int32_t num_tokens;          /* == subsequence_begins[num_seqs], >= num_seqs */
+  int32_t num_q_heads;         /* Hq */
+  int32_t num_kv_heads;        /* Hkv, divides Hq */
+  int32_t head_dim;            /* D */
+  int32_t block_size;          /* tokens per page */
+  int32_t num_blocks;          /* physical pages in the pool (device bounds check) */
+  int32_t max_blocks_per_seq;  /* row stride of block_tables; >= ceil(max_context_len / block_size) */
+  int32_t sliding_window;      /* W; 0 = full causal */
+  int32_t num_segments;        /* 0 = planner decides; > 0 forces the segment count (clamped) */
+  int32_t q_dtype;             /* pa_dtype of q and out: PA_F16 or PA_BF16 */
+  int32_t kv_dtype;            /* pa_dtype of the caches: q_dtype, or PA_U8 (u8 entry point) */
+  void* workspace;             /* device scratch >= pa_verify_workspace_bytes; its first 4 bytes
+                                  are the sticky device status word: zero them once at allocation */
+  size_t workspace_bytes;
+  void* stream;                /* hipStream_t to enqueue on; NULL = the null stream */
+  void* prof_event_begin;      /* optional hipEvent_t recorded right before the segment kernel */
+  void* prof_event_end;        /* optional hipEvent_t recorded right after the segment kernel */
+} pa_verify_params;
+
+/* The launch plan, a pure function of host scalars: segment count S, keys per
+ * segment, grids and workspace size.  Exposed so callers and tests can see
+ * what a call will launch. */
+typedef struct pa_verify_plan {
+  int32_t num_segments;        /* S: KV segments per (sequence, KV head) */
+  int32_t steps_per_segment;   /* key steps of keys_per_step keys per segment */
+  int32_t keys_per_step;       /* keys one wavefront consumes per loop iteration */
+  int32_t span;                /* bound on keys any one sequence's rows touch */
+  int32_t waves_per_group;     /* wavefronts per segment workgroup */
+  int32_t grid[3];             /* segment kernel grid: (S, Hkv, num_seqs) */
+  int32_t block_threads;       /* segment kernel workgroup size */
+  int32_t combine_grid[3];     /* combine kernel grid */
+  int32_t combine_threads;     /* combine kernel workgroup size */
+  size_t workspace_bytes;      /* status word + per-token segment partials */
+} pa_verify_plan;
+
+/* Fill *plan for params p, host scalar max_context_len (>= max_s L_s + T_s)
+ * and a compute-unit count num_cus (> 0).  No device access.  Returns PA_OK or
+ * the same host-side error pa_verify_forward would return (except workspace). */
+int pa_verify_make_plan(const pa_verify_params* p, int32_t max_context_len,
+                        int32_t num_cus, pa_verify_plan* plan);
+
+/* Workspace bytes a forward call with these params needs on the current
+ * device (queries its compute-unit count once).  Returns 0 on invalid input
+ * or when no device is present. */
+size_t pa_verify_workspace_bytes(const pa_verify_params* p, int32_t max_context_len);
+
+/* Paged verify attention, f16 or bf16 KV cache (kv_dtype == q_dtype).
+ * q, k_cache, v_cache, out: device pointers in the layouts above.
+ * block_tables, past_lens, subsequence_begins: device int32 arrays.
+ * max_context_len: host scalar >= max over s of past_lens[s] + T_s; it sizes
+ * the grid and workspace without reading device memory.
+ * scale: multiplies q.k before the softmax (e.g. 1/sqrt(D)).
+ * Returns PA_OK once both kernels are enqueued. */
+int pa_verify_forward(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* past_lens,
+                      const int32_t* subsequence_begins, int32_t max_context_len,
+                      float scale, void* out, const pa_verify_params* p);
+
+/* The same operation over a u8 KV cache (kv_dtype == PA_U8): a cached value u
+ * of token t, KV head g stands for (u - zp) * scale with (scale, zp) read as
+ * f16 from k_scale_zp / v_scale_zp[block, g, slot, 0..1].  Dequantisation
+ * follows that formula exactly in f32/f16 arithmetic inside the kernel. */
+int pa_verify_forward_u8(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                         const void* k_scale_zp, const void* v_scale_zp,
+                         const int32_t* block_tables, const int32_t* past_lens,
+                         const int32_t* subsequence_begins, int32_t max_context_len,
+                         float scale, void* out, const pa_verify_params* p);
+
+/* Synchronise p->stream, read the sticky device status word from
+ * p->workspace into *device_status (PA_OK or PA_ERR_DEVICE_CONTRACT) and clear
+ * it.  For tests and debugging; it blocks the host. */
+int pa_verify_read_status(const pa_verify_params* p, int32_t* device_status);
+
+/* Static, human-readable name of a pa_status value. */
+const char* pa_verify_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_VERIFY_H */

@@ -1,0 +1,224 @@
+/*
+ * pa_oracle.c — the CPU oracle for paged verify attention.  TEST
+ * INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+ * baseline use it; the library never does.  It shares no code, header,
+ * table or helper with the GPU path.
+ *
+ * It is the plain definition of the operation, in fp64, written as loops:
+ *
+ *  - New query token i (0-based inside its sequence) of a sequence with
+ *    past_len L attends to cache positions below L + i + 1: OpenVINO issue
+ *    #38153 "[GPU] PagedAttention with 2-4 query tokens per sequence
+ *    (speculative decoding verify) is ~8x slower than single-token decode",
+ *    section "Performance issue description" (the suggested key limit).
+ *  - The op metadata (past_lens, subsequence_begins, max_context_len, one
+ *    block table per sequence) and the u8 KV cache: same issue, section
+ *    "Step-by-step reproduction".
+ *  - A sliding-window layer (window 1024 in the model measured) keeps only the
+ *    last W positions, the token itself included: SGLang discussion #36314
+ *    "FROZEN_KV_MTP slower than no-spec on Gemma 4 (SWA hybrid)", section
+ *    "Observation 3".  Reading: W counts the token itself.
+ *  - Grouped-query attention: q head h reads KV head h / (Hq / Hkv).  The
+ *    pages only name "GQA read-once"; consecutive grouping is the reading.
+ *  - Softmax is taken over scale * q.k, two passes (max, then exp-sum), no
+ *    segmentation, no online rescaling: the segmented GPU reduction must
+ *    reach the same value up to rounding order (vLLM article "speculative
+ *    decoding net loss", passage on the 18 fixed-input kernel cases).
+ *
+ * Layouts (the library's C ABI defines them; restated here on purpose):
+ *   q [num_tokens][Hq][D], k [nb][Hkv][bs][D], v [nb][Hkv][D][bs],
+ *   scale/zero point [nb][Hkv][bs][2] (f16), block_tables [num_seqs][mbps].
+ * Element codes: 0 = f16 bits, 1 = bf16 bits, 2 = u8 code with f16
+ * (scale, zero point), 3 = fp64 value (test-only input form).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+#include "pa_oracle.h"
+
+/* IEEE binary16 bit pattern -> exact double. */
+static double dec_f16(uint16_t b) {
+  int sign = (b >> 15) & 1;
+  int exp = (b >> 10) & 0x1f;
+  int man = b & 0x3ff;
+  double v;
+  if (exp == 0) {
+    v = ldexp((double)man, -24);                   /* subnormal: man * 2^-24 */
+  } else if (exp == 31) {
+    v = man ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(man | 0x400), exp - 25);    /* (1024 + man) * 2^(exp-15-10) */
+  }
+  return sign ? -v : v;
+}
+
+/* bfloat16 bit pattern -> exact double (bf16 is the top half of a float32). */
+static double dec_bf16(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static double dec_elem(const void* base, size_t idx, int code) {
+  switch (code) {
+    case PA_ORACLE_F16: return dec_f16(((const uint16_t*)base)[idx]);
+    case PA_ORACLE_BF16: return dec_bf16(((const uint16_t*)base)[idx]);
+    case PA_ORACLE_F64: return ((const double*)base)[idx];
+    default: return NAN;
+  }
+}
+
+/* One KV value.  For u8, code u of (block, head, slot) means (u - zp) * scale
+ * with the per-token per-KV-head f16 pair stored next to the cache. */
+static double kv_value(const pa_oracle_args* a, const void* cache, const void* sz,
+                       size_t elem_idx, size_t slot_idx) {
+  if (a->kv_dtype == PA_ORACLE_U8) {
+    const uint16_t* p = (const uint16_t*)sz;
+    double s = dec_f16(p[2 * slot_idx + 0]);
+    double zp = dec_f16(p[2 * slot_idx + 1]);
+    return ((double)((const uint8_t*)cache)[elem_idx] - zp) * s;
+  }
+  return dec_elem(cache, elem_idx, a->kv_dtype);
+}
+
+/* Check the metadata the way the definition needs it: returns 0 when every
+ * sequence has 1 <= T, 0 <= L, L + T <= max_context_len, a well-formed
+ * subsequence_begins and in-range block ids for every position it reads. */
+static int check_args(const pa_oracle_args* a) {
+  if (a->num_seqs < 1 || a->num_q_heads < 1 || a->num_kv_heads < 1 || a->head_dim < 1 ||
+      a->block_size < 1 || a->num_q_heads % a->num_kv_heads != 0)
+    return PA_ORACLE_ERR_ARG;
+  if (!a->q || !a->k_cache || !a->v_cache || !a->block_tables || !a->past_lens ||
+      !a->subsequence_begins)
+    return PA_ORACLE_ERR_ARG;
+  if (a->kv_dtype == PA_ORACLE_U8 && (!a->k_scale_zp || !a->v_scale_zp)) return PA_ORACLE_ERR_ARG;
+  if (a->subsequence_begins[0] != 0 || a->subsequence_begins[a->num_seqs] != a->num_tokens)
+    return PA_ORACLE_ERR_META;
+  for (int s = 0; s < a->num_seqs; ++s) {
+    int T = a->subsequence_begins[s + 1] - a->subsequence_begins[s];
+    int L = a->past_lens[s];
+    if (T < 1 || L < 0 || (int64_t)L + T > a->max_context_len) return PA_ORACLE_ERR_META;
+    int nblk = (L + T + a->block_size - 1) / a->block_size;
+    if (nblk > a->max_blocks_per_seq) return PA_ORACLE_ERR_META;
+    int lo_first = a->sliding_window > 0 ? L + 1 - a->sliding_window : 0;
+    if (lo_first < 0) lo_first = 0;
+    for (int b = lo_first / a->block_size; b < nblk; ++b) {
+      int id = a->block_tables[(size_t)s * a->max_blocks_per_seq + b];
+      if (id < 0 || id >= a->num_blocks) return PA_ORACLE_ERR_META;
+    }
+  }
+  return PA_ORACLE_OK;
+}
+
+/* out[row][:] for query token n, q head h: the definition, two-pass softmax. */
+static void attend_one(const pa_oracle_args* a, int n, int h, double* z, double* out_row) {
+  const int D = a->head_dim, bs = a->block_size, Hq = a->num_q_heads, Hkv = a->num_kv_heads;
+  int s = 0;
+  while (!(a->subsequence_begins[s] <= n && n < a->subsequence_begins[s + 1])) ++s;
+  const int i = n - a->subsequence_begins[s];      /* index of the token inside its sequence */
+  const int L = a->past_lens[s];
+  const int hi = L + i + 1;                         /* keys [lo, hi) */
+  int lo = 0;
+  if (a->sliding_window > 0) {
+    lo = hi - a->sliding_window;
+    if (lo < 0) lo = 0;
+  }
+  const int g = h / (Hq / Hkv);                     /* KV head serving q head h */
+  const int32_t* table = a->block_tables + (size_t)s * a->max_blocks_per_seq;
+  const size_t q_off = ((size_t)n * Hq + h) * D;
+
+  /* pass 1: logits and their max */
+  double m = -INFINITY;
+  for (int t = lo; t < hi; ++t) {
+    const size_t blk = (size_t)table[t / bs];
+    const int slot = t % bs;
+    const size_t row = (blk * Hkv + g) * bs + slot; /* index of (blk, g, slot) */
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d)
+      dot += dec_elem(a->q, q_off + d, a->q_dtype) *
+             kv_value(a, a->k_cache, a->k_scale_zp, row * D + d, row);
+    z[t - lo] = a->scale * dot;
+    if (z[t - lo] > m) m = z[t - lo];
+  }
+  /* pass 2: weights, their sum, and the weighted sum of V rows */
+  double Z = 0.0;
+  for (int d = 0; d < D; ++d) out_row[d] = 0.0;
+  for (int t = lo; t < hi; ++t) {
+    const double w = exp(z[t - lo] - m);
+    Z += w;
+    const size_t blk = (size_t)table[t / bs];
+    const int slot = t % bs;
+    const size_t row = (blk * Hkv + g) * bs + slot;
+    for (int d = 0; d < D; ++d) {
+      const size_t vidx = ((blk * Hkv + g) * D + d) * bs + slot;   /* v is [nb][Hkv][D][bs] */
+      out_row[d] += w * kv_value(a, a->v_cache, a->v_scale_zp, vidx, row);
+    }
+  }
+  for (int d = 0; d < D; ++d) out_row[d] /= Z;
+}
+
+typedef struct {
+  const pa_oracle_args* a;
+  double* out;
+  int64_t num_items;
+  int tid, nthreads;
+} worker_t;
+
+static void* worker(void* arg) {
+  worker_t* w = (worker_t*)arg;
+  const pa_oracle_args* a = w->a;
+  double* z = (double*)malloc(sizeof(double) * (size_t)(a->max_context_len > 0 ? a->max_context_len : 1));
+  if (!z) return (void*)1;
+  for (int64_t it = w->tid; it < w->num_items; it += w->nthreads) {
+    int n, h;
+    if (a->pairs) {
+      n = a->pairs[2 * it];
+      h = a->pairs[2 * it + 1];
+    } else {
+      n = (int)(it / a->num_q_heads);
+      h = (int)(it % a->num_q_heads);
+    }
+    attend_one(a, n, h, z, w->out + (size_t)it * a->head_dim);
+  }
+  free(z);
+  return NULL;
+}
+
+int pa_oracle_num_threads(void) {
+  long n = sysconf(_SC_NPROCESSORS_ONLN);
+  return n > 0 ? (int)n : 1;
+}
+
+int pa_oracle_forward(const pa_oracle_args* a, double* out) {
+  if (!a || !out) return PA_ORACLE_ERR_ARG;
+  int rc = check_args(a);
+  if (rc) return rc;
+  int64_t items = a->pairs ? a->num_pairs : (int64_t)a->num_tokens * a->num_q_heads;
+  if (a->pairs) {
+    for (int64_t it = 0; it < items; ++it)
+      if (a->pairs[2 * it] < 0 || a->pairs[2 * it] >= a->num_tokens || a->pairs[2 * it + 1] < 0 ||
+          a->pairs[2 * it + 1] >= a->num_q_heads)
+        return PA_ORACLE_ERR_ARG;
+  }
+  int nt = a->num_threads > 0 ? a->num_threads : pa_oracle_num_threads();
+  if (nt > items) nt = items > 0 ? (int)items : 1;
+  pthread_t th[256];
+  worker_t ws[256];
+  if (nt > 256) nt = 256;
+  for (int t = 0; t < nt; ++t) {
+    ws[t] = (worker_t){a, out, items, t, nt};
+    if (pthread_create(&th[t], NULL, worker, &ws[t]) != 0) return PA_ORACLE_ERR_ARG;
+  }
+  int bad = 0;
+  for (int t = 0; t < nt; ++t) {
+    void* r = NULL;
+    pthread_join(th[t], &r);
+    if (r) bad = 1;
+  }
+  return bad ? PA_ORACLE_ERR_ARG : PA_ORACLE_OK;
+}

@@ -1,0 +1,340 @@
+"""Seeded synthetic inputs for paged verify attention.
+
+This module only *makes* inputs: random values, their rounding to the storage
+dtype, the u8 quantisation of the cache, the paged pool and its block tables,
+and NaN poisoning of cache slots no query may read.  It contains none of the
+attention arithmetic; both the CPU oracle (``oracle/``) and the GPU path
+(``speculative_decoding_verify_paged_amd``) consume what it returns, and
+neither imports the other.
+
+Recipe (also the basis of every parity case and of the benchmark):
+
+* ``rng = numpy.random.default_rng(seed)`` with a per-case integer list seed.
+* Draw order: (ragged batches only: past_len_s, then T_s) -> q -> K pool ->
+  V pool -> block permutation.  Pools are drawn in chunks of whole blocks,
+  float32 N(0, 1), one array of shape [blocks, Hkv, block_size, D] each.
+* fp16 / bf16 values are the float32 draws rounded to nearest-even.
+* u8 values quantise each (block, KV head, slot) row of D float32 values
+  asymmetrically (``quantize_u8``), as the OpenVINO issue #38153 setup runs a
+  u8 KV cache with f16 compute ("Step-by-step reproduction"); the per-token
+  per-KV-head (scale, zero point) pair is stored as f16.
+* Physical blocks are a random permutation of the pool, dealt to sequences in
+  order; block-table entries past a sequence's last block hold an
+  out-of-range id so any read of them is caught by the device bounds check.
+* ``poison=True`` writes NaN into every cache slot no query row may read: slots
+  at positions >= past_len + T in a sequence's last block, slots below the
+  sliding window, and spare pool blocks (for u8: NaN scale/zero point).
+
+Layouts match the C ABI header: k [nb, Hkv, bs, D]; v [nb, Hkv, D, bs]
+(d-major pages); scale/zp [nb, Hkv, bs, 2] f16; q [num_tokens, Hq, D].
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+F16, BF16, U8 = 0, 1, 2          # same integer codes as the C ABI's pa_dtype
+DTYPE_NAMES = {F16: "f16", BF16: "bf16", U8: "u8"}
+BAD_BLOCK_ID = 0x7FFFFFF0        # block-table filler past a sequence's last block
+_CHUNK_VALUES = 1 << 22          # pools are drawn in chunks of whole blocks of about this size
+
+F16_NAN = np.uint16(0x7E00)
+BF16_NAN = np.uint16(0x7FC0)
+
+
+# ----------------------------------------------------------------------------
+# storage rounding and decoding (representation only)
+# ----------------------------------------------------------------------------
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to IEEE binary16, nearest-even; return the bit patterns."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16, nearest-even (NaN stays NaN); return bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    rounded = (u + np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1))) >> 16
+    out = rounded.astype(np.uint16)
+    out[nan] = BF16_NAN
+    return out
+
+
+def f16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return np.asarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def bits_to_f32(b: np.ndarray, dtype: int) -> np.ndarray:
+    if dtype == F16:
+        return f16_bits_to_f32(b)
+    if dtype == BF16:
+        return bf16_bits_to_f32(b)
+    raise ValueError(f"not a 16-bit float dtype: {dtype}")
+
+
+def f32_to_bits(x: np.ndarray, dtype: int) -> np.ndarray:
+    if dtype == F16:
+        return f32_to_f16_bits(x)
+    if dtype == BF16:
+        return f32_to_bf16_bits(x)
+    raise ValueError(f"not a 16-bit float dtype: {dtype}")
+
+
+def quantize_u8(x: np.ndarray):
+    """Asymmetric u8 quantisation of each row (last axis) of float32 ``x``.
+
+    scale = (max - min) / 255 and zero_point = -min / scale, both rounded to
+    f16; u = clamp(round_half_even(x / scale16 + zp16), 0, 255).  A constant
+    row uses scale = 1, zero_point = -min.  The value a code stands for is
+    (u - zp16) * scale16.  Returns (u8 codes, scale f16 bits, zp f16 bits),
+    the last two with the row shape.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    mn = x.min(axis=-1)
+    mx = x.max(axis=-1)
+    flat = mx == mn
+    scale = np.where(flat, np.float32(1.0), (mx - mn) / np.float32(255.0)).astype(np.float32)
+    s16 = scale.astype(np.float16)
+    zp = np.where(flat, -mn, -mn / s16.astype(np.float32)).astype(np.float32)
+    zp16 = zp.astype(np.float16)
+    q = np.rint(x / s16.astype(np.float32)[..., None] + zp16.astype(np.float32)[..., None])
+    u = np.clip(q, 0, 255).astype(np.uint8)
+    return u, s16.view(np.uint16), zp16.view(np.uint16)
+
+
+# ----------------------------------------------------------------------------
+# cases
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass
+class Case:
+    """One call's inputs, in the C ABI layouts (numpy, host memory)."""
+    name: str
+    num_seqs: int
+    num_tokens: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    sliding_window: int
+    q_dtype: int
+    kv_dtype: int
+    scale: float
+    max_context_len: int
+    q: np.ndarray                 # uint16 bits [num_tokens, Hq, D]
+    k_cache: np.ndarray           # uint16 bits or uint8 [nb, Hkv, bs, D]
+    v_cache: np.ndarray           # uint16 bits or uint8 [nb, Hkv, D, bs]
+    k_scale_zp: Optional[np.ndarray]  # uint16 f16 bits [nb, Hkv, bs, 2] (u8 only)
+    v_scale_zp: Optional[np.ndarray]
+    block_tables: np.ndarray      # int32 [num_seqs, max_blocks_per_seq]
+    past_lens: np.ndarray         # int32 [num_seqs]
+    subsequence_begins: np.ndarray  # int32 [num_seqs + 1]
+
+    @property
+    def Ts(self) -> List[int]:
+        sb = self.subsequence_begins
+        return [int(sb[i + 1] - sb[i]) for i in range(self.num_seqs)]
+
+    def kv_keys(self) -> int:
+        """Keys whose K and V the call must read (the union over each sequence's rows)."""
+        total = 0
+        for L, T in zip(self.past_lens.tolist(), self.Ts):
+            n = L + T
+            if self.sliding_window > 0:
+                n = min(n, self.sliding_window + T - 1)
+            total += n
+        return total
+
+    def kv_bytes(self) -> int:
+        """Algorithmic KV bytes of one call: each needed (key, KV head) K and V row once."""
+        e = 1 if self.kv_dtype == U8 else 2
+        per_key = self.num_kv_heads * (2 * self.head_dim * e + (8 if self.kv_dtype == U8 else 0))
+        return self.kv_keys() * per_key
+
+    def logical_kv_f32(self, s: int):
+        """Float32 values of sequence s's K and V as [L+T, Hkv, D] (tests only).
+
+        For u8 the values are the dequantised codes in float64 precision."""
+        L = int(self.past_lens[s])
+        T = self.Ts[s]
+        n = L + T
+        bs = self.block_size
+        pos = np.arange(n)
+        blk = self.block_tables[s, pos // bs]
+        off = pos % bs
+        if self.kv_dtype == U8:
+            ku = self.k_cache[blk, :, off, :].astype(np.float64)          # [n, Hkv, D]
+            vu = self.v_cache[blk, :, :, off].astype(np.float64)          # [n, Hkv, D]
+            ksz = self.k_scale_zp[blk, :, off, :]
+            vsz = self.v_scale_zp[blk, :, off, :]
+            ks = f16_bits_to_f32(ksz[..., 0]).astype(np.float64)
+            kz = f16_bits_to_f32(ksz[..., 1]).astype(np.float64)
+            vs = f16_bits_to_f32(vsz[..., 0]).astype(np.float64)
+            vz = f16_bits_to_f32(vsz[..., 1]).astype(np.float64)
+            return (ku - kz[..., None]) * ks[..., None], (vu - vz[..., None]) * vs[..., None]
+        k = bits_to_f32(self.k_cache[blk, :, off, :], self.kv_dtype)
+        v = bits_to_f32(self.v_cache[blk, :, :, off], self.kv_dtype)
+        return k.astype(np.float64), v.astype(np.float64)
+
+    def q_f32(self) -> np.ndarray:
+        return bits_to_f32(self.q, self.q_dtype)
+
+
+def _draw_pool(rng, nb, Hkv, bs, D):
+    """Draw float32 N(0,1) of shape [nb, Hkv, bs, D] in chunks of whole blocks."""
+    out = np.empty((nb, Hkv, bs, D), dtype=np.float32)
+    per_block = Hkv * bs * D
+    step = max(1, _CHUNK_VALUES // per_block)
+    for b in range(0, nb, step):
+        e = min(nb, b + step)
+        out[b:e] = rng.standard_normal((e - b, Hkv, bs, D), dtype=np.float32)
+    return out
+
+
+def _store_pool(x, kv_dtype, transpose_v):
+    """Round or quantise a float32 [nb, Hkv, bs, D] pool to its storage form."""
+    if kv_dtype == U8:
+        u, s, z = quantize_u8(x)
+        sz = np.stack([s, z], axis=-1)                 # [nb, Hkv, bs, 2]
+        if transpose_v:
+            u = np.ascontiguousarray(np.swapaxes(u, 2, 3))
+        return u, sz
+    bits = f32_to_bits(x, kv_dtype)
+    if transpose_v:
+        bits = np.ascontiguousarray(np.swapaxes(bits, 2, 3))
+    return bits, None
+
+
+def build_case(seed: Sequence[int], past_lens: Sequence[int], Ts: Sequence[int], *,
+               num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+               q_dtype: int = F16, kv_dtype: int = F16, sliding_window: int = 0,
+               spare_blocks: int = 0, poison: bool = False,
+               scale: Optional[float] = None, max_blocks_per_seq: Optional[int] = None,
+               max_context_len: Optional[int] = None, name: str = "case",
+               rng: Optional[np.random.Generator] = None) -> Case:
+    """Build one call's inputs following the module recipe."""
+    if rng is None:
+        rng = np.random.default_rng(list(seed))
+    past_lens = [int(x) for x in past_lens]
+    Ts = [int(x) for x in Ts]
+    num_seqs = len(past_lens)
+    assert num_seqs == len(Ts) and num_seqs >= 1
+    bs = block_size
+    sb = np.zeros(num_seqs + 1, dtype=np.int32)
+    sb[1:] = np.cumsum(Ts)
+    num_tokens = int(sb[-1])
+    ctx = [L + T for L, T in zip(past_lens, Ts)]
+    nblk = [max(1, -(-c // bs)) for c in ctx]
+    nb = sum(nblk) + spare_blocks
+    if max_context_len is None:
+        max_context_len = max(ctx)
+    mbps = max_blocks_per_seq or max(max(nblk), -(-max_context_len // bs))
+
+    qf = rng.standard_normal((num_tokens, num_q_heads, head_dim), dtype=np.float32)
+    q = f32_to_bits(qf, q_dtype)
+    kf = _draw_pool(rng, nb, num_kv_heads, bs, head_dim)
+    k_cache, k_sz = _store_pool(kf, kv_dtype, transpose_v=False)
+    del kf
+    vf = _draw_pool(rng, nb, num_kv_heads, bs, head_dim)
+    v_cache, v_sz = _store_pool(vf, kv_dtype, transpose_v=True)
+    del vf
+    perm = rng.permutation(nb).astype(np.int32)
+
+    bt = np.full((num_seqs, mbps), BAD_BLOCK_ID, dtype=np.int32)
+    o = 0
+    for s in range(num_seqs):
+        bt[s, :nblk[s]] = perm[o:o + nblk[s]]
+        o += nblk[s]
+    spare = perm[o:]
+
+    if poison:
+        _poison(k_cache, v_cache, k_sz, v_sz, kv_dtype, bt, past_lens, Ts, bs,
+                sliding_window, spare)
+
+    return Case(name=name, num_seqs=num_seqs, num_tokens=num_tokens,
+                num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+                block_size=bs, num_blocks=nb, max_blocks_per_seq=mbps,
+                sliding_window=sliding_window, q_dtype=q_dtype, kv_dtype=kv_dtype,
+                scale=float(scale if scale is not None else 1.0 / math.sqrt(head_dim)),
+                max_context_len=int(max_context_len), q=q, k_cache=k_cache, v_cache=v_cache,
+                k_scale_zp=k_sz, v_scale_zp=v_sz, block_tables=bt,
+                past_lens=np.asarray(past_lens, dtype=np.int32), subsequence_begins=sb)
+
+
+def _poison(k, v, ksz, vsz, kv_dtype, bt, past_lens, Ts, bs, W, spare):
+    """NaN every cache slot that no query row may read (see module docstring)."""
+    def kill(blk, slots):
+        if len(slots) == 0:
+            return
+        if kv_dtype == U8:
+            ksz[blk, :, slots, :] = F16_NAN
+            vsz[blk, :, slots, :] = F16_NAN
+        else:
+            nanv = F16_NAN if kv_dtype == F16 else BF16_NAN
+            k[blk, :, slots, :] = nanv
+            v[blk, :, :, slots] = nanv
+    for s, (L, T) in enumerate(zip(past_lens, Ts)):
+        n = L + T
+        last = (n - 1) // bs
+        kill(bt[s, last], np.arange(n - last * bs, bs))
+        if W > 0:
+            lo0 = max(0, L + 1 - W)            # first key any row of the sequence reads
+            for b in range(0, lo0 // bs + 1):
+                slots = np.arange(bs)
+                slots = slots[b * bs + slots < lo0]
+                kill(bt[s, b], slots)
+    for blk in spare:
+        kill(int(blk), np.arange(bs))
+
+
+# ----------------------------------------------------------------------------
+# the five workloads
+# ----------------------------------------------------------------------------
+def config1(rep: int = 0, poison: bool = False) -> Case:
+    """Tiny: 1 seq, past_len 512, T=3, Hq 4 / Hkv 1, D 64, bs 16, fp16, 33 permuted blocks."""
+    return build_case([1, 512, 3, rep], [512], [3], num_q_heads=4, num_kv_heads=1,
+                      head_dim=64, block_size=16, q_dtype=F16, kv_dtype=F16,
+                      scale=1.0 / 8.0, poison=poison, name="tiny_L512_T3")
+
+
+def config2(L: int, T: int, rep: int = 0, poison: bool = False) -> Case:
+    """1 seq, Hq 32 / Hkv 8 (GQA 4), D 128, bs 16, fp16 Q/KV/out."""
+    return build_case([2, L, T, rep], [L], [T], num_q_heads=32, num_kv_heads=8,
+                      head_dim=128, block_size=16, q_dtype=F16, kv_dtype=F16,
+                      poison=poison, name=f"gqa4_d128_f16_L{L}_T{T}")
+
+
+def config3(L: int = 32768, T: int = 3, rep: int = 0, poison: bool = False) -> Case:
+    """1 seq, Hq 16 / Hkv 4, D 256, bs 16, fp16 Q/out, u8 KV with f16 scale/zero point."""
+    return build_case([3, L, T, rep], [L], [T], num_q_heads=16, num_kv_heads=4,
+                      head_dim=256, block_size=16, q_dtype=F16, kv_dtype=U8,
+                      poison=poison, name=f"u8kv_d256_L{L}_T{T}")
+
+
+def config4(L: int, window: int = 0, T: int = 2, rep: int = 0, poison: bool = False) -> Case:
+    """Global (window 0) or sliding-window layer: Hq 32 / Hkv 16, D 256, bs 64, bf16."""
+    return build_case([4, L, T, rep, window], [L], [T], num_q_heads=32, num_kv_heads=16,
+                      head_dim=256, block_size=64, q_dtype=BF16, kv_dtype=BF16,
+                      sliding_window=window, poison=poison,
+                      name=f"swa_pair_{'swa' + str(window) if window else 'global'}_L{L}_T{T}")
+
+
+def config5(rep: int = 0, num_seqs: int = 8, lo: int = 1024, hi: int = 131072,
+            spare_blocks: int = 64, poison: bool = False) -> Case:
+    """Ragged batch: past_len log-uniform in [lo, hi], T_s uniform in 1..4, bf16,
+    Hq 32 / Hkv 8, D 128, bs 16, one shuffled shared pool plus spare blocks."""
+    rng = np.random.default_rng([5, lo, hi, rep, num_seqs])
+    Ls = np.floor(np.exp(rng.uniform(math.log(lo), math.log(hi), size=num_seqs))).astype(int)
+    Ts = rng.integers(1, 5, size=num_seqs)
+    return build_case(None, Ls.tolist(), Ts.tolist(), num_q_heads=32, num_kv_heads=8,
+                      head_dim=128, block_size=16, q_dtype=BF16, kv_dtype=BF16,
+                      spare_blocks=spare_blocks, poison=poison,
+                      name=f"ragged{num_seqs}_bf16_rep{rep}", rng=rng)

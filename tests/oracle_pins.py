@@ -1,0 +1,337 @@
+"""Pins of the fp64 oracle to things other than itself.
+
+Each pin takes an ``oracle.Oracle`` and raises AssertionError on a mismatch, so
+the same pins run against the real oracle (tests/test_oracle_pins.py) and
+against deliberately broken copies of it (tests/test_oracle_mutants.py).
+
+What pins what:
+  * sdpa        — torch's library scaled_dot_product_attention (fp64, CPU) on
+                  contiguous K/V with an explicit boolean mask built from the
+                  key-limit rule: random tiny cases over L, T, GQA, block size,
+                  window and all three KV formats.
+  * hand        — hand-worked cases with exact rational outputs (tests/golden).
+  * closed      — closed forms: q = 0 gives the mean of the visible V rows;
+                  V = c gives c (also for f16/bf16 subnormal and extreme c);
+                  L = 0, T = 1 gives v_0; one key made dominant gives its V;
+                  adding c to every V adds c.
+  * rows        — row i of a T-row call equals the T = 1 call with
+                  past_len L + i on the same cache (the issue's suggested
+                  reading of the verify rows as single-token decodes).
+  * permutation — relabelling physical blocks changes nothing (bitwise).
+  * window      — a window covering the whole context equals the global layer.
+  * gqa         — G > 1 equals G = 1 with each KV head duplicated.
+  * u8          — the u8 path equals the fp64 path fed the dequantised values.
+  * ragged      — a ragged batch equals each sequence run alone.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import pa_inputs as pi
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+F64 = 3
+
+
+# ----------------------------------------------------------------------------
+# helpers: build oracle fields from logical (unpaged) arrays
+# ----------------------------------------------------------------------------
+def paged_fields(q, keys, values, past_lens, Ts, *, bs, W=0, scale=1.0, perm_seed=0,
+                 block_table=None, extra_blocks=0):
+    """Scatter logical fp64 K/V of each sequence into a paged pool (f64 codes).
+
+    q: [num_tokens, Hq, D]; keys/values: list per sequence of [L+T, Hkv, D]."""
+    num_seqs = len(past_lens)
+    Hkv, D = keys[0].shape[1], keys[0].shape[2]
+    nblk = [-(-(L + T) // bs) for L, T in zip(past_lens, Ts)]
+    nb = sum(nblk) + extra_blocks
+    rng = np.random.default_rng(perm_seed)
+    perm = np.arange(nb) if block_table is not None else rng.permutation(nb)
+    mbps = max(nblk)
+    bt = np.full((num_seqs, mbps), pi.BAD_BLOCK_ID, dtype=np.int32)
+    kp = np.zeros((nb, Hkv, bs, D))
+    vp = np.zeros((nb, Hkv, D, bs))
+    o = 0
+    for s in range(num_seqs):
+        ids = np.asarray(block_table, np.int32) if block_table is not None else perm[o:o + nblk[s]]
+        o += nblk[s]
+        bt[s, :nblk[s]] = ids
+        for t in range(past_lens[s] + Ts[s]):
+            kp[ids[t // bs], :, t % bs, :] = keys[s][t]
+            vp[ids[t // bs], :, :, t % bs] = values[s][t]
+    sb = np.concatenate([[0], np.cumsum(Ts)]).astype(np.int32)
+    return dict(num_seqs=num_seqs, num_tokens=int(sb[-1]), num_q_heads=q.shape[1],
+                num_kv_heads=Hkv, head_dim=D, block_size=bs, num_blocks=nb,
+                max_blocks_per_seq=mbps, sliding_window=W,
+                max_context_len=max(L + T for L, T in zip(past_lens, Ts)),
+                q_dtype=F64, kv_dtype=F64, scale=scale, q=np.ascontiguousarray(q, np.float64),
+                k_cache=kp, v_cache=vp, block_tables=bt,
+                past_lens=np.asarray(past_lens, np.int32), subsequence_begins=sb)
+
+
+def run_ok(orc, **f):
+    st, out = orc.run(**f)
+    assert st == 0, f"oracle status {st}"
+    return out
+
+
+def sdpa_reference(case):
+    """torch SDPA (fp64, CPU) per sequence, mask from the key-limit rule."""
+    import torch
+    import torch.nn.functional as F
+    G = case.num_q_heads // case.num_kv_heads
+    qf = case.q_f32().astype(np.float64)
+    out = np.zeros((case.num_tokens, case.num_q_heads, case.head_dim))
+    sb = case.subsequence_begins
+    for s in range(case.num_seqs):
+        L, T = int(case.past_lens[s]), case.Ts[s]
+        k, v = case.logical_kv_f32(s)                      # [L+T, Hkv, D]
+        if case.sliding_window > 0:                        # positions no row sees may be NaN
+            lo0 = max(0, L + 1 - case.sliding_window)
+            k[:lo0] = 0.0
+            v[:lo0] = 0.0
+        k = np.repeat(k, G, axis=1).transpose(1, 0, 2)     # [Hq, L+T, D]
+        v = np.repeat(v, G, axis=1).transpose(1, 0, 2)
+        qs = qf[sb[s]:sb[s + 1]].transpose(1, 0, 2)        # [Hq, T, D]
+        mask = np.zeros((T, L + T), dtype=bool)
+        for i in range(T):
+            hi = L + i + 1
+            lo = max(0, hi - case.sliding_window) if case.sliding_window > 0 else 0
+            mask[i, lo:hi] = True
+        o = F.scaled_dot_product_attention(torch.from_numpy(qs), torch.from_numpy(np.ascontiguousarray(k)),
+                                           torch.from_numpy(np.ascontiguousarray(v)),
+                                           attn_mask=torch.from_numpy(mask), scale=case.scale)
+        out[sb[s]:sb[s + 1]] = o.numpy().transpose(1, 0, 2)
+    return out
+
+
+def tiny_random_cases(n=48, seed=7):
+    """Random tiny cases over the whole parameter space of the definition."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in range(n):
+        G = int(rng.choice([1, 2, 4]))
+        Hkv = int(rng.choice([1, 2]))
+        D = int(rng.choice([8, 16]))
+        bs = int(rng.choice([1, 4, 16]))
+        W = int(rng.choice([0, 0, 1, 5, 64]))
+        kv = int(rng.choice([pi.F16, pi.BF16, pi.U8]))
+        qd = pi.BF16 if kv == pi.BF16 else pi.F16
+        num_seqs = int(rng.choice([1, 1, 2, 3]))
+        Ls = rng.integers(0, 300, size=num_seqs).tolist()
+        if c % 8 == 0:
+            Ls[0] = 0
+        Ts = rng.integers(1, 5, size=num_seqs).tolist()
+        cases.append(pi.build_case([100, c], Ls, Ts, num_q_heads=G * Hkv, num_kv_heads=Hkv,
+                                   head_dim=D, block_size=bs, q_dtype=qd, kv_dtype=kv,
+                                   sliding_window=W, spare_blocks=2, poison=True,
+                                   name=f"tiny{c}"))
+    return cases
+
+
+# ----------------------------------------------------------------------------
+# pins
+# ----------------------------------------------------------------------------
+def pin_sdpa(orc, n=48):
+    for case in tiny_random_cases(n):
+        got = orc.forward(case)
+        ref = sdpa_reference(case)
+        err = np.max(np.abs(got - ref))
+        assert np.all(np.isfinite(got)), case.name
+        assert err <= 1e-12, f"{case.name}: max err {err}"
+
+
+def _num(x):
+    if isinstance(x, str):
+        m = {"ln3": math.log(3.0), "ln2": math.log(2.0), "2ln3": 2 * math.log(3.0)}
+        return m[x]
+    return float(x)
+
+
+def pin_hand(orc):
+    with open(os.path.join(HERE, "golden", "hand_worked.json")) as f:
+        data = json.load(f)
+    for c in data["cases"]:
+        q = np.array([[[_num(x) for x in row] for row in tok] for tok in c["q"]])
+        keys = np.array(c["keys"], dtype=np.float64)
+        vals = np.array(c["values"], dtype=np.float64)
+        f = paged_fields(q, [keys], [vals], [c["L"]], [c["T"]], bs=c["bs"], W=c["W"],
+                         scale=c["scale"], block_table=c["block_table"])
+        out = run_ok(orc, **f)
+        exp = np.array(c["expected"], dtype=np.float64)
+        assert np.max(np.abs(out - exp)) <= 1e-12, f"{c['name']}: {out.tolist()} vs {exp.tolist()}"
+
+
+def _rand_logical(rng, L, T, Hkv, D, Hq):
+    q = rng.standard_normal((T, Hq, D))
+    k = rng.standard_normal((L + T, Hkv, D))
+    v = rng.standard_normal((L + T, Hkv, D))
+    return q, k, v
+
+
+def pin_closed(orc):
+    rng = np.random.default_rng(11)
+    for (L, T, W, bs, Hkv, G) in [(37, 3, 0, 4, 2, 2), (5, 4, 3, 1, 1, 4), (64, 2, 16, 16, 1, 1)]:
+        D = 8
+        Hq = Hkv * G
+        q, k, v = _rand_logical(rng, L, T, Hkv, D, Hq)
+        # q = 0: uniform weights over the visible rows -> their mean
+        f = paged_fields(np.zeros_like(q), [k], [v], [L], [T], bs=bs, W=W, perm_seed=L)
+        out = run_ok(orc, **f)
+        for i in range(T):
+            hi = L + i + 1
+            lo = max(0, hi - W) if W else 0
+            for h in range(Hq):
+                mean = v[lo:hi, h // G, :].mean(axis=0)
+                assert np.max(np.abs(out[i, h] - mean)) <= 1e-12, ("q=0", L, T, W, i, h)
+        # V + c adds c
+        f2 = paged_fields(q, [k], [v + 3.25], [L], [T], bs=bs, W=W, perm_seed=L)
+        f1 = paged_fields(q, [k], [v], [L], [T], bs=bs, W=W, perm_seed=L)
+        d = run_ok(orc, **f2) - run_ok(orc, **f1)
+        assert np.max(np.abs(d - 3.25)) <= 1e-12, ("shift", L, T, W)
+        # one dominant key: k_t = 60 q for the last visible key of every row's q
+        for i in range(T):
+            hi = L + i + 1
+            kk = k.copy()
+            t = hi - 1
+            # make key t dominant for every q head sharing a KV head: use q of head g*G
+            qq = q.copy()
+            for g in range(Hkv):
+                qq[i, g * G:(g + 1) * G, :] = q[i, g * G, :]
+                kk[t, g, :] = 60.0 * q[i, g * G, :] / np.linalg.norm(q[i, g * G, :])
+            f = paged_fields(qq, [kk], [v], [L], [T], bs=bs, W=W, perm_seed=L,
+                             scale=1.0)
+            out = run_ok(orc, **f)
+            for h in range(Hq):
+                assert np.max(np.abs(out[i, h] - v[t, h // G])) <= 1e-6, ("dominant", i, h)
+    # L = 0, T = 1: the only visible key is position 0
+    q, k, v = _rand_logical(rng, 0, 1, 2, 16, 4)
+    out = run_ok(orc, **paged_fields(q, [k], [v], [0], [1], bs=16))
+    for h in range(4):
+        assert np.array_equal(out[0, h], v[0, h // 2]), "L=0,T=1"
+    # V = c for storage dtypes, including subnormal and large c: c
+    for kvd, c_bits in [(pi.F16, [0x0001, 0x03FF, 0x0400, 0x7BFF, 0xBC00, 0x3555]),
+                        (pi.BF16, [0x0001, 0x007F, 0x7F7F, 0xBF80, 0x3EAB])]:
+        base = pi.build_case([200, kvd], [21], [2], num_q_heads=2, num_kv_heads=1, head_dim=8,
+                             block_size=4, q_dtype=kvd, kv_dtype=kvd)
+        for cb in c_bits:
+            vv = np.full_like(base.v_cache, np.uint16(cb))
+            out = orc.forward(base, v_cache=vv)
+            cval = float(pi.bits_to_f32(np.array([cb], np.uint16), kvd)[0])
+            # exact up to fp64 rounding of sum(w c) / sum(w)
+            assert np.max(np.abs(out - cval)) <= 1e-14 * abs(cval), (kvd, hex(cb), out.ravel()[:3], cval)
+    # q dtype decode: q = c e_0 with k = e_0 gives logits c * scale; with two keys the
+    # weights are sigmoid(c*scale) — exact form checked for f16 and bf16 q codes
+    for qd, cb in [(pi.F16, 0x3C00), (pi.F16, 0x4100), (pi.BF16, 0x3FC0), (pi.BF16, 0x4020)]:
+        base = pi.build_case([201, qd], [1], [1], num_q_heads=1, num_kv_heads=1, head_dim=4,
+                             block_size=2, q_dtype=qd, kv_dtype=qd, scale=1.0)
+        cval = float(pi.bits_to_f32(np.array([cb], np.uint16), qd)[0])
+        qb = np.zeros_like(base.q)
+        qb[0, 0, 0] = cb
+        one = pi.f32_to_bits(np.array([1.0], np.float32), qd)[0]
+        kb = np.zeros_like(base.k_cache)
+        vb = np.zeros_like(base.v_cache)
+        blk = base.block_tables[0, 0]
+        kb[blk, 0, 1, 0] = one          # key 1 = e_0, key 0 = 0
+        vb[blk, 0, 0, 1] = one          # v_1 = e_0, v_0 = 0
+        out = orc.forward(base, q=qb, k_cache=kb, v_cache=vb)
+        w1 = math.exp(cval) / (1.0 + math.exp(cval))
+        assert abs(out[0, 0, 0] - w1) <= 1e-15, (qd, hex(cb), out[0, 0, 0], w1)
+
+
+def pin_rows(orc):
+    for case in tiny_random_cases(24, seed=3):
+        if case.num_seqs != 1:
+            continue
+        full = orc.forward(case)
+        L, T = int(case.past_lens[0]), case.Ts[0]
+        for i in range(T):
+            one = orc.forward(case, q=case.q[i:i + 1], num_tokens=1,
+                              past_lens=np.array([L + i], np.int32),
+                              subsequence_begins=np.array([0, 1], np.int32))
+            assert np.array_equal(one[0], full[i]), (case.name, i)
+
+
+def pin_permutation(orc):
+    rng = np.random.default_rng(5)
+    for (L, T, bs, W) in [(50, 3, 4, 0), (90, 4, 16, 20), (7, 2, 1, 0)]:
+        q, k, v = _rand_logical(rng, L, T, 2, 8, 4)
+        a = run_ok(orc, **paged_fields(q, [k], [v], [L], [T], bs=bs, W=W, perm_seed=1, extra_blocks=3))
+        b = run_ok(orc, **paged_fields(q, [k], [v], [L], [T], bs=bs, W=W, perm_seed=2, extra_blocks=3))
+        assert np.array_equal(a, b), (L, T, bs, W)
+
+
+def pin_window(orc):
+    for case in tiny_random_cases(24, seed=9):
+        if case.sliding_window != 0:
+            continue
+        g = orc.forward(case)
+        wmax = max(int(L) + T for L, T in zip(case.past_lens, case.Ts))
+        for W in (wmax, wmax + 5):
+            w = orc.forward(case, sliding_window=W)
+            assert np.array_equal(g, w), (case.name, W)
+        # a window of 1 keeps only the token itself: out = its own v
+        w1 = orc.forward(case, sliding_window=1)
+        G = case.num_q_heads // case.num_kv_heads
+        for s in range(case.num_seqs):
+            kf, vf = case.logical_kv_f32(s)
+            L = int(case.past_lens[s])
+            for i in range(case.Ts[s]):
+                n = int(case.subsequence_begins[s]) + i
+                for h in range(case.num_q_heads):
+                    assert np.max(np.abs(w1[n, h] - vf[L + i, h // G])) <= 1e-12, (case.name, n, h)
+
+
+def pin_gqa(orc):
+    rng = np.random.default_rng(13)
+    for G in (2, 4, 8):
+        L, T, Hkv, D = 40, 3, 2, 8
+        q, k, v = _rand_logical(rng, L, T, Hkv, D, Hkv * G)
+        grouped = run_ok(orc, **paged_fields(q, [k], [v], [L], [T], bs=4, perm_seed=3))
+        kd = np.repeat(k, G, axis=1)
+        vd = np.repeat(v, G, axis=1)
+        dup = run_ok(orc, **paged_fields(q, [kd], [vd], [L], [T], bs=4, perm_seed=3))
+        assert np.array_equal(grouped, dup), G
+
+
+def pin_u8(orc):
+    for seed in range(6):
+        case = pi.build_case([300, seed], [int(30 + 17 * seed)], [1 + seed % 4], num_q_heads=4,
+                             num_kv_heads=2, head_dim=16, block_size=4, q_dtype=pi.F16,
+                             kv_dtype=pi.U8, sliding_window=(0 if seed % 2 else 9),
+                             spare_blocks=1, poison=True)
+        got = orc.forward(case)
+        ks = pi.f16_bits_to_f32(case.k_scale_zp[..., 0]).astype(np.float64)
+        kz = pi.f16_bits_to_f32(case.k_scale_zp[..., 1]).astype(np.float64)
+        vs = pi.f16_bits_to_f32(case.v_scale_zp[..., 0]).astype(np.float64)
+        vz = pi.f16_bits_to_f32(case.v_scale_zp[..., 1]).astype(np.float64)
+        kd = (case.k_cache.astype(np.float64) - kz[..., None]) * ks[..., None]
+        vd = (case.v_cache.astype(np.float64) - vz[:, :, None, :]) * vs[:, :, None, :]
+        ref = orc.forward(case, kv_dtype=F64, q_dtype=F64, q=case.q_f32().astype(np.float64),
+                          k_cache=kd, v_cache=vd)
+        assert np.array_equal(np.isnan(got), np.isnan(ref)) and np.array_equal(got, ref), seed
+
+
+def pin_ragged(orc):
+    for case in tiny_random_cases(32, seed=21):
+        if case.num_seqs < 2:
+            continue
+        full = orc.forward(case)
+        sb = case.subsequence_begins
+        for s in range(case.num_seqs):
+            one = orc.forward(case, num_seqs=1, num_tokens=case.Ts[s], q=case.q[sb[s]:sb[s + 1]],
+                              block_tables=case.block_tables[s:s + 1],
+                              past_lens=case.past_lens[s:s + 1],
+                              subsequence_begins=np.array([0, case.Ts[s]], np.int32))
+            assert np.array_equal(one, full[sb[s]:sb[s + 1]]), (case.name, s)
+
+
+ALL_PINS = {
+    "sdpa": pin_sdpa, "hand": pin_hand, "closed": pin_closed, "rows": pin_rows,
+    "permutation": pin_permutation, "window": pin_window, "gqa": pin_gqa, "u8": pin_u8,
+    "ragged": pin_ragged,
+}

@@ -1,0 +1,69 @@
+"""Each plausible mistake planted in a copy of the oracle must fail some pin.
+
+The copy is compiled on the CPU from the oracle source with one edit; the real
+oracle is untouched.  Every edit keeps all memory accesses in bounds.
+"""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+# (name, [(text in pa_oracle.c, replacement), ...])
+MUTANTS = [
+    ("key_limit_off_by_one", [("const int hi = L + i + 1;", "const int hi = L + i;")]),
+    ("row_index_dropped", [("const int i = n - a->subsequence_begins[s];", "const int i = 0;")]),
+    ("gqa_modulo_mapping", [("const int g = h / (Hq / Hkv);", "const int g = h % Hkv;")]),
+    ("scale_dropped", [("z[t - lo] = a->scale * dot;", "z[t - lo] = dot;")]),
+    ("window_one_short", [("lo = hi - a->sliding_window;", "lo = hi - a->sliding_window + 1;")]),
+    ("v_read_in_k_layout", [("const size_t vidx = ((blk * Hkv + g) * D + d) * bs + slot;",
+                             "const size_t vidx = row * D + d;")]),
+    ("block_table_ignored", [("const size_t blk = (size_t)table[t / bs];",
+                              "const size_t blk = (size_t)(t / bs);")]),
+    ("slot_shifted", [("const int slot = t % bs;", "const int slot = (t + 1) % bs;")]),
+    ("dequant_sign", [("[elem_idx] - zp) * s;", "[elem_idx] + zp) * s;")]),
+    ("scale_zp_swapped", [("double s = dec_f16(p[2 * slot_idx + 0]);", "double s = dec_f16(p[2 * slot_idx + 1]);"),
+                          ("double zp = dec_f16(p[2 * slot_idx + 1]);", "double zp = dec_f16(p[2 * slot_idx + 0]);")]),
+    ("no_normalisation", [("for (int d = 0; d < D; ++d) out_row[d] /= Z;",
+                           "for (int d = 0; d < D; ++d) out_row[d] /= 1.0;")]),
+    ("softmax_temperature", [("const double w = exp(z[t - lo] - m);",
+                              "const double w = exp(2.0 * (z[t - lo] - m));")]),
+    ("f16_exponent_bias", [("v = ldexp((double)(man | 0x400), exp - 25);",
+                            "v = ldexp((double)(man | 0x400), exp - 24);")]),
+    ("f16_subnormal_scale", [("v = ldexp((double)man, -24);", "v = ldexp((double)man, -25);")]),
+    ("bf16_shift", [("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;")]),
+    ("q_head_major_layout", [("const size_t q_off = ((size_t)n * Hq + h) * D;",
+                              "const size_t q_off = ((size_t)h * a->num_tokens + n) * D;")]),
+    ("k_dims_reversed", [("row * D + d, row);", "row * D + (D - 1 - d), row);")]),
+]
+
+PIN_ORDER = ["hand", "closed", "rows", "window", "gqa", "u8", "permutation", "ragged", "sdpa"]
+
+
+def _source():
+    with open(oracle.SRC) as f:
+        return f.read()
+
+
+def test_pin_list_is_complete():
+    assert sorted(PIN_ORDER) == sorted(ALL_PINS)
+
+
+@pytest.mark.parametrize("name,edits", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, edits):
+    src = _source()
+    for old, new in edits:
+        assert old in src, f"mutation site for {name} not found in the oracle source"
+        src = src.replace(old, new)
+    with tempfile.TemporaryDirectory() as d:
+        orc = oracle.build_variant(src, d)
+        caught = []
+        for pin in PIN_ORDER:
+            try:
+                ALL_PINS[pin](orc)
+            except (AssertionError, ValueError) as e:
+                caught.append(pin)
+                break
+        assert caught, f"no pin catches the planted mistake {name}"
