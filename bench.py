@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark of paged verify attention on one MI355X; prints ONE JSON line.
+
+Default workload: one sequence, past_len 32768, 32 q heads / 8 KV heads
+(GQA 4), head_dim 128, block 16, fp16 Q/KV/out, random block permutation —
+a "step" is one pa_verify_forward call with T=3 verify rows (segment kernel +
+combine kernel).  The same call with T=1 is timed beside it for the T-cost
+ratio.  Inputs are resident in HBM before timing; KV pools are rotated over
+>= 1 GiB of copies so the 256 MB Infinity Cache cannot serve them.
+
+value = algorithmic KV bytes of one call / measured time per call (GB/s).
+roofline = the segment kernel's algorithmic KV bytes / its own average
+duration from HIP events recorded around it in the timed region, against
+MI355X's 8 TB/s HBM peak.  cpu_baseline = the fp64 oracle timed on the host
+cores over a bounded sample of the same call.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "µs/call + achieved KV GB/s (% of HBM peak) at 32k ctx, T=3 vs T=1, 1 GPU"
+ROTATE_BYTES = 1 << 30
+
+
+def workloads():
+    import pa_inputs as pi
+    return {
+        "gqa4_d128_f16_L32768": lambda T: pi.config2(32768, T),
+        "gqa4_d128_f16_L8192": lambda T: pi.config2(8192, T),
+        "u8kv_d256_L32768": lambda T: pi.config3(32768, T),
+        "swa_pair_global_L32768": lambda T: pi.config4(32768, window=0, T=T),
+        "swa_pair_global_L51200": lambda T: pi.config4(51200, window=0, T=T),
+        "swa_pair_window1024_L32768": lambda T: pi.config4(32768, window=1024, T=T),
+        "ragged8_bf16": lambda T: pi.config5(),
+    }
+
+
+def kernel_source_hash():
+    d = os.path.join(ROOT, "speculative_decoding_verify_paged_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, T):
+    """HBM bytes per segment-kernel launch from committed rocprofv3 counter
+    runs, if they were taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(f"{workload}_T{T}")
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Runner:
+    """Device-resident inputs for one case with rotated KV pool copies."""
+
+    def __init__(self, case, copies=None):
+        import torch
+        from gpu_util import to_device
+        import speculative_decoding_verify_paged_amd as pav
+        self.pav = pav
+        self.case = case
+        self.dev = to_device(case)
+        pool_bytes = sum(self.dev[k].numel() * self.dev[k].element_size()
+                         for k in ("k_cache", "v_cache", "k_scale_zp", "v_scale_zp") if k in self.dev)
+        self.copies = copies or max(1, math.ceil(ROTATE_BYTES / pool_bytes))
+        self.pools = [self.dev]
+        for _ in range(self.copies - 1):
+            d = dict(self.dev)
+            for k in ("k_cache", "v_cache", "k_scale_zp", "v_scale_zp"):
+                if k in d:
+                    d[k] = d[k].clone()
+            self.pools.append(d)
+        self.out = torch.empty_like(self.dev["q"])
+        self.stream = torch.cuda.current_stream()
+
+    def call(self, i, prof=None):
+        c, d = self.case, self.pools[i % self.copies]
+        if c.kv_dtype == 2:
+            self.pav.pa_verify_forward_u8(d["q"], d["k_cache"], d["v_cache"], d["k_scale_zp"],
+                                          d["v_scale_zp"], d["block_tables"], d["past_lens"],
+                                          d["subsequence_begins"], c.max_context_len, c.scale,
+                                          self.out, sliding_window=c.sliding_window,
+                                          stream=self.stream.cuda_stream, prof_events=prof)
+        else:
+            self.pav.pa_verify_forward(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                       d["past_lens"], d["subsequence_begins"], c.max_context_len,
+                                       c.scale, self.out, sliding_window=c.sliding_window,
+                                       stream=self.stream.cuda_stream, prof_events=prof)
+
+    def time(self, steps, warmup, repeats):
+        """Median µs per call and median segment-kernel µs over `repeats` timed regions."""
+        import torch
+        for i in range(warmup):
+            self.call(i)
+        torch.cuda.synchronize()
+        per_call, per_kernel = [], []
+        evb = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        eve = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for e in evb + eve:
+            e.record(self.stream)           # create the underlying hipEvent
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        for r in range(repeats):
+            torch.cuda.synchronize()
+            t0.record(self.stream)
+            for i in range(steps):
+                self.call(i, prof=(evb[i].cuda_event, eve[i].cuda_event))
+            t1.record(self.stream)
+            torch.cuda.synchronize()
+            per_call.append(t0.elapsed_time(t1) * 1000.0 / steps)
+            per_kernel.append(statistics.mean(evb[i].elapsed_time(eve[i]) * 1000.0
+                                              for i in range(steps)))
+        return statistics.median(per_call), statistics.median(per_kernel), per_call
+
+
+def cpu_baseline(case, seconds):
+    import oracle
+    orc = oracle.get()
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.forward(case)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per = el / n
+    return {"value": round(case.kv_bytes() / per / 1e9, 4), "unit": "GB/s", "cores": orc.num_threads(),
+            "kind": "oracle", "seconds_per_call": round(per, 4),
+            "sample": f"{n} full oracle call(s) of the timed workload ({case.num_tokens * case.num_q_heads} "
+                      f"rows x {case.kv_keys()} keys), {el:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200, help="timed calls per timed region")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--repeats", type=int, default=5, help="timed regions; the median is reported")
+    ap.add_argument("--workload", default="gqa4_d128_f16_L32768", choices=sorted(workloads()))
+    ap.add_argument("--T", type=int, default=3, help="verify rows per sequence of the timed call")
+    ap.add_argument("--no-t1", action="store_true", help="skip the T=1 comparison call")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this build measures the single-GPU kernel and has no "
+              f"multi-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    mk = workloads()[args.workload]
+
+    case = mk(args.T)
+    run = Runner(case)
+    us, us_kernel, spread = run.time(args.steps, args.warmup, args.repeats)
+    kv = case.kv_bytes()
+    res = {"T": args.T, "us_per_call": us, "us_segment_kernel": us_kernel}
+
+    t1 = None
+    if not args.no_t1 and args.T != 1 and args.workload.startswith("gqa4"):
+        case1 = mk(1)
+        run1 = Runner(case1)
+        us1, us1_kernel, _ = run1.time(args.steps, args.warmup, args.repeats)
+        t1 = {"us_per_call": round(us1, 3), "us_segment_kernel": round(us1_kernel, 3),
+              "kv_gbs": round(case1.kv_bytes() / us1 / 1e3, 1)}
+        del run1
+
+    value = kv / us / 1e3                                  # bytes/µs -> GB/s
+    achieved = kv / us_kernel / 1e3
+    traffic = measured_traffic(args.workload, args.T)
+    dtype = {0: "f16", 1: "bf16", 2: "u8"}[case.kv_dtype]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1000.0, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}_T{args.T}", "num_seqs": case.num_seqs,
+                   "past_lens": case.past_lens.tolist()[:8], "T": case.Ts[:8],
+                   "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads,
+                   "head_dim": case.head_dim, "block_size": case.block_size,
+                   "sliding_window": case.sliding_window, "kv_dtype": dtype,
+                   "kv_bytes_per_call": kv, "pool_copies": run.copies},
+        "us_per_call": round(us, 3),
+        "us_per_call_spread": [round(x, 3) for x in spread],
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": "pa_segment_fp" if case.kv_dtype != 2 else "pa_segment_u8",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "kernel_us": round(us_kernel, 3), "traffic": traffic},
+    }
+    if t1 is not None:
+        line["T1"] = t1
+        line["t_over_t1"] = round(us / t1["us_per_call"], 4)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

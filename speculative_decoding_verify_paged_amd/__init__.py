@@ -1,0 +1,287 @@
+"""Python binding of libpa_verify.so — paged verify attention on MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI (include/pa_verify.h).  torch provides device
+memory and the current stream.  Importing this module loads nothing; the
+first call loads the in-tree library and raises if it is missing — there is
+no fallback.
+
+Functions keep the C names:
+  pa_verify_forward(q, k_cache, v_cache, block_tables, past_lens,
+                    subsequence_begins, max_context_len, scale, out=None, ...)
+  pa_verify_forward_u8(q, k_cache, v_cache, k_scale_zp, v_scale_zp, ...)
+  pa_verify_workspace_bytes(...), pa_verify_make_plan(...),
+  pa_verify_read_status(...), pa_verify_status_string(code)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpa_verify.so")
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_DEVICE_CONTRACT = range(6)
+PA_F16, PA_BF16, PA_U8 = 0, 1, 2
+
+# every symbol include/pa_verify.h declares
+EXPORTS = ("pa_verify_make_plan", "pa_verify_workspace_bytes", "pa_verify_forward",
+           "pa_verify_forward_u8", "pa_verify_read_status", "pa_verify_status_string")
+
+
+class PaVerifyParams(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+        ("sliding_window", ctypes.c_int32), ("num_segments", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p),
+        ("prof_event_begin", ctypes.c_void_p), ("prof_event_end", ctypes.c_void_p),
+    ]
+
+
+class PaVerifyPlan(ctypes.Structure):
+    _fields_ = [
+        ("num_segments", ctypes.c_int32), ("steps_per_segment", ctypes.c_int32),
+        ("keys_per_step", ctypes.c_int32), ("span", ctypes.c_int32),
+        ("waves_per_group", ctypes.c_int32), ("grid", ctypes.c_int32 * 3),
+        ("block_threads", ctypes.c_int32), ("combine_grid", ctypes.c_int32 * 3),
+        ("combine_threads", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+    def as_dict(self):
+        return {f: (list(getattr(self, f)) if f.endswith("grid") else getattr(self, f))
+                for f, _ in self._fields_}
+
+
+class PaVerifyError(RuntimeError):
+    def __init__(self, code: int):
+        super().__init__(pa_verify_status_string(code))
+        self.code = code
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib():
+    """The loaded libpa_verify.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                                      "`python -m speculative_decoding_verify_paged_amd.build`")
+                L = ctypes.CDLL(LIB_PATH)
+                vp, i32, P = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(PaVerifyParams)
+                L.pa_verify_make_plan.argtypes = [P, i32, i32, ctypes.POINTER(PaVerifyPlan)]
+                L.pa_verify_make_plan.restype = ctypes.c_int
+                L.pa_verify_workspace_bytes.argtypes = [P, i32]
+                L.pa_verify_workspace_bytes.restype = ctypes.c_size_t
+                L.pa_verify_forward.argtypes = [vp, vp, vp, vp, vp, vp, i32, ctypes.c_float, vp, P]
+                L.pa_verify_forward.restype = ctypes.c_int
+                L.pa_verify_forward_u8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                                   ctypes.c_float, vp, P]
+                L.pa_verify_forward_u8.restype = ctypes.c_int
+                L.pa_verify_read_status.argtypes = [P, ctypes.POINTER(i32)]
+                L.pa_verify_read_status.restype = ctypes.c_int
+                L.pa_verify_status_string.argtypes = [ctypes.c_int]
+                L.pa_verify_status_string.restype = ctypes.c_char_p
+                _lib = L
+    return _lib
+
+
+def pa_verify_status_string(code: int) -> str:
+    return lib().pa_verify_status_string(int(code)).decode()
+
+
+def make_params(*, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, block_size,
+                num_blocks, max_blocks_per_seq, q_dtype, kv_dtype, sliding_window=0,
+                num_segments=0, workspace=0, workspace_bytes=0, stream=0,
+                prof_event_begin=0, prof_event_end=0) -> PaVerifyParams:
+    return PaVerifyParams(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, block_size,
+                          num_blocks, max_blocks_per_seq, sliding_window, num_segments,
+                          q_dtype, kv_dtype, workspace or None, workspace_bytes, stream or None,
+                          prof_event_begin or None, prof_event_end or None)
+
+
+def pa_verify_make_plan(params: PaVerifyParams, max_context_len: int, num_cus: int) -> dict:
+    plan = PaVerifyPlan()
+    rc = lib().pa_verify_make_plan(ctypes.byref(params), int(max_context_len), int(num_cus),
+                                   ctypes.byref(plan))
+    if rc != PA_OK:
+        raise PaVerifyError(rc)
+    return plan.as_dict()
+
+
+def pa_verify_workspace_bytes(params: PaVerifyParams, max_context_len: int) -> int:
+    return int(lib().pa_verify_workspace_bytes(ctypes.byref(params), int(max_context_len)))
+
+
+# ---------------------------------------------------------------------------
+# torch-facing calls
+# ---------------------------------------------------------------------------
+_ws_cache = {}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return PA_F16
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if t.dtype == torch.uint8:
+        return PA_U8
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def workspace(nbytes: int, device):
+    """A zero-initialised device workspace of at least nbytes, cached per device."""
+    torch = _torch()
+    key = (str(device),)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def _check(t, name, dtype=None, ndim=None, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def _call(u8, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
+          subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
+          ws, stream, prof_events):
+    torch = _torch()
+    dev = q.device
+    _check(q, "q", ndim=3, device=dev)
+    _check(k_cache, "k_cache", ndim=4, device=dev)
+    _check(v_cache, "v_cache", ndim=4, device=dev)
+    for n, t in (("block_tables", block_tables), ("past_lens", past_lens),
+                 ("subsequence_begins", subsequence_begins)):
+        _check(t, n, dtype=torch.int32, device=dev)
+    num_tokens, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != (nb, Hkv, D, bs):
+        raise ValueError("k_cache must be [nb, Hkv, bs, D] and v_cache [nb, Hkv, D, bs]")
+    if k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache dtypes differ")
+    if u8:
+        for n, t in (("k_scale_zp", k_scale_zp), ("v_scale_zp", v_scale_zp)):
+            _check(t, n, dtype=torch.float16, device=dev)
+            if tuple(t.shape) != (nb, Hkv, bs, 2):
+                raise ValueError(f"{n} must be [nb, Hkv, bs, 2] float16")
+    if block_tables.dim() != 2 or past_lens.dim() != 1 or subsequence_begins.dim() != 1:
+        raise ValueError("block_tables must be 2-D, past_lens and subsequence_begins 1-D")
+    num_seqs = past_lens.shape[0]
+    if block_tables.shape[0] != num_seqs or subsequence_begins.shape[0] != num_seqs + 1:
+        raise ValueError("block_tables / subsequence_begins do not match past_lens")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", dtype=q.dtype, device=dev)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    params = make_params(num_seqs=num_seqs, num_tokens=num_tokens, num_q_heads=Hq,
+                         num_kv_heads=Hkv, head_dim=D, block_size=bs, num_blocks=nb,
+                         max_blocks_per_seq=block_tables.shape[1], q_dtype=_dtype_code(q),
+                         kv_dtype=_dtype_code(k_cache), sliding_window=int(sliding_window),
+                         num_segments=int(num_segments))
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    params.stream = stream or None
+    need = pa_verify_workspace_bytes(params, max_context_len)
+    if need == 0:
+        # let the library name the problem
+        need = 256
+    if ws is None:
+        with torch.cuda.device(dev):
+            ws = workspace(need, dev)
+    params.workspace = ws.data_ptr()
+    params.workspace_bytes = ws.numel() * ws.element_size()
+    if prof_events is not None:
+        params.prof_event_begin = prof_events[0]
+        params.prof_event_end = prof_events[1]
+    L = lib()
+    if u8:
+        rc = L.pa_verify_forward_u8(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                    k_scale_zp.data_ptr(), v_scale_zp.data_ptr(),
+                                    block_tables.data_ptr(), past_lens.data_ptr(),
+                                    subsequence_begins.data_ptr(), int(max_context_len),
+                                    float(scale), out.data_ptr(), ctypes.byref(params))
+    else:
+        rc = L.pa_verify_forward(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                 block_tables.data_ptr(), past_lens.data_ptr(),
+                                 subsequence_begins.data_ptr(), int(max_context_len),
+                                 float(scale), out.data_ptr(), ctypes.byref(params))
+    if rc != PA_OK:
+        raise PaVerifyError(rc)
+    return out
+
+
+def pa_verify_forward(q, k_cache, v_cache, block_tables, past_lens, subsequence_begins,
+                      max_context_len: int, scale: float, out=None, *, sliding_window: int = 0,
+                      num_segments: int = 0, workspace=None, stream: Optional[int] = None,
+                      prof_events=None):
+    """Paged verify attention over an f16/bf16 cache; returns ``out``.
+
+    q [num_tokens, Hq, D]; k_cache [nb, Hkv, bs, D]; v_cache [nb, Hkv, D, bs];
+    block_tables [num_seqs, max_blocks_per_seq], past_lens [num_seqs],
+    subsequence_begins [num_seqs + 1] (int32, device).  ``stream`` is a raw
+    hipStream_t (default: torch's current stream); ``prof_events`` is an
+    optional pair of raw hipEvent_t recorded around the segment kernel."""
+    return _call(False, q, k_cache, v_cache, None, None, block_tables, past_lens,
+                 subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
+                 workspace, stream, prof_events)
+
+
+def pa_verify_forward_u8(q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
+                         subsequence_begins, max_context_len: int, scale: float, out=None, *,
+                         sliding_window: int = 0, num_segments: int = 0, workspace=None,
+                         stream: Optional[int] = None, prof_events=None):
+    """The same over a u8 cache with f16 (scale, zero point) per token per KV head."""
+    return _call(True, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
+                 subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
+                 workspace, stream, prof_events)
+
+
+def pa_verify_read_status(device=None) -> int:
+    """Synchronise and read-and-clear the sticky device status word of the cached workspace."""
+    torch = _torch()
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    buf = _ws_cache.get((str(dev),))
+    if buf is None:
+        return PA_OK
+    p = PaVerifyParams()
+    p.workspace = buf.data_ptr()
+    p.workspace_bytes = buf.numel()
+    p.stream = torch.cuda.current_stream(dev).cuda_stream or None
+    st = ctypes.c_int32(0)
+    rc = lib().pa_verify_read_status(ctypes.byref(p), ctypes.byref(st))
+    if rc != PA_OK:
+        raise PaVerifyError(rc)
+    return int(st.value)

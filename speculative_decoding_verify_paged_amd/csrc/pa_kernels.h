@@ -1,0 +1,55 @@
+// pa_kernels.h — what the host side of libpa_verify passes to the gfx950
+// kernels (internal; not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pav {
+
+enum : int { kF16 = 0, kBF16 = 1, kU8 = 2 };
+
+constexpr int kKeysPerStep = 32;     // keys one wavefront consumes per iteration
+constexpr int kRows = 16;            // stacked query rows per MFMA tile (G * T <= 16)
+constexpr int kMaxT = 4;             // verify rows per sequence
+constexpr int kWavesPerGroup = 4;    // wavefronts per segment workgroup
+constexpr int kMaxSegBlocks = 1040;  // LDS slots for a segment's block ids
+constexpr int kDeviceContract = 5;   // value of PA_ERR_DEVICE_CONTRACT
+
+struct SegmentArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* ksz;                   // u8 only: f16 (scale, zero point) per token
+  const void* vsz;
+  const int32_t* bt;
+  const int32_t* past_lens;
+  const int32_t* sb;
+  float* ws_o;                       // [num_tokens, Hq, S, D] unnormalised partial outputs
+  float* ws_ml;                      // [num_tokens, Hq, S, 2] (max in log2 units, sum)
+  int32_t* status;                   // sticky device status word
+  int32_t num_seqs, num_tokens, Hq, Hkv, G;
+  int32_t num_blocks, mbps, window, max_ctx;
+  int32_t S, steps_per_seg;
+  float scale_log2;                  // scale * log2(e)
+};
+
+struct CombineArgs {
+  SegmentArgs seg;
+  void* out;
+  int32_t num_tokens, Hq;
+};
+
+hipError_t launch_segment(const SegmentArgs& a, int kv_dtype, int D, int bs, dim3 grid,
+                          hipStream_t st);
+hipError_t launch_segment_u8(const SegmentArgs& a, int q_dtype, int D, int bs, dim3 grid,
+                             hipStream_t st);
+hipError_t launch_combine(const CombineArgs& a, int out_dtype, int D, dim3 grid, hipStream_t st);
+
+// Resident segment workgroups per CU the kernels are built for (register and
+// LDS budgets fixed at compile time), used by the planner.
+constexpr int groups_per_cu(int kv_dtype, int D) {
+  return (D >= 256) ? 1 : (D >= 128 ? 2 : 4);
+}
+
+}  // namespace pav

@@ -1,0 +1,268 @@
+// pa_verify.hip — host side of libpa_verify.so: argument validation, the
+// launch planner and the C ABI declared in include/pa_verify.h.
+//
+// Nothing here touches the device before the arguments have been checked,
+// so every host-side error path runs without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <mutex>
+#include <set>
+#include <tuple>
+
+#include "pa_kernels.h"
+#include "pa_verify.h"
+
+namespace {
+
+using pav::kKeysPerStep;
+using pav::kWavesPerGroup;
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool is_pow2_in(int v, int lo, int hi) {
+  if (v < lo || v > hi) return false;
+  return (v & (v - 1)) == 0;
+}
+
+// Host-checkable contract.  u8_entry selects which entry point is asking.
+int validate(const pa_verify_params* p, int32_t max_ctx, bool u8_entry) {
+  if (!p) return PA_ERR_INVALID_ARG;
+  if (p->num_seqs < 1 || p->num_tokens < p->num_seqs || p->num_q_heads < 1 ||
+      p->num_kv_heads < 1 || p->head_dim < 1 || p->block_size < 1 || p->num_blocks < 1 ||
+      p->max_blocks_per_seq < 1 || p->sliding_window < 0 || p->num_segments < 0 || max_ctx < 1)
+    return PA_ERR_INVALID_ARG;
+  if (p->num_q_heads % p->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (cdiv(max_ctx, p->block_size) > p->max_blocks_per_seq) return PA_ERR_INVALID_ARG;
+  const int G = p->num_q_heads / p->num_kv_heads;
+  if (!is_pow2_in(G, 1, 8)) return PA_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256) return PA_ERR_UNSUPPORTED;
+  if (p->block_size != 16 && p->block_size != 32 && p->block_size != 64) return PA_ERR_UNSUPPORTED;
+  if (p->q_dtype != PA_F16 && p->q_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (u8_entry) {
+    if (p->kv_dtype != PA_U8) return PA_ERR_UNSUPPORTED;
+  } else {
+    if (p->kv_dtype != p->q_dtype) return PA_ERR_UNSUPPORTED;
+  }
+  // sizes that index 32-bit device arithmetic stay in range
+  if ((int64_t)p->num_blocks * p->num_kv_heads * p->block_size > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)p->num_tokens * p->num_q_heads > INT32_MAX / 4) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_verify_plan* pl) {
+  const int bs = p->block_size;
+  int64_t span = max_ctx;
+  if (p->sliding_window > 0) {
+    // rows of one sequence read at most W + T - 1 keys; the first step is
+    // aligned down to a step boundary
+    span = std::min<int64_t>(span, (int64_t)p->sliding_window + pav::kMaxT - 1 + kKeysPerStep - 1);
+  }
+  const int64_t n_steps = cdiv(span, kKeysPerStep);
+  const int64_t max_sps = ((int64_t)(pav::kMaxSegBlocks - 2) * bs) / kKeysPerStep;
+  int64_t sps;
+  if (p->num_segments > 0) {
+    sps = cdiv(n_steps, std::min<int64_t>(p->num_segments, n_steps));
+  } else {
+    // enough workgroups to fill every CU at the occupancy the kernels are
+    // built for, with an equal number of steps per wavefront
+    const int64_t groups = (int64_t)num_cus * pav::groups_per_cu(p->kv_dtype, p->head_dim);
+    const int64_t s0 = std::max<int64_t>(1, cdiv(groups, (int64_t)p->num_kv_heads * p->num_seqs));
+    sps = cdiv(n_steps, s0 * kWavesPerGroup) * kWavesPerGroup;
+  }
+  sps = std::max<int64_t>(1, std::min(sps, max_sps));
+  const int64_t S = cdiv(n_steps, sps);
+  pl->num_segments = (int32_t)S;
+  pl->steps_per_segment = (int32_t)sps;
+  pl->keys_per_step = kKeysPerStep;
+  pl->span = (int32_t)span;
+  pl->waves_per_group = kWavesPerGroup;
+  pl->grid[0] = (int32_t)S;
+  pl->grid[1] = p->num_kv_heads;
+  pl->grid[2] = p->num_seqs;
+  pl->block_threads = kWavesPerGroup * 64;
+  const int64_t rows = (int64_t)p->num_tokens * p->num_q_heads;
+  pl->combine_grid[0] = (int32_t)cdiv(rows, 4);
+  pl->combine_grid[1] = 1;
+  pl->combine_grid[2] = 1;
+  pl->combine_threads = 256;
+  const size_t ml_bytes = (size_t)rows * S * 2 * sizeof(float);
+  const size_t o_bytes = (size_t)rows * S * p->head_dim * sizeof(float);
+  pl->workspace_bytes = 256 + ((ml_bytes + 255) / 256) * 256 + o_bytes;
+  (void)num_cus;
+  return PA_OK;
+}
+
+// Compute units of the current device, queried once per device.
+int device_cus(int* cus) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+  if (dev >= 0 && dev < 64) {
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return PA_OK;
+    }
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return PA_ERR_HIP;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  *cus = n;
+  return PA_OK;
+}
+
+void maybe_log(const pa_verify_params* p, const pa_verify_plan& pl, int32_t max_ctx) {
+  static const bool on = [] {
+    const char* e = std::getenv("PA_VERIFY_LOG");
+    return e && e[0] && e[0] != '0';
+  }();
+  if (!on) return;
+  static std::mutex mu;
+  static std::set<std::tuple<int, int, int, int, int, int, int>> seen;
+  std::lock_guard<std::mutex> g(mu);
+  auto key = std::make_tuple(p->num_seqs, p->num_kv_heads, p->head_dim, p->block_size,
+                             p->kv_dtype, pl.num_segments, pl.steps_per_segment);
+  if (!seen.insert(key).second) return;
+  std::fprintf(stderr,
+               "[pa_verify] kv=%d D=%d bs=%d Hq=%d Hkv=%d seqs=%d max_ctx=%d W=%d -> S=%d "
+               "steps/seg=%d (x%d keys) grid=(%d,%d,%d)x%d combine=%dx%d ws=%zu B\n",
+               p->kv_dtype, p->head_dim, p->block_size, p->num_q_heads, p->num_kv_heads,
+               p->num_seqs, max_ctx, p->sliding_window, pl.num_segments, pl.steps_per_segment,
+               pl.keys_per_step, pl.grid[0], pl.grid[1], pl.grid[2], pl.block_threads,
+               pl.combine_grid[0], pl.combine_threads, pl.workspace_bytes);
+}
+
+int run(const void* q, const void* k, const void* v, const void* ksz, const void* vsz,
+        const int32_t* bt, const int32_t* past_lens, const int32_t* sb, int32_t max_ctx,
+        float scale, void* out, const pa_verify_params* p, bool u8_entry) {
+  int rc = validate(p, max_ctx, u8_entry);
+  if (rc) return rc;
+  if (!q || !k || !v || !bt || !past_lens || !sb || !out) return PA_ERR_INVALID_ARG;
+  if (u8_entry && (!ksz || !vsz)) return PA_ERR_INVALID_ARG;
+  if (!(scale == scale)) return PA_ERR_INVALID_ARG;
+  int cus = 0;
+  rc = device_cus(&cus);
+  if (rc) return rc;
+  pa_verify_plan pl;
+  make_plan(p, max_ctx, cus, &pl);
+  if (!p->workspace || p->workspace_bytes < pl.workspace_bytes) return PA_ERR_WORKSPACE;
+  maybe_log(p, pl, max_ctx);
+
+  char* ws = static_cast<char*>(p->workspace);
+  const size_t rows = (size_t)p->num_tokens * p->num_q_heads;
+  const size_t ml_bytes = ((rows * pl.num_segments * 2 * sizeof(float) + 255) / 256) * 256;
+  pav::SegmentArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.ksz = ksz;
+  a.vsz = vsz;
+  a.bt = bt;
+  a.past_lens = past_lens;
+  a.sb = sb;
+  a.status = reinterpret_cast<int32_t*>(ws);
+  a.ws_ml = reinterpret_cast<float*>(ws + 256);
+  a.ws_o = reinterpret_cast<float*>(ws + 256 + ml_bytes);
+  a.num_seqs = p->num_seqs;
+  a.num_tokens = p->num_tokens;
+  a.Hq = p->num_q_heads;
+  a.Hkv = p->num_kv_heads;
+  a.G = p->num_q_heads / p->num_kv_heads;
+  a.num_blocks = p->num_blocks;
+  a.mbps = p->max_blocks_per_seq;
+  a.window = p->sliding_window;
+  a.max_ctx = max_ctx;
+  a.S = pl.num_segments;
+  a.steps_per_seg = pl.steps_per_segment;
+  a.scale_log2 = scale * 1.4426950408889634f;
+
+  hipStream_t st = static_cast<hipStream_t>(p->stream);
+  if (p->prof_event_begin &&
+      hipEventRecord(static_cast<hipEvent_t>(p->prof_event_begin), st) != hipSuccess)
+    return PA_ERR_HIP;
+  const dim3 grid(pl.grid[0], pl.grid[1], pl.grid[2]);
+  hipError_t e = u8_entry ? pav::launch_segment_u8(a, p->q_dtype, p->head_dim, p->block_size, grid, st)
+                          : pav::launch_segment(a, p->kv_dtype, p->head_dim, p->block_size, grid, st);
+  if (e != hipSuccess) return PA_ERR_HIP;
+  if (p->prof_event_end &&
+      hipEventRecord(static_cast<hipEvent_t>(p->prof_event_end), st) != hipSuccess)
+    return PA_ERR_HIP;
+  pav::CombineArgs c;
+  c.seg = a;
+  c.out = out;
+  c.num_tokens = p->num_tokens;
+  c.Hq = p->num_q_heads;
+  e = pav::launch_combine(c, p->q_dtype, p->head_dim, dim3(pl.combine_grid[0]), st);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_verify_make_plan(const pa_verify_params* p, int32_t max_context_len, int32_t num_cus,
+                        pa_verify_plan* plan) {
+  if (!plan || num_cus < 1) return PA_ERR_INVALID_ARG;
+  const bool u8 = p && p->kv_dtype == PA_U8;
+  int rc = validate(p, max_context_len, u8);
+  if (rc) return rc;
+  return make_plan(p, max_context_len, num_cus, plan);
+}
+
+size_t pa_verify_workspace_bytes(const pa_verify_params* p, int32_t max_context_len) {
+  const bool u8 = p && p->kv_dtype == PA_U8;
+  if (validate(p, max_context_len, u8)) return 0;
+  int cus = 0;
+  if (device_cus(&cus)) return 0;
+  pa_verify_plan pl;
+  make_plan(p, max_context_len, cus, &pl);
+  return pl.workspace_bytes;
+}
+
+int pa_verify_forward(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* past_lens,
+                      const int32_t* subsequence_begins, int32_t max_context_len, float scale,
+                      void* out, const pa_verify_params* p) {
+  return run(q, k_cache, v_cache, nullptr, nullptr, block_tables, past_lens, subsequence_begins,
+             max_context_len, scale, out, p, false);
+}
+
+int pa_verify_forward_u8(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                         const void* k_scale_zp, const void* v_scale_zp,
+                         const int32_t* block_tables, const int32_t* past_lens,
+                         const int32_t* subsequence_begins, int32_t max_context_len, float scale,
+                         void* out, const pa_verify_params* p) {
+  return run(q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
+             subsequence_begins, max_context_len, scale, out, p, true);
+}
+
+int pa_verify_read_status(const pa_verify_params* p, int32_t* device_status) {
+  if (!p || !device_status || !p->workspace || p->workspace_bytes < sizeof(int32_t))
+    return PA_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(p->stream);
+  if (hipStreamSynchronize(st) != hipSuccess) return PA_ERR_HIP;
+  int32_t w = 0;
+  if (hipMemcpy(&w, p->workspace, sizeof w, hipMemcpyDeviceToHost) != hipSuccess) return PA_ERR_HIP;
+  if (w != 0 && hipMemset(p->workspace, 0, sizeof w) != hipSuccess) return PA_ERR_HIP;
+  *device_status = w == 0 ? PA_OK : PA_ERR_DEVICE_CONTRACT;
+  return PA_OK;
+}
+
+const char* pa_verify_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG: null pointer or inconsistent sizes";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: head_dim, block_size, group size or dtype combination not built";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or smaller than pa_verify_workspace_bytes";
+    case PA_ERR_HIP: return "PA_ERR_HIP: HIP runtime call or kernel launch failed";
+    case PA_ERR_DEVICE_CONTRACT: return "PA_ERR_DEVICE_CONTRACT: device metadata violated the contract";
+  }
+  return "unknown pa_status";
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+"""Helpers shared by the GPU tests: move a pa_inputs.Case to the device, call
+the library through its C ABI binding, and compare with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+import pa_inputs as pi
+
+TOL_FP = 2e-3      # max-abs error bound, f16/bf16 KV
+TOL_U8 = 4e-3      # max-abs error bound, u8 KV dequantised identically
+
+
+def _t(arr, torch_dtype, device):
+    import torch
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch_dtype)
+    return torch.from_numpy(a).to(device)
+
+
+def to_device(case: pi.Case, device="cuda"):
+    import torch
+    qt = torch.float16 if case.q_dtype == pi.F16 else torch.bfloat16
+    if case.kv_dtype == pi.U8:
+        kt = torch.uint8
+    else:
+        kt = torch.float16 if case.kv_dtype == pi.F16 else torch.bfloat16
+    d = dict(q=_t(case.q, qt, device), k_cache=_t(case.k_cache, kt, device),
+             v_cache=_t(case.v_cache, kt, device),
+             block_tables=_t(case.block_tables, None, device),
+             past_lens=_t(case.past_lens, None, device),
+             subsequence_begins=_t(case.subsequence_begins, None, device))
+    if case.kv_dtype == pi.U8:
+        d["k_scale_zp"] = _t(case.k_scale_zp, torch.float16, device)
+        d["v_scale_zp"] = _t(case.v_scale_zp, torch.float16, device)
+    return d
+
+
+def run_gpu(case: pi.Case, dev=None, *, num_segments=0, out=None, max_context_len=None,
+            sync=True, **kw):
+    """Call the library on the case; returns the output tensor (device)."""
+    import torch
+    import speculative_decoding_verify_paged_amd as pav
+    if dev is None:
+        dev = to_device(case)
+    mcl = case.max_context_len if max_context_len is None else max_context_len
+    common = dict(sliding_window=case.sliding_window, num_segments=num_segments, **kw)
+    if case.kv_dtype == pi.U8:
+        o = pav.pa_verify_forward_u8(dev["q"], dev["k_cache"], dev["v_cache"], dev["k_scale_zp"],
+                                     dev["v_scale_zp"], dev["block_tables"], dev["past_lens"],
+                                     dev["subsequence_begins"], mcl, case.scale, out, **common)
+    else:
+        o = pav.pa_verify_forward(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                                  dev["past_lens"], dev["subsequence_begins"], mcl, case.scale,
+                                  out, **common)
+    if sync:
+        torch.cuda.synchronize()
+    return o
+
+
+def to_f64(t) -> np.ndarray:
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def max_err(gpu, ref) -> float:
+    g = to_f64(gpu) if not isinstance(gpu, np.ndarray) else gpu
+    return float(np.max(np.abs(g - ref)))
+
+
+def tol(case) -> float:
+    return TOL_U8 if case.kv_dtype == pi.U8 else TOL_FP
+
+
+def sample_pairs(case, n, seed=0):
+    """n (token, q head) pairs spread over the batch, always including the
+    first and last token and the first and last head."""
+    rng = np.random.default_rng(seed)
+    pairs = {(0, 0), (case.num_tokens - 1, case.num_q_heads - 1)}
+    while len(pairs) < min(n, case.num_tokens * case.num_q_heads):
+        pairs.add((int(rng.integers(case.num_tokens)), int(rng.integers(case.num_q_heads))))
+    return np.array(sorted(pairs), dtype=np.int32)

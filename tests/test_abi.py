@@ -1,0 +1,178 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and every host-side error path returns its code before touching a device.
+Also the launch planner, a pure host function."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import speculative_decoding_verify_paged_amd as pav
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa_verify.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(pa_verify_[a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = pav.lib()
+    names = declared_functions()
+    assert names, "no declarations parsed from the header"
+    assert sorted(names) == sorted(pav.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", pav.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r" T (pa_verify_\w+)", nm))
+    assert set(names) <= exported
+
+
+def test_struct_layout_matches_header():
+    # offsets the C side sees, from the header compiled by the host compiler
+    src = f"""
+#include <stddef.h>
+#include <stdio.h>
+#include "{HEADER}"
+int main(void) {{
+  printf("%zu %zu %zu %zu %zu\\n", sizeof(pa_verify_params), offsetof(pa_verify_params, workspace),
+         offsetof(pa_verify_params, stream), sizeof(pa_verify_plan),
+         offsetof(pa_verify_plan, workspace_bytes));
+  return 0;
+}}
+"""
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", c, "-o", os.path.join(d, "t")], check=True)
+        out = subprocess.run([os.path.join(d, "t")], capture_output=True, text=True).stdout.split()
+    got = [int(x) for x in out]
+    want = [ctypes.sizeof(pav.PaVerifyParams), pav.PaVerifyParams.workspace.offset,
+            pav.PaVerifyParams.stream.offset, ctypes.sizeof(pav.PaVerifyPlan),
+            pav.PaVerifyPlan.workspace_bytes.offset]
+    assert got == want
+
+
+def params(**over):
+    base = dict(num_seqs=1, num_tokens=3, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                block_size=16, num_blocks=2049, max_blocks_per_seq=2049, q_dtype=pav.PA_F16,
+                kv_dtype=pav.PA_F16)
+    base.update(over)
+    return pav.make_params(**base)
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def call(p, max_ctx=32771, u8=False, null=None):
+    L = pav.lib()
+    args = [FAKE] * 6
+    if null is not None:
+        args[null] = None
+    if u8:
+        return L.pa_verify_forward_u8(args[0], args[1], args[2], FAKE, FAKE, args[3], args[4],
+                                      args[5], max_ctx, 0.1, FAKE, ctypes.byref(p))
+    return L.pa_verify_forward(*args, max_ctx, 0.1, FAKE, ctypes.byref(p))
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(num_seqs=0), pav.PA_ERR_INVALID_ARG),
+    (dict(num_tokens=0), pav.PA_ERR_INVALID_ARG),
+    (dict(num_q_heads=30), pav.PA_ERR_INVALID_ARG),           # Hq % Hkv != 0
+    (dict(num_blocks=0), pav.PA_ERR_INVALID_ARG),
+    (dict(max_blocks_per_seq=100), pav.PA_ERR_INVALID_ARG),   # too short for max_context_len
+    (dict(sliding_window=-1), pav.PA_ERR_INVALID_ARG),
+    (dict(num_segments=-2), pav.PA_ERR_INVALID_ARG),
+    (dict(head_dim=96), pav.PA_ERR_UNSUPPORTED),
+    (dict(block_size=8, max_blocks_per_seq=5000), pav.PA_ERR_UNSUPPORTED),
+    (dict(num_q_heads=24, num_kv_heads=8), pav.PA_ERR_UNSUPPORTED),  # G = 3
+    (dict(num_q_heads=128, num_kv_heads=8), pav.PA_ERR_UNSUPPORTED),  # G = 16
+    (dict(kv_dtype=pav.PA_BF16), pav.PA_ERR_UNSUPPORTED),      # (f16, bf16) pair
+    (dict(q_dtype=pav.PA_U8, kv_dtype=pav.PA_U8), pav.PA_ERR_UNSUPPORTED),
+])
+def test_host_errors(over, code):
+    assert call(params(**over)) == code
+
+
+def test_null_pointers_and_entry_mismatch():
+    for k in range(6):
+        assert call(params(), null=k) == pav.PA_ERR_INVALID_ARG
+    assert pav.lib().pa_verify_forward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 0.1, FAKE, None) \
+        == pav.PA_ERR_INVALID_ARG
+    assert call(params(kv_dtype=pav.PA_U8)) == pav.PA_ERR_UNSUPPORTED        # u8 cache, fp entry
+    assert call(params(), u8=True) == pav.PA_ERR_UNSUPPORTED                 # fp cache, u8 entry
+    assert call(params(), max_ctx=0) == pav.PA_ERR_INVALID_ARG
+
+
+def test_missing_workspace_is_reported_before_any_launch():
+    # valid arguments, no workspace: PA_ERR_WORKSPACE on a GPU machine, PA_ERR_HIP
+    # (no device to size the plan for) here; nothing is enqueued either way
+    assert call(params()) in (pav.PA_ERR_WORKSPACE, pav.PA_ERR_HIP)
+
+
+def test_status_strings():
+    for c in range(6):
+        s = pav.pa_verify_status_string(c)
+        assert s.startswith("PA_")
+    assert "unknown" in pav.pa_verify_status_string(99)
+
+
+# ---------------------------------------------------------------------------
+# planner
+# ---------------------------------------------------------------------------
+def plan(max_ctx, cus=256, **over):
+    return pav.pa_verify_make_plan(params(**over), max_ctx, cus)
+
+
+def check_plan_covers(pl, max_ctx, window=0, nseq=1, hkv=8, bs=16):
+    span = max_ctx if not window else min(max_ctx, window + 3 + 31)
+    assert pl["span"] == span
+    steps = -(-span // pl["keys_per_step"])
+    assert pl["num_segments"] * pl["steps_per_segment"] >= steps
+    assert (pl["num_segments"] - 1) * pl["steps_per_segment"] < steps      # no empty tail segment
+    assert pl["grid"] == [pl["num_segments"], hkv, nseq]
+    assert pl["steps_per_segment"] * pl["keys_per_step"] // bs + 2 <= 1040
+
+
+@pytest.mark.parametrize("L,T", [(8192, 1), (8192, 4), (32768, 1), (32768, 3), (32768, 4)])
+def test_plan_fills_the_gpu_at_batch_one(L, T):
+    pl = plan(L + T, num_tokens=T)
+    check_plan_covers(pl, L + T)
+    wgs = pl["grid"][0] * pl["grid"][1] * pl["grid"][2]
+    assert wgs >= 256                                   # at least one workgroup per CU
+    assert pl["steps_per_segment"] % pl["waves_per_group"] == 0   # equal steps per wavefront
+    rows = T * 32
+    assert pl["workspace_bytes"] == 256 + -(-rows * pl["num_segments"] * 8 // 256) * 256 + \
+        rows * pl["num_segments"] * 128 * 4
+
+
+def test_plan_window_and_forced_segments():
+    pl = plan(51202, num_q_heads=32, num_kv_heads=16, head_dim=256, block_size=64,
+              num_blocks=801, max_blocks_per_seq=801, sliding_window=1024, num_tokens=2,
+              q_dtype=pav.PA_BF16, kv_dtype=pav.PA_BF16)
+    check_plan_covers(pl, 51202, window=1024, hkv=16, bs=64)
+    min_s = -(-1025 // ((1040 - 2) * 16 // 32))     # LDS block-id limit per segment
+    for S in (1, 2, 7, 63, 5000):
+        pl = plan(32771, num_segments=S)
+        check_plan_covers(pl, 32771)
+        assert pl["num_segments"] <= max(S, min_s)
+    assert plan(8195, num_segments=1)["num_segments"] == 1
+
+
+def test_plan_long_context_respects_lds_block_limit():
+    pl = plan(1 << 20, max_blocks_per_seq=(1 << 20) // 16, num_blocks=(1 << 20) // 16,
+              num_seqs=1, num_tokens=4, num_segments=1)
+    check_plan_covers(pl, 1 << 20)
+    assert pl["num_segments"] > 1
+
+
+def test_plan_ragged_batch():
+    pl = plan(131072, num_seqs=8, num_tokens=20, max_blocks_per_seq=8192, num_blocks=60000)
+    check_plan_covers(pl, 131072, nseq=8)

@@ -1,0 +1,193 @@
+"""GPU parity: the HIP path against the fp64 oracle, element by element.
+
+Bars: max-abs error <= 2e-3 for f16/bf16 KV, <= 4e-3 for u8 KV (outputs are
+rounded to the q dtype by the GPU; the oracle is unrounded).  Bitwise checks
+where the arithmetic order cannot change: block relabelling, repeated runs,
+poisoned unread slots.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import pa_inputs as pi
+from gpu_util import (max_err, run_gpu, sample_pairs, to_device, to_f64, tol)
+
+pytestmark = pytest.mark.gpu
+
+
+def _full(case, **kw):
+    ref = oracle.forward(case)
+    got = run_gpu(case, **kw)
+    err = max_err(got, ref)
+    print(f"{case.name}: max err {err:.3e}", flush=True)
+    assert np.all(np.isfinite(to_f64(got))), case.name
+    assert err <= tol(case), f"{case.name}: max err {err}"
+    return got, ref
+
+
+def _sampled(case, n=96, **kw):
+    pairs = sample_pairs(case, n)
+    ref = oracle.forward(case, pairs=pairs)
+    got = to_f64(run_gpu(case, **kw))
+    g = got[pairs[:, 0], pairs[:, 1]]
+    err = float(np.max(np.abs(g - ref)))
+    print(f"{case.name}: max err over {len(pairs)} sampled rows {err:.3e}", flush=True)
+    assert np.all(np.isfinite(got)), case.name
+    assert err <= tol(case), f"{case.name}: max err {err}"
+    return got
+
+
+def test_tiny():
+    _full(pi.config1())
+    _full(pi.config1(rep=1, poison=True))
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_gqa4_d128_8k(T):
+    _full(pi.config2(8192, T, poison=True))
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_gqa4_d128_32k(T):
+    _full(pi.config2(32768, T))
+
+
+@pytest.mark.parametrize("L", [32768, 51200])
+def test_swa_pair_global_and_window(L):
+    _full(pi.config4(L, window=0))
+    _full(pi.config4(L, window=1024, poison=True))
+
+
+def test_ragged_batch():
+    _sampled(pi.config5(poison=True), n=160)
+
+
+def test_max_context():
+    case = pi.build_case([9, 131068, 4], [131068], [4], num_q_heads=32, num_kv_heads=8,
+                         head_dim=128, block_size=16, q_dtype=pi.BF16, kv_dtype=pi.BF16,
+                         name="ctx131072_T4")
+    _sampled(case, n=48)
+
+
+def _small_cases():
+    rng = np.random.default_rng(77)
+    out = []
+    k = 0
+    for D in (64, 128, 256):
+        for bs in (16, 32, 64):
+            for G in (1, 2, 4, 8):
+                dt = pi.F16 if (k % 2 == 0) else pi.BF16
+                Tmax = max(1, min(4, 16 // G))
+                T = int(rng.integers(1, Tmax + 1))
+                L = int(rng.choice([0, 1, 15, 31, 32, 33, 100, int(rng.integers(0, 700))]))
+                W = int(rng.choice([0, 0, 1, 7, 40, 300]))
+                Hkv = int(rng.choice([1, 2, 3]))
+                out.append(pi.build_case([500, k], [L], [T], num_q_heads=G * Hkv,
+                                         num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                                         q_dtype=dt, kv_dtype=dt, sliding_window=W,
+                                         spare_blocks=2, poison=True,
+                                         name=f"small_D{D}_bs{bs}_G{G}_T{T}_L{L}_W{W}"))
+                k += 1
+    return out
+
+
+def test_small_shapes_all_instances():
+    for case in _small_cases():
+        _full(case)
+
+
+def test_small_ragged_batches():
+    for rep in range(4):
+        _full(pi.config5(rep=rep, lo=1, hi=3000, poison=True))
+
+
+@pytest.mark.parametrize("S", [1, 2, 7, 0, 10 ** 6])
+def test_segment_count_invariance(S):
+    case = pi.config2(8192, 3)
+    got, _ = _full(case, num_segments=S)
+    again = run_gpu(case, num_segments=S)
+    assert np.array_equal(to_f64(got), to_f64(again)), "not bitwise repeatable"
+
+
+def _relabel(case, seed):
+    """Same logical cache under another physical block numbering."""
+    rng = np.random.default_rng(seed)
+    pi_ = rng.permutation(case.num_blocks).astype(np.int32)
+    new = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+    new.k_cache = np.empty_like(case.k_cache)
+    new.v_cache = np.empty_like(case.v_cache)
+    new.k_cache[pi_] = case.k_cache
+    new.v_cache[pi_] = case.v_cache
+    if case.kv_dtype == pi.U8:
+        new.k_scale_zp = np.empty_like(case.k_scale_zp)
+        new.v_scale_zp = np.empty_like(case.v_scale_zp)
+        new.k_scale_zp[pi_] = case.k_scale_zp
+        new.v_scale_zp[pi_] = case.v_scale_zp
+    bt = case.block_tables.copy()
+    used = bt != pi.BAD_BLOCK_ID
+    bt[used] = pi_[bt[used]]
+    new.block_tables = bt
+    return new
+
+
+def test_block_relabelling_is_bitwise_invisible():
+    for case in (pi.config2(8192, 3), pi.config4(4096, window=1024, poison=True),
+                 pi.config5(rep=2, lo=100, hi=5000, poison=True)):
+        a = to_f64(run_gpu(case))
+        b = to_f64(run_gpu(_relabel(case, 3)))
+        assert np.array_equal(a, b), case.name
+
+
+def test_poisoned_slots_change_nothing():
+    for mk in (lambda p: pi.config2(8192, 4, rep=5, poison=p),
+               lambda p: pi.config4(3000, window=1024, rep=5, poison=p)):
+        a = to_f64(run_gpu(mk(False)))
+        b = to_f64(run_gpu(mk(True)))
+        assert np.array_equal(a, b)
+
+
+def test_rows_match_single_token_decodes():
+    case = pi.config2(8192, 4, rep=2)
+    full = to_f64(run_gpu(case))
+    dev = to_device(case)
+    import torch
+    for i in range(4):
+        one = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+        one.q = case.q[i:i + 1]
+        one.num_tokens = 1
+        one.past_lens = np.array([8192 + i], np.int32)
+        one.subsequence_begins = np.array([0, 1], np.int32)
+        got = to_f64(run_gpu(one))
+        assert np.max(np.abs(got[0] - full[i])) <= 2e-3, i
+
+
+def test_device_contract_violations_give_nan_and_status():
+    import speculative_decoding_verify_paged_amd as pav
+    base = pi.build_case([31], [300, 200], [2, 3], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                         block_size=16, name="contract")
+    ref = oracle.forward(base)
+    assert pav.pa_verify_read_status() in (pav.PA_OK, pav.PA_ERR_DEVICE_CONTRACT)
+    # T = 5 for sequence 1: its rows are NaN, sequence 0 is untouched
+    bad = pi.Case(**{f: getattr(base, f) for f in base.__dataclass_fields__})
+    bad.subsequence_begins = np.array([0, 2, 7], np.int32)
+    bad.q = np.concatenate([base.q, base.q[:2]], axis=0)
+    bad.num_tokens = 7
+    bad.max_context_len = 210
+    got = to_f64(run_gpu(bad))
+    assert pav.pa_verify_read_status() == pav.PA_ERR_DEVICE_CONTRACT
+    assert np.all(np.isnan(got[2:]))
+    assert np.max(np.abs(got[:2] - ref[:2])) <= 2e-3
+    assert pav.pa_verify_read_status() == pav.PA_OK           # read clears it
+    # a used block id out of range
+    bad2 = pi.Case(**{f: getattr(base, f) for f in base.__dataclass_fields__})
+    bt = base.block_tables.copy()
+    bt[0, 5] = base.num_blocks + 7
+    bad2.block_tables = bt
+    got = to_f64(run_gpu(bad2))
+    assert pav.pa_verify_read_status() == pav.PA_ERR_DEVICE_CONTRACT
+    assert np.all(np.isnan(got[:2]))
+    assert np.max(np.abs(got[2:] - ref[2:])) <= 2e-3
+    # past_len + T beyond max_context_len
+    got = to_f64(run_gpu(base, max_context_len=250))
+    assert pav.pa_verify_read_status() == pav.PA_ERR_DEVICE_CONTRACT
+    assert np.all(np.isnan(got[:2]))
