@@ -8,7 +8,9 @@ combine kernel).  The same call with T=1 is timed beside it for the T-cost
 ratio.  Inputs are resident in HBM before timing; KV pools are rotated over
 >= 1 GiB of copies so the 256 MB Infinity Cache cannot serve them.
 
-value = algorithmic KV bytes of one call / measured time per call (GB/s).
+value = algorithmic KV bytes of one call / device time per call (GB/s), the
+calls replayed from a HIP graph so host launch overhead is excluded (the
+eager per-call time is reported beside it).
 roofline = the segment kernel's algorithmic KV bytes / its own average
 duration from HIP events recorded around it in the timed region, against
 MI355X's 8 TB/s HBM peak.  cpu_baseline = the fp64 oracle timed on the host
@@ -94,22 +96,54 @@ class Runner:
         self.out = torch.empty_like(self.dev["q"])
         self.stream = torch.cuda.current_stream()
 
-    def call(self, i, prof=None):
+    def call(self, i, prof=None, stream=None):
         c, d = self.case, self.pools[i % self.copies]
+        st = self.stream.cuda_stream if stream is None else stream
         if c.kv_dtype == 2:
             self.pav.pa_verify_forward_u8(d["q"], d["k_cache"], d["v_cache"], d["k_scale_zp"],
                                           d["v_scale_zp"], d["block_tables"], d["past_lens"],
                                           d["subsequence_begins"], c.max_context_len, c.scale,
                                           self.out, sliding_window=c.sliding_window,
-                                          stream=self.stream.cuda_stream, prof_events=prof)
+                                          stream=st, prof_events=prof)
         else:
             self.pav.pa_verify_forward(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
                                        d["past_lens"], d["subsequence_begins"], c.max_context_len,
                                        c.scale, self.out, sliding_window=c.sliding_window,
-                                       stream=self.stream.cuda_stream, prof_events=prof)
+                                       stream=st, prof_events=prof)
+
+    def time_graph(self, steps, warmup, repeats):
+        """µs per call with the `steps` calls captured in one HIP graph and
+        replayed: device time per call, host launch overhead excluded (a
+        serving engine replays the verify forward from a graph).  Median and
+        all values over `repeats` replays."""
+        import torch
+        for i in range(warmup):
+            self.call(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream().cuda_stream
+            for i in range(steps):
+                self.call(i, stream=cs)
+        torch.cuda.synchronize()
+        g.replay()                                      # untimed replay
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        per_call = []
+        for r in range(repeats):
+            torch.cuda.synchronize()
+            t0.record()
+            g.replay()
+            t1.record()
+            torch.cuda.synchronize()
+            per_call.append(t0.elapsed_time(t1) * 1000.0 / steps)
+        del g
+        return statistics.median(per_call), per_call
 
     def time(self, steps, warmup, repeats):
-        """Median µs per call and median segment-kernel µs over `repeats` timed regions."""
+        """Eager launches: median µs per call and the segment kernel's mean
+        duration from events its own dispatch stamps, over `repeats` regions."""
         import torch
         for i in range(warmup):
             self.call(i)
@@ -133,6 +167,41 @@ class Runner:
             per_kernel.append(statistics.mean(evb[i].elapsed_time(eve[i]) * 1000.0
                                               for i in range(steps)))
         return statistics.median(per_call), statistics.median(per_kernel), per_call
+
+
+def read_ceiling():
+    """Best HBM streaming-read rate of a plain 16-byte-load kernel over 4 GiB
+    (beyond the 256 MB Infinity Cache), GB/s.  Also runs one 1 GiB copy, the
+    known-size kernel that calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "speculative_decoding_verify_paged_amd", "libpa_membench.so"))
+    lib.pa_membench_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                     ctypes.c_int, ctypes.c_void_p]
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    best = 0.0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for grid in (1024, 2048, 4096, 8192, 16384):
+        for rep in range(3):
+            torch.cuda.synchronize()
+            e0.record()
+            rc = lib.pa_membench_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, st.cuda_stream)
+            e1.record()
+            torch.cuda.synchronize()
+            assert rc == 0
+            best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    lib.pa_membench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                     ctypes.c_int, ctypes.c_void_p]
+    half = 1 << 30
+    rc = lib.pa_membench_copy(buf.data_ptr() + half, buf.data_ptr(), half, 4096, st.cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0
+    del buf
+    return round(best, 1)
 
 
 def cpu_baseline(case, seconds):
@@ -164,6 +233,7 @@ def main():
     ap.add_argument("--no-t1", action="store_true", help="skip the T=1 comparison call")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the HBM read-ceiling kernel")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -178,18 +248,21 @@ def main():
 
     case = mk(args.T)
     run = Runner(case)
-    us, us_kernel, spread = run.time(args.steps, args.warmup, args.repeats)
+    us, spread = run.time_graph(args.steps, args.warmup, args.repeats)
+    us_eager, us_kernel, _ = run.time(args.steps, args.warmup, args.repeats)
     kv = case.kv_bytes()
-    res = {"T": args.T, "us_per_call": us, "us_segment_kernel": us_kernel}
+    del run
 
     t1 = None
     if not args.no_t1 and args.T != 1 and args.workload.startswith("gqa4"):
         case1 = mk(1)
         run1 = Runner(case1)
-        us1, us1_kernel, _ = run1.time(args.steps, args.warmup, args.repeats)
+        us1, _ = run1.time_graph(args.steps, args.warmup, args.repeats)
+        _, us1_kernel, _ = run1.time(args.steps, args.warmup, args.repeats)
         t1 = {"us_per_call": round(us1, 3), "us_segment_kernel": round(us1_kernel, 3),
               "kv_gbs": round(case1.kv_bytes() / us1 / 1e3, 1)}
         del run1
+    ceiling = None if args.no_ceiling else read_ceiling()
 
     value = kv / us / 1e3                                  # bytes/µs -> GB/s
     achieved = kv / us_kernel / 1e3
@@ -216,7 +289,9 @@ def main():
                    "kv_bytes_per_call": kv, "pool_copies": run.copies},
         "us_per_call": round(us, 3),
         "us_per_call_spread": [round(x, 3) for x in spread],
+        "us_per_call_eager": round(us_eager, 3),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "hbm_read_ceiling_gbs": ceiling,
         "roofline": {"bound": "hbm", "kernel": "pa_segment_fp" if case.kv_dtype != 2 else "pa_segment_u8",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),

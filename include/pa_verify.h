@@ -37,7 +37,7 @@
  *  k_cache       [num_blocks, Hkv, block_size, D]     one page tile per (block, head)
  *  v_cache       [num_blocks, Hkv, D, block_size]     V pages are stored d-major
  *                (transposed) so that the PV contraction over keys reads
- *                keys contiguously; see DESIGN notes in the library source.
+ *                8 consecutive keys of one d as a single 16-byte load.
  *  k_scale_zp,   [num_blocks, Hkv, block_size, 2]     f16 (scale, zero_point) per
  *  v_scale_zp    token per KV head, u8 variant only; dequant = (u - zp) * scale
  *  block_tables  [num_seqs, max_blocks_per_seq] int32 physical block ids
@@ -105,8 +105,10 @@ typedef struct pa_verify_params {
                                   are the sticky device status word: zero them once at allocation */
   size_t workspace_bytes;
   void* stream;                /* hipStream_t to enqueue on; NULL = the null stream */
-  void* prof_event_begin;      /* optional hipEvent_t recorded right before the segment kernel */
-  void* prof_event_end;        /* optional hipEvent_t recorded right after the segment kernel */
+  void* prof_event_begin;      /* optional hipEvent_t stamped when the segment kernel starts */
+  void* prof_event_end;        /* optional hipEvent_t stamped when the segment kernel ends; both
+                                  are set by the kernel's own dispatch (hipExtLaunchKernel),
+                                  so their elapsed time is the kernel's duration */
 } pa_verify_params;
 
 /* The launch plan, a pure function of host scalars: segment count S, keys per

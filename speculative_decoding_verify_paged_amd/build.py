@@ -17,6 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa_verify.so")
+MEMBENCH_SRC = os.path.join(PKG, "membench", "membench.hip")
+MEMBENCH_LIB = os.path.join(PKG, "libpa_membench.so")
 ARCH = "gfx950"
 
 FLAGS = [
@@ -48,19 +50,26 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra_flags=(), verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(extra_flags=(), verbose: bool = False) -> str:
+    """Build libpa_verify.so (the attention library) and libpa_membench.so
+    (the read-ceiling and copy reference kernels the benchmark uses)."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources() + [MEMBENCH_SRC]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], MEMBENCH_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {MEMBENCH_LIB}")
     return LIB
 
 

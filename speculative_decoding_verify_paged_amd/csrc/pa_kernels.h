@@ -40,10 +40,11 @@ struct CombineArgs {
   int32_t num_tokens, Hq;
 };
 
+// ev0/ev1: optional events timestamped by the segment kernel's own dispatch
 hipError_t launch_segment(const SegmentArgs& a, int kv_dtype, int D, int bs, dim3 grid,
-                          hipStream_t st);
+                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_segment_u8(const SegmentArgs& a, int q_dtype, int D, int bs, dim3 grid,
-                             hipStream_t st);
+                             hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_combine(const CombineArgs& a, int out_dtype, int D, dim3 grid, hipStream_t st);
 
 // Resident segment workgroups per CU the kernels are built for (register and

@@ -26,7 +26,7 @@
 //   online softmax over the step's keys per row (lane-local, 2 cross-lane max)
 //   O^T[d, r] += V^T[d, key] . P^T[key, r] A = V^T read from the d-major V page
 //                                          (8 keys contiguous, 16 B per lane),
-//                                          B = P converted to f16/bf16 in place
+//                                          B = P split into hi + lo f16/bf16 parts
 // Every lane owns one stacked row r = lane % 16 in all three products, so the
 // softmax state and its rescale never leave the lane.  The cross-lane steps
 // are two shuffles for the row max and the workgroup merge at the end.
@@ -35,6 +35,7 @@
 // contraction runs over keys, and the MFMA operand wants 8 consecutive keys
 // per lane, which that layout makes one 16-byte load instead of eight 2-byte
 // gathers or an LDS transpose.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -64,19 +65,30 @@ __device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
   }
 }
 
-// Eight softmax weights as one MFMA operand (round to nearest even).
+// Eight softmax weights as two MFMA operands, hi = rne16(p) and
+// lo = rne16(p - hi): PV runs on both, so the weights keep ~16 more bits than
+// one 16-bit rounding (bf16 alone would cost up to 2^-9 of max|v| when a few
+// keys dominate).
 template <int KV>
-__device__ __forceinline__ u32x4 pack8(const float (&p)[8]) {
+__device__ __forceinline__ void pack8_split(const float (&p)[8], u32x4& hi, u32x4& lo) {
   if constexpr (KV == kF16) {
-    f16x8 h;
+    f16x8 h, l;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = (_Float16)p[e];
-    return __builtin_bit_cast(u32x4, h);
+    for (int e = 0; e < 8; ++e) {
+      h[e] = (_Float16)p[e];
+      l[e] = (_Float16)(p[e] - (float)h[e]);
+    }
+    hi = __builtin_bit_cast(u32x4, h);
+    lo = __builtin_bit_cast(u32x4, l);
   } else {
-    bf16x8 h;
+    bf16x8 h, l;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = (__bf16)p[e];
-    return __builtin_bit_cast(u32x4, h);
+    for (int e = 0; e < 8; ++e) {
+      h[e] = (__bf16)p[e];
+      l[e] = (__bf16)(p[e] - (float)h[e]);
+    }
+    hi = __builtin_bit_cast(u32x4, h);
+    lo = __builtin_bit_cast(u32x4, l);
   }
 }
 
@@ -268,11 +280,13 @@ void pa_segment_fp(SegmentArgs a) {
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    const u32x4 pb = pack8<KV>(p);
+    u32x4 pb_hi, pb_lo;
+    pack8_split<KV>(p, pb_hi, pb_lo);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       o[dt] *= alpha;
-      o[dt] = mfma32<KV>(vr[dt], pb, o[dt]);
+      o[dt] = mfma32<KV>(vr[dt], pb_hi, o[dt]);
+      o[dt] = mfma32<KV>(vr[dt], pb_lo, o[dt]);
     }
   };
 
@@ -346,68 +360,86 @@ void pa_segment_fp(SegmentArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Combine kernel: one wavefront per (token, q head).
+// Combine kernel: one workgroup per (token, q head).  Thread t owns d columns
+// [c4, c4 + 4) of the segments sub, sub + NSUB, ...; it merges them with the
+// same online rescaling as the segment kernel (every load independent of the
+// previous iteration's arithmetic, so they all go out at once), then the
+// NSUB partial states are merged through LDS in a fixed order.
 // ---------------------------------------------------------------------------
 template <int D, int OUT>
 __global__ __launch_bounds__(256) void pa_combine(CombineArgs a) {
-  constexpr int PER = D / kWave;                              // output values per lane
-  const int lane = threadIdx.x & (kWave - 1);
-  const int pair = blockIdx.x * 4 + threadIdx.x / kWave;
-  if (pair >= a.num_tokens * a.Hq) return;
+  constexpr int LPS = D / 4;                                  // threads per segment row
+  constexpr int NSUB = 256 / LPS;                             // segment rows in flight
+  __shared__ float s_m[NSUB];
+  __shared__ float s_den[NSUB];
+  __shared__ __attribute__((aligned(16))) f32x4 s_acc[NSUB][LPS];
+
+  const int pair = blockIdx.x;                                // token * Hq + q head
+  const int tid = threadIdx.x;
+  const int sub = tid / LPS;
+  const int col = tid % LPS;
   const int n = pair / a.Hq;
 
   // sequence of token n (subsequence_begins is cumulative)
   int s = 0;
   while (s < a.seg.num_seqs && !(n < a.seg.sb[s + 1])) ++s;
   bool ok = s < a.seg.num_seqs && n >= a.seg.sb[s];
-  SeqInfo si;
+  int n_seg = 0;
   if (ok) {
-    si = seq_info(a.seg, s);
+    const SeqInfo si = seq_info(a.seg, s);
     ok = si.ok;
+    n_seg = min(a.seg.S, (si.n_steps + a.seg.steps_per_seg - 1) / a.seg.steps_per_seg);
   }
-  float res[PER];
-  if (!ok) {
-#pragma unroll
-    for (int k = 0; k < PER; ++k) res[k] = NAN;
-    if (lane == 0) atomicExch(a.seg.status, kDeviceContract);
-  } else {
-    const int n_seg = min(a.seg.S, (si.n_steps + a.seg.steps_per_seg - 1) / a.seg.steps_per_seg);
-    const float* ml = a.seg.ws_ml + (size_t)pair * a.seg.S * 2;
-    const float* op = a.seg.ws_o + (size_t)pair * a.seg.S * D + lane * PER;
-    float M = -INFINITY;
-    bool nan_seen = false;
-    for (int jj = lane; jj < n_seg; jj += kWave) {
-      const float mj = ml[jj * 2];
-      nan_seen |= mj != mj;
-      M = fmaxf(M, mj);
-    }
-#pragma unroll
-    for (int w = 32; w >= 1; w >>= 1) M = fmaxf(M, __shfl_xor(M, w, kWave));
-    nan_seen = __any(nan_seen);
-    float acc[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-    float den = 0.f;
-    for (int jj = 0; jj < n_seg; ++jj) {
-      const float mj = ml[jj * 2];
-      if (mj == -INFINITY) continue;
-      const float f = __builtin_amdgcn_exp2f(mj - M);
-      den += f * ml[jj * 2 + 1];
-#pragma unroll
-      for (int k = 0; k < PER; ++k) acc[k] += f * op[(size_t)jj * D + k];
-    }
-    const float inv = 1.f / den;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) res[k] = nan_seen ? NAN : acc[k] * inv;
+  const float* ml = a.seg.ws_ml + (size_t)pair * a.seg.S * 2;
+  const float* op = a.seg.ws_o + (size_t)pair * a.seg.S * D + col * 4;
+  float m = -INFINITY, den = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  bool nan_seen = false;
+#pragma unroll 4
+  for (int jj = sub; jj < n_seg; jj += NSUB) {
+    const float mj = ml[jj * 2];
+    const float lj = ml[jj * 2 + 1];
+    const f32x4 oj = *reinterpret_cast<const f32x4*>(op + (size_t)jj * D);
+    nan_seen |= mj != mj;
+    const float m_new = fmaxf(m, mj);
+    const float base = m_new == -INFINITY ? 0.f : m_new;
+    const float sc = __builtin_amdgcn_exp2f(m - base);
+    const float f = __builtin_amdgcn_exp2f(mj - base);
+    den = den * sc + f * lj;
+    // a segment in which this row saw no key left its O slot unwritten
+    acc = mj == -INFINITY ? acc * sc : acc * sc + f * oj;
+    m = m_new;
   }
+  if (col == 0) {
+    s_m[sub] = m;
+    s_den[sub] = den;
+  }
+  s_acc[sub][col] = acc;
+  const bool bad = __syncthreads_or(nan_seen || !ok);
+  if (bad && tid == 0) atomicExch(a.seg.status, kDeviceContract);
+  if (tid >= LPS) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NSUB; ++k) M = fmaxf(M, s_m[k]);
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  float dsum = 0.f;
+#pragma unroll
+  for (int k = 0; k < NSUB; ++k) {
+    const float f = s_m[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[k] - M);
+    num += f * s_acc[k][tid];
+    dsum += f * s_den[k];
+  }
+  float res[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) res[k] = bad ? NAN : num[k] / dsum;
   if constexpr (OUT == kF16) {
-    _Float16* out = reinterpret_cast<_Float16*>(a.out) + (size_t)pair * D + lane * PER;
+    _Float16* out = reinterpret_cast<_Float16*>(a.out) + (size_t)pair * D + tid * 4;
 #pragma unroll
-    for (int k = 0; k < PER; ++k) out[k] = (_Float16)res[k];
+    for (int k = 0; k < 4; ++k) out[k] = (_Float16)res[k];
   } else {
-    __bf16* out = reinterpret_cast<__bf16*>(a.out) + (size_t)pair * D + lane * PER;
+    __bf16* out = reinterpret_cast<__bf16*>(a.out) + (size_t)pair * D + tid * 4;
 #pragma unroll
-    for (int k = 0; k < PER; ++k) out[k] = (__bf16)res[k];
+    for (int k = 0; k < 4; ++k) out[k] = (__bf16)res[k];
   }
 }
 
@@ -415,41 +447,50 @@ __global__ __launch_bounds__(256) void pa_combine(CombineArgs a) {
 // Instances and launchers.
 // ---------------------------------------------------------------------------
 template <int KV, int D, int BS>
-static hipError_t launch_segment_fp(const SegmentArgs& a, dim3 grid, hipStream_t st) {
-  constexpr int WPE = D >= 256 ? 1 : 2;
-  hipLaunchKernelGGL((pa_segment_fp<KV, D, BS, kWavesPerGroup, WPE>), grid,
-                     dim3(kWavesPerGroup * kWave), 0, st, a);
+static hipError_t launch_segment_fp(const SegmentArgs& a, dim3 grid, hipStream_t st,
+                                    hipEvent_t ev0, hipEvent_t ev1) {
+  constexpr int WPE = D >= 256 ? 1 : (D >= 128 ? 2 : 4);
+  // with events, the dispatch itself timestamps the kernel's start and end
+  if (ev0 || ev1)
+    hipExtLaunchKernelGGL((pa_segment_fp<KV, D, BS, kWavesPerGroup, WPE>), grid,
+                          dim3(kWavesPerGroup * kWave), 0, st, ev0, ev1, 0, a);
+  else
+    hipLaunchKernelGGL((pa_segment_fp<KV, D, BS, kWavesPerGroup, WPE>), grid,
+                       dim3(kWavesPerGroup * kWave), 0, st, a);
   return hipGetLastError();
 }
 
 template <int KV, int D>
-static hipError_t dispatch_bs(const SegmentArgs& a, int bs, dim3 grid, hipStream_t st) {
+static hipError_t dispatch_bs(const SegmentArgs& a, int bs, dim3 grid, hipStream_t st,
+                              hipEvent_t e0, hipEvent_t e1) {
   switch (bs) {
-    case 16: return launch_segment_fp<KV, D, 16>(a, grid, st);
-    case 32: return launch_segment_fp<KV, D, 32>(a, grid, st);
-    case 64: return launch_segment_fp<KV, D, 64>(a, grid, st);
+    case 16: return launch_segment_fp<KV, D, 16>(a, grid, st, e0, e1);
+    case 32: return launch_segment_fp<KV, D, 32>(a, grid, st, e0, e1);
+    case 64: return launch_segment_fp<KV, D, 64>(a, grid, st, e0, e1);
   }
   return hipErrorInvalidValue;
 }
 
 template <int KV>
-static hipError_t dispatch_d(const SegmentArgs& a, int D, int bs, dim3 grid, hipStream_t st) {
+static hipError_t dispatch_d(const SegmentArgs& a, int D, int bs, dim3 grid, hipStream_t st,
+                             hipEvent_t e0, hipEvent_t e1) {
   switch (D) {
-    case 64: return dispatch_bs<KV, 64>(a, bs, grid, st);
-    case 128: return dispatch_bs<KV, 128>(a, bs, grid, st);
-    case 256: return dispatch_bs<KV, 256>(a, bs, grid, st);
+    case 64: return dispatch_bs<KV, 64>(a, bs, grid, st, e0, e1);
+    case 128: return dispatch_bs<KV, 128>(a, bs, grid, st, e0, e1);
+    case 256: return dispatch_bs<KV, 256>(a, bs, grid, st, e0, e1);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_segment(const SegmentArgs& a, int kv_dtype, int D, int bs, dim3 grid,
-                          hipStream_t st) {
-  if (kv_dtype == kF16) return dispatch_d<kF16>(a, D, bs, grid, st);
-  if (kv_dtype == kBF16) return dispatch_d<kBF16>(a, D, bs, grid, st);
+                          hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  if (kv_dtype == kF16) return dispatch_d<kF16>(a, D, bs, grid, st, e0, e1);
+  if (kv_dtype == kBF16) return dispatch_d<kBF16>(a, D, bs, grid, st, e0, e1);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_segment_u8(const SegmentArgs&, int, int, int, dim3, hipStream_t) {
+hipError_t launch_segment_u8(const SegmentArgs&, int, int, int, dim3, hipStream_t, hipEvent_t,
+                             hipEvent_t) {
   return hipErrorNotSupported;
 }
 

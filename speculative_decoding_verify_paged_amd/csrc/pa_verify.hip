@@ -85,7 +85,7 @@ int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_ve
   pl->grid[2] = p->num_seqs;
   pl->block_threads = kWavesPerGroup * 64;
   const int64_t rows = (int64_t)p->num_tokens * p->num_q_heads;
-  pl->combine_grid[0] = (int32_t)cdiv(rows, 4);
+  pl->combine_grid[0] = (int32_t)rows;
   pl->combine_grid[1] = 1;
   pl->combine_grid[2] = 1;
   pl->combine_threads = 256;
@@ -182,16 +182,14 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
   a.scale_log2 = scale * 1.4426950408889634f;
 
   hipStream_t st = static_cast<hipStream_t>(p->stream);
-  if (p->prof_event_begin &&
-      hipEventRecord(static_cast<hipEvent_t>(p->prof_event_begin), st) != hipSuccess)
-    return PA_ERR_HIP;
+  hipEvent_t e0 = static_cast<hipEvent_t>(p->prof_event_begin);
+  hipEvent_t e1 = static_cast<hipEvent_t>(p->prof_event_end);
   const dim3 grid(pl.grid[0], pl.grid[1], pl.grid[2]);
-  hipError_t e = u8_entry ? pav::launch_segment_u8(a, p->q_dtype, p->head_dim, p->block_size, grid, st)
-                          : pav::launch_segment(a, p->kv_dtype, p->head_dim, p->block_size, grid, st);
+  hipError_t e =
+      u8_entry ? pav::launch_segment_u8(a, p->q_dtype, p->head_dim, p->block_size, grid, st, e0, e1)
+               : pav::launch_segment(a, p->kv_dtype, p->head_dim, p->block_size, grid, st, e0, e1);
+  if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
   if (e != hipSuccess) return PA_ERR_HIP;
-  if (p->prof_event_end &&
-      hipEventRecord(static_cast<hipEvent_t>(p->prof_event_end), st) != hipSuccess)
-    return PA_ERR_HIP;
   pav::CombineArgs c;
   c.seg = a;
   c.out = out;

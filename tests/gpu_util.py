@@ -72,6 +72,23 @@ def tol(case) -> float:
     return TOL_U8 if case.kv_dtype == pi.U8 else TOL_FP
 
 
+def half_ulp(ref: np.ndarray, dtype: int) -> np.ndarray:
+    """Half a unit in the last place of the output dtype at |ref| (the most
+    round-to-nearest-even can move a value)."""
+    mant = 10 if dtype == pi.F16 else 7
+    a = np.maximum(np.abs(ref), 2.0 ** -14)
+    return 0.5 * 2.0 ** (np.floor(np.log2(a)) - mant)
+
+
+def excess(case, got: np.ndarray, ref: np.ndarray) -> float:
+    """Largest amount by which |got - ref| exceeds the bound for contexts too
+    short for the fixed bar: the computation's bar plus the rounding of the
+    output to the q dtype (outputs of a few keys reach |x| ~ 1, where half an
+    ulp of bf16 alone is 2e-3)."""
+    bound = tol(case) + half_ulp(ref, case.q_dtype)
+    return float(np.max(np.abs(got - ref) - bound))
+
+
 def sample_pairs(case, n, seed=0):
     """n (token, q head) pairs spread over the batch, always including the
     first and last token and the first and last head."""

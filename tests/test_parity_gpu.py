@@ -10,18 +10,23 @@ import pytest
 
 import oracle
 import pa_inputs as pi
-from gpu_util import (max_err, run_gpu, sample_pairs, to_device, to_f64, tol)
+from gpu_util import (excess, max_err, run_gpu, sample_pairs, to_f64, tol)
 
 pytestmark = pytest.mark.gpu
 
 
-def _full(case, **kw):
+def _full(case, rounding_aware=False, **kw):
+    """All outputs against the oracle.  The five workloads use the fixed bar;
+    rounding_aware adds the output dtype's half ulp (short-context sweeps)."""
     ref = oracle.forward(case)
     got = run_gpu(case, **kw)
     err = max_err(got, ref)
     print(f"{case.name}: max err {err:.3e}", flush=True)
     assert np.all(np.isfinite(to_f64(got))), case.name
-    assert err <= tol(case), f"{case.name}: max err {err}"
+    if rounding_aware:
+        assert excess(case, to_f64(got), ref) <= 0.0, f"{case.name}: max err {err}"
+    else:
+        assert err <= tol(case), f"{case.name}: max err {err}"
     return got, ref
 
 
@@ -93,12 +98,12 @@ def _small_cases():
 
 def test_small_shapes_all_instances():
     for case in _small_cases():
-        _full(case)
+        _full(case, rounding_aware=True)
 
 
 def test_small_ragged_batches():
     for rep in range(4):
-        _full(pi.config5(rep=rep, lo=1, hi=3000, poison=True))
+        _full(pi.config5(rep=rep, lo=1, hi=3000, poison=True), rounding_aware=True)
 
 
 @pytest.mark.parametrize("S", [1, 2, 7, 0, 10 ** 6])
@@ -149,8 +154,6 @@ def test_poisoned_slots_change_nothing():
 def test_rows_match_single_token_decodes():
     case = pi.config2(8192, 4, rep=2)
     full = to_f64(run_gpu(case))
-    dev = to_device(case)
-    import torch
     for i in range(4):
         one = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
         one.q = case.q[i:i + 1]
@@ -172,7 +175,6 @@ def test_device_contract_violations_give_nan_and_status():
     bad.subsequence_begins = np.array([0, 2, 7], np.int32)
     bad.q = np.concatenate([base.q, base.q[:2]], axis=0)
     bad.num_tokens = 7
-    bad.max_context_len = 210
     got = to_f64(run_gpu(bad))
     assert pav.pa_verify_read_status() == pav.PA_ERR_DEVICE_CONTRACT
     assert np.all(np.isnan(got[2:]))
@@ -191,3 +193,36 @@ def test_device_contract_violations_give_nan_and_status():
     got = to_f64(run_gpu(base, max_context_len=250))
     assert pav.pa_verify_read_status() == pav.PA_ERR_DEVICE_CONTRACT
     assert np.all(np.isnan(got[:2]))
+
+
+def test_graph_capture_replays_match_eager():
+    """A call captured in a HIP graph replays to the eager result, replay after
+    replay, with other eager work and synchronisations in between."""
+    import torch
+    from gpu_util import to_device
+    import speculative_decoding_verify_paged_amd as pav
+    cases = [pi.config2(8192, 3, rep=7), pi.config4(4096, window=1024, rep=7)]
+    devs = [to_device(c) for c in cases]
+    outs = [torch.empty_like(d["q"]) for d in devs]
+
+    def call_all(stream):
+        for c, d, o in zip(cases, devs, outs):
+            pav.pa_verify_forward(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                  d["past_lens"], d["subsequence_begins"], c.max_context_len,
+                                  c.scale, o, sliding_window=c.sliding_window, stream=stream)
+
+    call_all(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    eager = [to_f64(o) for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call_all(torch.cuda.current_stream().cuda_stream)
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for e, o in zip(eager, outs):
+            assert np.array_equal(e, to_f64(o)), rep
+    assert pav.pa_verify_read_status() == pav.PA_OK
