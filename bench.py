@@ -185,7 +185,7 @@ def read_ceiling():
     st = torch.cuda.current_stream()
     best = 0.0
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for grid in (1024, 2048, 4096, 8192, 16384):
+    for grid in (4096, 8192, 16384, 32768):
         for rep in range(3):
             torch.cuda.synchronize()
             e0.record()
@@ -251,6 +251,7 @@ def main():
     us, spread = run.time_graph(args.steps, args.warmup, args.repeats)
     us_eager, us_kernel, _ = run.time(args.steps, args.warmup, args.repeats)
     kv = case.kv_bytes()
+    copies = run.copies
     del run
 
     t1 = None
@@ -286,7 +287,7 @@ def main():
                    "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads,
                    "head_dim": case.head_dim, "block_size": case.block_size,
                    "sliding_window": case.sliding_window, "kv_dtype": dtype,
-                   "kv_bytes_per_call": kv, "pool_copies": run.copies},
+                   "kv_bytes_per_call": kv, "pool_copies": copies},
         "us_per_call": round(us, 3),
         "us_per_call_spread": [round(x, 3) for x in spread],
         "us_per_call_eager": round(us_eager, 3),

@@ -32,12 +32,18 @@
  *  - Graph replay must stay intact (no allocation, no host sync in a call):
  *    the same vLLM article, torch-profiler trace passage (hipGraphLaunch).
  *
- * Memory layouts (all row-major, contiguous, caller-owned device memory):
- *  q, out        [num_tokens, Hq, D]            f16 or bf16 (out dtype == q dtype)
- *  k_cache       [num_blocks, Hkv, block_size, D]     one page tile per (block, head)
- *  v_cache       [num_blocks, Hkv, D, block_size]     V pages are stored d-major
- *                (transposed) so that the PV contraction over keys reads
- *                8 consecutive keys of one d as a single 16-byte load.
+ * Memory layouts (contiguous, caller-owned device memory):
+ *  q, out        [num_tokens, Hq, D]  row-major, f16 or bf16 (out dtype == q dtype)
+ *  k_cache,      [num_blocks, Hkv, page]: one page of block_size x D elements
+ *  v_cache       per (block, KV head).  A page is block_size/16 sub-tiles of 16
+ *                slots; inside a sub-tile the elements are stored in the order
+ *                the gfx950 MFMA operands consume them, so that each wavefront
+ *                load reads 1 KB of contiguous memory.  Element (slot s, dim d)
+ *                of a page sits at element offset
+ *     K f16/bf16: ((((s/16)*(D/32) + d/32)*4 + (d%32)/8)*16 + s%16)*8 + d%8
+ *     V f16/bf16: (((((s/16)*(D/32) + d/32)*4 + (s%16)/4)*16 + d%16)*2 + (d%32)/16)*4 + s%4
+ *     K u8:       ((((s/16)*(D/64) + d/64)*4 + (d%64)/16)*16 + s%16)*16 + d%16
+ *     V u8:       (((((s/16)*(D/64) + d/64)*4 + (s%16)/4)*16 + d%16)*4 + (d%64)/16)*4 + s%4
  *  k_scale_zp,   [num_blocks, Hkv, block_size, 2]     f16 (scale, zero_point) per
  *  v_scale_zp    token per KV head, u8 variant only; dequant = (u - zp) * scale
  *  block_tables  [num_seqs, max_blocks_per_seq] int32 physical block ids

@@ -26,8 +26,11 @@
  *    decoding net loss", passage on the 18 fixed-input kernel cases).
  *
  * Layouts (the library's C ABI defines them; restated here on purpose):
- *   q [num_tokens][Hq][D], k [nb][Hkv][bs][D], v [nb][Hkv][D][bs],
- *   scale/zero point [nb][Hkv][bs][2] (f16), block_tables [num_seqs][mbps].
+ *   q [num_tokens][Hq][D]; k and v [nb][Hkv][page], each page holding the
+ *   block_size x D elements of one (block, KV head) in the tiled order of
+ *   k_offset / v_offset below; scale/zero point [nb][Hkv][bs][2] (f16);
+ *   block_tables [num_seqs][mbps].  Requires block_size % 16 == 0 and
+ *   D % 32 == 0 (D % 64 == 0 for u8).
  * Element codes: 0 = f16 bits, 1 = bf16 bits, 2 = u8 code with f16
  * (scale, zero point), 3 = fp64 value (test-only input form).
  */
@@ -73,6 +76,22 @@ static double dec_elem(const void* base, size_t idx, int code) {
   }
 }
 
+/* Offsets of element (slot, d) inside one page.  Sub-tiles of 16 slots; in
+ * each, K is ordered [d/32][(d%32)/8][slot%16][d%8] (u8: [d/64][(d%64)/16]
+ * [slot%16][d%16]) and V [d/32][(slot%16)/4][d%16][(d%32)/16][slot%4] (u8:
+ * [d/64][(slot%16)/4][d%16][(d%64)/16][slot%4]). */
+static size_t k_offset(int slot, int d, int D, int u8) {
+  const size_t st = (size_t)(slot / 16), m = (size_t)(slot % 16);
+  if (u8) return (((st * (D / 64) + d / 64) * 4 + (d % 64) / 16) * 16 + m) * 16 + d % 16;
+  return (((st * (D / 32) + d / 32) * 4 + (d % 32) / 8) * 16 + m) * 8 + d % 8;
+}
+
+static size_t v_offset(int slot, int d, int D, int u8) {
+  const size_t st = (size_t)(slot / 16), qq = (size_t)((slot % 16) / 4);
+  if (u8) return ((((st * (D / 64) + d / 64) * 4 + qq) * 16 + d % 16) * 4 + (d % 64) / 16) * 4 + slot % 4;
+  return ((((st * (D / 32) + d / 32) * 4 + qq) * 16 + d % 16) * 2 + (d % 32) / 16) * 4 + slot % 4;
+}
+
 /* One KV value.  For u8, code u of (block, head, slot) means (u - zp) * scale
  * with the per-token per-KV-head f16 pair stored next to the cache. */
 static double kv_value(const pa_oracle_args* a, const void* cache, const void* sz,
@@ -93,6 +112,8 @@ static int check_args(const pa_oracle_args* a) {
   if (a->num_seqs < 1 || a->num_q_heads < 1 || a->num_kv_heads < 1 || a->head_dim < 1 ||
       a->block_size < 1 || a->num_q_heads % a->num_kv_heads != 0)
     return PA_ORACLE_ERR_ARG;
+  if (a->block_size % 16 != 0 || a->head_dim % (a->kv_dtype == PA_ORACLE_U8 ? 64 : 32) != 0)
+    return PA_ORACLE_ERR_ARG;                       /* the tiled page layout needs these */
   if (!a->q || !a->k_cache || !a->v_cache || !a->block_tables || !a->past_lens ||
       !a->subsequence_begins)
     return PA_ORACLE_ERR_ARG;
@@ -132,16 +153,19 @@ static void attend_one(const pa_oracle_args* a, int n, int h, double* z, double*
   const int32_t* table = a->block_tables + (size_t)s * a->max_blocks_per_seq;
   const size_t q_off = ((size_t)n * Hq + h) * D;
 
+  const int u8 = a->kv_dtype == PA_ORACLE_U8;
+
   /* pass 1: logits and their max */
   double m = -INFINITY;
   for (int t = lo; t < hi; ++t) {
     const size_t blk = (size_t)table[t / bs];
     const int slot = t % bs;
     const size_t row = (blk * Hkv + g) * bs + slot; /* index of (blk, g, slot) */
+    const size_t page = (blk * Hkv + g) * (size_t)bs * D;
     double dot = 0.0;
     for (int d = 0; d < D; ++d)
       dot += dec_elem(a->q, q_off + d, a->q_dtype) *
-             kv_value(a, a->k_cache, a->k_scale_zp, row * D + d, row);
+             kv_value(a, a->k_cache, a->k_scale_zp, page + k_offset(slot, d, D, u8), row);
     z[t - lo] = a->scale * dot;
     if (z[t - lo] > m) m = z[t - lo];
   }
@@ -154,8 +178,9 @@ static void attend_one(const pa_oracle_args* a, int n, int h, double* z, double*
     const size_t blk = (size_t)table[t / bs];
     const int slot = t % bs;
     const size_t row = (blk * Hkv + g) * bs + slot;
+    const size_t page = (blk * Hkv + g) * (size_t)bs * D;
     for (int d = 0; d < D; ++d) {
-      const size_t vidx = ((blk * Hkv + g) * D + d) * bs + slot;   /* v is [nb][Hkv][D][bs] */
+      const size_t vidx = page + v_offset(slot, d, D, u8);
       out_row[d] += w * kv_value(a, a->v_cache, a->v_scale_zp, vidx, row);
     }
   }

@@ -16,8 +16,8 @@ typedef struct pa_oracle_args {
   int32_t q_dtype, kv_dtype;          /* element codes above */
   double scale;
   const void* q;                      /* [num_tokens][Hq][D] */
-  const void* k_cache;                /* [nb][Hkv][bs][D] */
-  const void* v_cache;                /* [nb][Hkv][D][bs] */
+  const void* k_cache;                /* [nb][Hkv][bs * D], tiled pages (see pa_oracle.c) */
+  const void* v_cache;                /* [nb][Hkv][bs * D], tiled pages */
   const void* k_scale_zp;             /* f16 [nb][Hkv][bs][2], u8 only */
   const void* v_scale_zp;
   const int32_t* block_tables;        /* [num_seqs][max_blocks_per_seq] */

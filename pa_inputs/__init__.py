@@ -25,8 +25,11 @@ Recipe (also the basis of every parity case and of the benchmark):
   at positions >= past_len + T in a sequence's last block, slots below the
   sliding window, and spare pool blocks (for u8: NaN scale/zero point).
 
-Layouts match the C ABI header: k [nb, Hkv, bs, D]; v [nb, Hkv, D, bs]
-(d-major pages); scale/zp [nb, Hkv, bs, 2] f16; q [num_tokens, Hq, D].
+Layouts match the C ABI header: every (block, KV head) page of K and V holds
+its block_size x D elements in the tiled order of ``k_page_offset`` /
+``v_page_offset`` (16-slot sub-tiles in MFMA operand order); scale/zp
+[nb, Hkv, bs, 2] f16; q [num_tokens, Hq, D].  ``tile_k`` / ``tile_v`` turn
+[..., bs, D] pages into that order and ``untile_k`` / ``untile_v`` back.
 """
 from __future__ import annotations
 
@@ -110,6 +113,59 @@ def quantize_u8(x: np.ndarray):
 
 
 # ----------------------------------------------------------------------------
+# page layouts (data movement only)
+# ----------------------------------------------------------------------------
+def k_page_offset(slot, d, D, u8=False):
+    """Element offset of K[slot, d] inside one (block, KV head) page."""
+    if u8:
+        return ((((slot // 16) * (D // 64) + d // 64) * 4 + (d % 64) // 16) * 16 + slot % 16) * 16 + d % 16
+    return ((((slot // 16) * (D // 32) + d // 32) * 4 + (d % 32) // 8) * 16 + slot % 16) * 8 + d % 8
+
+
+def v_page_offset(slot, d, D, u8=False):
+    """Element offset of V[slot, d] inside one (block, KV head) page."""
+    if u8:
+        return (((((slot // 16) * (D // 64) + d // 64) * 4 + (slot % 16) // 4) * 16 + d % 16) * 4
+                + (d % 64) // 16) * 4 + slot % 4
+    return (((((slot // 16) * (D // 32) + d // 32) * 4 + (slot % 16) // 4) * 16 + d % 16) * 2
+            + (d % 32) // 16) * 4 + slot % 4
+
+
+def _perm(bs, D, fn, u8):
+    slot = np.arange(bs)[:, None]
+    d = np.arange(D)[None, :]
+    return fn(slot, d, D, u8).reshape(-1)          # offset of logical (slot, d), row-major
+
+
+def tile_k(pages, u8=False):
+    """[..., bs, D] logical pages -> [..., bs * D] tiled K pages."""
+    bs, D = pages.shape[-2:]
+    off = _perm(bs, D, k_page_offset, u8)
+    out = np.empty(pages.shape[:-2] + (bs * D,), dtype=pages.dtype)
+    out[..., off] = pages.reshape(pages.shape[:-2] + (bs * D,))
+    return out
+
+
+def tile_v(pages, u8=False):
+    bs, D = pages.shape[-2:]
+    off = _perm(bs, D, v_page_offset, u8)
+    out = np.empty(pages.shape[:-2] + (bs * D,), dtype=pages.dtype)
+    out[..., off] = pages.reshape(pages.shape[:-2] + (bs * D,))
+    return out
+
+
+def untile_k(tiled, bs, D, u8=False):
+    """[..., bs * D] tiled K pages -> [..., bs, D] logical pages."""
+    off = _perm(bs, D, k_page_offset, u8)
+    return tiled[..., off].reshape(tiled.shape[:-1] + (bs, D))
+
+
+def untile_v(tiled, bs, D, u8=False):
+    off = _perm(bs, D, v_page_offset, u8)
+    return tiled[..., off].reshape(tiled.shape[:-1] + (bs, D))
+
+
+# ----------------------------------------------------------------------------
 # cases
 # ----------------------------------------------------------------------------
 @dataclasses.dataclass
@@ -130,8 +186,8 @@ class Case:
     scale: float
     max_context_len: int
     q: np.ndarray                 # uint16 bits [num_tokens, Hq, D]
-    k_cache: np.ndarray           # uint16 bits or uint8 [nb, Hkv, bs, D]
-    v_cache: np.ndarray           # uint16 bits or uint8 [nb, Hkv, D, bs]
+    k_cache: np.ndarray           # uint16 bits or uint8 [nb, Hkv, bs, D], page contents tiled
+    v_cache: np.ndarray           # uint16 bits or uint8 [nb, Hkv, bs, D], page contents tiled
     k_scale_zp: Optional[np.ndarray]  # uint16 f16 bits [nb, Hkv, bs, 2] (u8 only)
     v_scale_zp: Optional[np.ndarray]
     block_tables: np.ndarray      # int32 [num_seqs, max_blocks_per_seq]
@@ -159,10 +215,18 @@ class Case:
         per_key = self.num_kv_heads * (2 * self.head_dim * e + (8 if self.kv_dtype == U8 else 0))
         return self.kv_keys() * per_key
 
-    def logical_kv_f32(self, s: int):
-        """Float32 values of sequence s's K and V as [L+T, Hkv, D] (tests only).
+    def logical_pages(self):
+        """K and V pools as logical [nb, Hkv, bs, D] arrays of stored codes."""
+        u8 = self.kv_dtype == U8
+        bs, D = self.block_size, self.head_dim
+        flat = self.k_cache.shape[:2] + (bs * D,)
+        return (untile_k(self.k_cache.reshape(flat), bs, D, u8),
+                untile_v(self.v_cache.reshape(flat), bs, D, u8))
 
-        For u8 the values are the dequantised codes in float64 precision."""
+    def logical_kv_f32(self, s: int):
+        """Values of sequence s's K and V as [L+T, Hkv, D] float64 (tests only).
+
+        For u8 the values are the dequantised codes."""
         L = int(self.past_lens[s])
         T = self.Ts[s]
         n = L + T
@@ -170,9 +234,10 @@ class Case:
         pos = np.arange(n)
         blk = self.block_tables[s, pos // bs]
         off = pos % bs
+        kl, vl = self.logical_pages()
         if self.kv_dtype == U8:
-            ku = self.k_cache[blk, :, off, :].astype(np.float64)          # [n, Hkv, D]
-            vu = self.v_cache[blk, :, :, off].astype(np.float64)          # [n, Hkv, D]
+            ku = kl[blk, :, off, :].astype(np.float64)                    # [n, Hkv, D]
+            vu = vl[blk, :, off, :].astype(np.float64)                    # [n, Hkv, D]
             ksz = self.k_scale_zp[blk, :, off, :]
             vsz = self.v_scale_zp[blk, :, off, :]
             ks = f16_bits_to_f32(ksz[..., 0]).astype(np.float64)
@@ -180,8 +245,8 @@ class Case:
             vs = f16_bits_to_f32(vsz[..., 0]).astype(np.float64)
             vz = f16_bits_to_f32(vsz[..., 1]).astype(np.float64)
             return (ku - kz[..., None]) * ks[..., None], (vu - vz[..., None]) * vs[..., None]
-        k = bits_to_f32(self.k_cache[blk, :, off, :], self.kv_dtype)
-        v = bits_to_f32(self.v_cache[blk, :, :, off], self.kv_dtype)
+        k = bits_to_f32(kl[blk, :, off, :], self.kv_dtype)
+        v = bits_to_f32(vl[blk, :, off, :], self.kv_dtype)
         return k.astype(np.float64), v.astype(np.float64)
 
     def q_f32(self) -> np.ndarray:
@@ -199,18 +264,13 @@ def _draw_pool(rng, nb, Hkv, bs, D):
     return out
 
 
-def _store_pool(x, kv_dtype, transpose_v):
-    """Round or quantise a float32 [nb, Hkv, bs, D] pool to its storage form."""
+def _store_pool(x, kv_dtype):
+    """Round or quantise a float32 [nb, Hkv, bs, D] pool to its stored codes
+    (still in logical [nb, Hkv, bs, D] order)."""
     if kv_dtype == U8:
         u, s, z = quantize_u8(x)
-        sz = np.stack([s, z], axis=-1)                 # [nb, Hkv, bs, 2]
-        if transpose_v:
-            u = np.ascontiguousarray(np.swapaxes(u, 2, 3))
-        return u, sz
-    bits = f32_to_bits(x, kv_dtype)
-    if transpose_v:
-        bits = np.ascontiguousarray(np.swapaxes(bits, 2, 3))
-    return bits, None
+        return u, np.stack([s, z], axis=-1)            # codes, [nb, Hkv, bs, 2]
+    return f32_to_bits(x, kv_dtype), None
 
 
 def build_case(seed: Sequence[int], past_lens: Sequence[int], Ts: Sequence[int], *,
@@ -241,10 +301,10 @@ def build_case(seed: Sequence[int], past_lens: Sequence[int], Ts: Sequence[int],
     qf = rng.standard_normal((num_tokens, num_q_heads, head_dim), dtype=np.float32)
     q = f32_to_bits(qf, q_dtype)
     kf = _draw_pool(rng, nb, num_kv_heads, bs, head_dim)
-    k_cache, k_sz = _store_pool(kf, kv_dtype, transpose_v=False)
+    k_log, k_sz = _store_pool(kf, kv_dtype)
     del kf
     vf = _draw_pool(rng, nb, num_kv_heads, bs, head_dim)
-    v_cache, v_sz = _store_pool(vf, kv_dtype, transpose_v=True)
+    v_log, v_sz = _store_pool(vf, kv_dtype)
     del vf
     perm = rng.permutation(nb).astype(np.int32)
 
@@ -256,8 +316,13 @@ def build_case(seed: Sequence[int], past_lens: Sequence[int], Ts: Sequence[int],
     spare = perm[o:]
 
     if poison:
-        _poison(k_cache, v_cache, k_sz, v_sz, kv_dtype, bt, past_lens, Ts, bs,
+        _poison(k_log, v_log, k_sz, v_sz, kv_dtype, bt, past_lens, Ts, bs,
                 sliding_window, spare)
+    u8 = kv_dtype == U8
+    k_cache = tile_k(k_log, u8).reshape(k_log.shape)
+    del k_log
+    v_cache = tile_v(v_log, u8).reshape(v_log.shape)
+    del v_log
 
     return Case(name=name, num_seqs=num_seqs, num_tokens=num_tokens,
                 num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
@@ -270,7 +335,8 @@ def build_case(seed: Sequence[int], past_lens: Sequence[int], Ts: Sequence[int],
 
 
 def _poison(k, v, ksz, vsz, kv_dtype, bt, past_lens, Ts, bs, W, spare):
-    """NaN every cache slot that no query row may read (see module docstring)."""
+    """NaN every cache slot that no query row may read (see module docstring);
+    k, v are logical [nb, Hkv, bs, D] code arrays."""
     def kill(blk, slots):
         if len(slots) == 0:
             return
@@ -280,7 +346,7 @@ def _poison(k, v, ksz, vsz, kv_dtype, bt, past_lens, Ts, bs, W, spare):
         else:
             nanv = F16_NAN if kv_dtype == F16 else BF16_NAN
             k[blk, :, slots, :] = nanv
-            v[blk, :, :, slots] = nanv
+            v[blk, :, slots, :] = nanv
     for s, (L, T) in enumerate(zip(past_lens, Ts)):
         n = L + T
         last = (n - 1) // bs

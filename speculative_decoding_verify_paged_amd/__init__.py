@@ -186,8 +186,9 @@ def _call(u8, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_le
         _check(t, n, dtype=torch.int32, device=dev)
     num_tokens, Hq, D = q.shape
     nb, Hkv, bs, D2 = k_cache.shape
-    if D2 != D or tuple(v_cache.shape) != (nb, Hkv, D, bs):
-        raise ValueError("k_cache must be [nb, Hkv, bs, D] and v_cache [nb, Hkv, D, bs]")
+    if D2 != D or tuple(v_cache.shape) != (nb, Hkv, bs, D):
+        raise ValueError("k_cache and v_cache must both be [nb, Hkv, bs, D] (page contents in "
+                         "the tiled order of include/pa_verify.h)")
     if k_cache.dtype != v_cache.dtype:
         raise ValueError("k_cache and v_cache dtypes differ")
     if u8:
@@ -249,7 +250,8 @@ def pa_verify_forward(q, k_cache, v_cache, block_tables, past_lens, subsequence_
                       prof_events=None):
     """Paged verify attention over an f16/bf16 cache; returns ``out``.
 
-    q [num_tokens, Hq, D]; k_cache [nb, Hkv, bs, D]; v_cache [nb, Hkv, D, bs];
+    q [num_tokens, Hq, D]; k_cache, v_cache [nb, Hkv, bs, D] with each page's
+    bs * D elements in the tiled order the C header defines;
     block_tables [num_seqs, max_blocks_per_seq], past_lens [num_seqs],
     subsequence_begins [num_seqs + 1] (int32, device).  ``stream`` is a raw
     hipStream_t (default: torch's current stream); ``prof_events`` is an

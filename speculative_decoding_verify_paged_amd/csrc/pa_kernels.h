@@ -47,10 +47,23 @@ hipError_t launch_segment_u8(const SegmentArgs& a, int q_dtype, int D, int bs, d
                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_combine(const CombineArgs& a, int out_dtype, int D, dim3 grid, hipStream_t st);
 
-// Resident segment workgroups per CU the kernels are built for (register and
-// LDS budgets fixed at compile time), used by the planner.
+// Per (cache dtype, head_dim): wavefronts per SIMD the segment kernel is
+// compiled for (its register budget, no spills) and the steps each
+// wavefront keeps loaded (1: load then compute; 2: the next step's loads in
+// flight during this step's math).  The planner sizes the grid from it.
+struct SegConfig {
+  int waves_per_simd;
+  int prefetch;
+};
+constexpr SegConfig seg_config(int kv_dtype, int D) {
+  if (kv_dtype == kU8) return D >= 256 ? SegConfig{1, 2} : D >= 128 ? SegConfig{2, 2} : SegConfig{4, 1};
+  return D >= 256 ? SegConfig{1, 1} : D >= 128 ? SegConfig{3, 1} : SegConfig{4, 1};
+}
+// Resident segment workgroups per CU (4 SIMDs per CU).
 constexpr int groups_per_cu(int kv_dtype, int D) {
-  return (D >= 256) ? 1 : (D >= 128 ? 2 : 4);
+  return seg_config(kv_dtype, D).waves_per_simd * 4 / kWavesPerGroup > 0
+             ? seg_config(kv_dtype, D).waves_per_simd * 4 / kWavesPerGroup
+             : 1;
 }
 
 }  // namespace pav

@@ -1,7 +1,7 @@
 // pa_kernels.hip — gfx950 kernels of paged verify attention.
 //
 // Two kernels per call:
-//   1. pa_segment_*: one workgroup per (KV segment j, KV head, sequence).  Its
+//   1. pa_segment: one workgroup per (KV segment j, KV head, sequence).  Its
 //      wavefronts stream the segment's K/V page tiles straight from HBM into
 //      MFMA operand registers, each tile read once for all G*T stacked query
 //      rows of the GQA group, and keep an online softmax.  The workgroup
@@ -19,34 +19,44 @@
 // rows ride along in the same MFMA tile (same article, direct kernel sweep:
 // one extra row costs a fraction of a percent).
 //
-// Data path of one wavefront step (32 keys, rows r = g*T + i padded to 16):
-//   S^T[key, r] = K[key, :] . Q[r, :]     v_mfma_f32_16x16x32_{f16,bf16}, A = K rows
-//                                          read from the page (16 B per lane),
-//                                          B = Q rows held in registers
-//   online softmax over the step's keys per row (lane-local, 2 cross-lane max)
-//   O^T[d, r] += V^T[d, key] . P^T[key, r] A = V^T read from the d-major V page
-//                                          (8 keys contiguous, 16 B per lane),
-//                                          B = P split into hi + lo f16/bf16 parts
-// Every lane owns one stacked row r = lane % 16 in all three products, so the
-// softmax state and its rescale never leave the lane.  The cross-lane steps
-// are two shuffles for the row max and the workgroup merge at the end.
+// Page layout.  A (block, KV head) page is a sequence of 16-slot sub-tiles,
+// each stored in the register order of the MFMA operands that consume it, so
+// that every wavefront load instruction (64 lanes x 16 B) reads 1 KB of
+// contiguous memory — whole cache lines, which is what lets the loads keep
+// enough requests in flight to approach the HBM streaming rate:
+//   K: [d/32][(d%32)/8][slot%16][d%8]          (u8: [d/64][(d%64)/16][slot%16][d%16])
+//   V: [d/32][(slot%16)/4][d%16][(d%32)/16][slot%4]
+//                                               (u8: [d/64][(slot%16)/4][d%16][(d%64)/16][slot%4])
 //
-// V pages are stored d-major ([block, head, D, block_size]): the PV
-// contraction runs over keys, and the MFMA operand wants 8 consecutive keys
-// per lane, which that layout makes one 16-byte load instead of eight 2-byte
-// gathers or an LDS transpose.
+// Data path of one wavefront step (32 keys = two sub-tiles, stacked rows
+// r = g*T + i padded to 16):
+//   S^T[slot, r] = K[slot, :] . Q[r, :]    v_mfma_f32_16x16x32, A = one K load per 32 d,
+//                                           B = Q rows held in registers
+//   online softmax per row (lane-local, two cross-lane max steps)
+//   O^T[d, r] += V^T[d, slot] . P^T[slot, r]  v_mfma_f32_16x16x16, A = half a V load,
+//                                           B = the S^T accumulator itself after exp
+//                                           (hi + lo 16-bit parts)
+// Every lane owns one stacked row r = lane % 16 in all three products, so the
+// softmax state and its rescale never leave the lane.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "pa_kernels.h"
 
 namespace pav {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -54,9 +64,17 @@ __device__ __forceinline__ u32x4 ld16(const char* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-template <int KV>
+// KV pages are read exactly once per call: nontemporal loads stream them
+// past the caches (measured ~7.0 TB/s streaming-read ceiling on MI355X with
+// the nontemporal hint, ~6.2 TB/s without).
+__device__ __forceinline__ u32x4 ld16_stream(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// 16x16x32: A and B hold 8 consecutive k values per lane.
+template <int QT>
 __device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
-  if constexpr (KV == kF16) {
+  if constexpr (QT == kF16) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   } else {
@@ -65,35 +83,74 @@ __device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
   }
 }
 
-// Eight softmax weights as two MFMA operands, hi = rne16(p) and
+// 16x16x16: A and B hold 4 consecutive k values per lane.
+template <int QT>
+__device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
+  if constexpr (QT == kF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+  }
+}
+
+// Four softmax weights as two 16-bit MFMA operands, hi = rne16(p) and
 // lo = rne16(p - hi): PV runs on both, so the weights keep ~16 more bits than
 // one 16-bit rounding (bf16 alone would cost up to 2^-9 of max|v| when a few
 // keys dominate).
-template <int KV>
-__device__ __forceinline__ void pack8_split(const float (&p)[8], u32x4& hi, u32x4& lo) {
-  if constexpr (KV == kF16) {
-    f16x8 h, l;
+template <int QT>
+__device__ __forceinline__ void split4(float p0, float p1, float p2, float p3, u32x2& hi, u32x2& lo) {
+  const float p[4] = {p0, p1, p2, p3};
+  if constexpr (QT == kF16) {
+    f16x4 h, l;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 4; ++e) {
       h[e] = (_Float16)p[e];
       l[e] = (_Float16)(p[e] - (float)h[e]);
     }
-    hi = __builtin_bit_cast(u32x4, h);
-    lo = __builtin_bit_cast(u32x4, l);
+    hi = __builtin_bit_cast(u32x2, h);
+    lo = __builtin_bit_cast(u32x2, l);
   } else {
-    bf16x8 h, l;
+    bf16x4 h, l;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 4; ++e) {
       h[e] = (__bf16)p[e];
       l[e] = (__bf16)(p[e] - (float)h[e]);
     }
-    hi = __builtin_bit_cast(u32x4, h);
-    lo = __builtin_bit_cast(u32x4, l);
+    hi = __builtin_bit_cast(u32x2, h);
+    lo = __builtin_bit_cast(u32x2, l);
+  }
+}
+
+// Four u8 codes (one dword) as four exact 16-bit values of the MFMA type.
+// f16: byte b placed under exponent 0x64 is the half 1024 + b; subtracting
+// 1024 is exact.  bf16 has too few mantissa bits for that trick and goes
+// through f32.
+template <int QT>
+__device__ __forceinline__ u32x2 u8x4_to_16(uint32_t w) {
+  if constexpr (QT == kF16) {
+    const f16x2 bias = {(_Float16)1024.f, (_Float16)1024.f};
+    const f16x2 a = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, w, 0x04010400u)) - bias;
+    const f16x2 b = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, w, 0x04030402u)) - bias;
+    return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+  } else {
+    bf16x4 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = (__bf16)(float)((w >> (8 * e)) & 0xffu);
+    return __builtin_bit_cast(u32x2, h);
   }
 }
 
 __device__ __forceinline__ float xor_max(float v, int m) {
   return fmaxf(v, __shfl_xor(v, m, kWave));
+}
+
+__device__ __forceinline__ float lo_f16(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2, w)[0];
+}
+__device__ __forceinline__ float hi_f16(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2, w)[1];
 }
 
 // Per-sequence decode shared by both kernels: the contract check and the
@@ -120,14 +177,20 @@ __device__ __forceinline__ SeqInfo seq_info(const SegmentArgs& a, int s) {
 }
 
 // ---------------------------------------------------------------------------
-// Segment kernel, f16 / bf16 KV.
+// Segment kernel.  QT: dtype of q (and of the MFMA operands); KV: cache dtype
+// (QT, or kU8 for codes with per-token f16 scale and zero point).
 // ---------------------------------------------------------------------------
-template <int KV, int D, int BS, int NW, int WPE>
+template <int QT, int KV, int D, int BS, int NW, int WPE, int PF>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE)))
-void pa_segment_fp(SegmentArgs a) {
-  constexpr int DC = D / 32;          // 32-wide d chunks of the QK contraction
-  constexpr int DT = D / 16;          // 16-wide d tiles of O^T
-  constexpr int OSTRIDE = D + 4;      // padded LDS row of the merge buffer
+void pa_segment(SegmentArgs a) {
+  constexpr bool U8 = KV == kU8;
+  constexpr int EB = U8 ? 1 : 2;                  // bytes per cached element
+  constexpr int QC = D / 32;                      // 16x16x32 k-chunks of the QK contraction
+  constexpr int LK = U8 ? D / 64 : D / 32;        // 1 KB K loads per 16-slot sub-tile
+  constexpr int LV = LK;                          // 1 KB V loads per sub-tile
+  constexpr int DT = D / 16;                      // 16-wide d tiles of O^T
+  constexpr int OSTRIDE = D + 4;                  // padded LDS row of the merge buffer
+  static_assert(BS % 16 == 0 && kKeysPerStep == 32, "two 16-slot sub-tiles per step");
   __shared__ int s_bt[kMaxSegBlocks];
   __shared__ float s_m[NW][kRows];
   __shared__ float s_l[NW][kRows];
@@ -137,86 +200,152 @@ void pa_segment_fp(SegmentArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int n16 = lane & 15;          // stacked query row owned by this lane
-  const int q4 = lane >> 4;           // lane group: 8 keys of a step, 8 d of a chunk
+  const int q4 = lane >> 4;           // lane group
   const int j = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int32_t* bt_row = a.bt + (size_t)s * a.mbps;
+
+  // Full-causal layers: segment j's block range does not depend on the
+  // sequence's length, so its block ids are requested together with the
+  // sequence metadata — one memory round trip before the first KV load
+  // instead of two.  The loads stay inside the block-table row; ids of
+  // blocks past the sequence are never used.
+  constexpr int kSlots = (kMaxSegBlocks + NW * kWave - 1) / (NW * kWave);
+  int spec_id[kSlots];
+  const int spec_lo = (j * a.steps_per_seg * kKeysPerStep) / BS;
+  const int spec_n = a.window == 0 ? min(a.mbps - spec_lo, (a.steps_per_seg * kKeysPerStep) / BS + 1) : 0;
+#pragma unroll
+  for (int k = 0; k < kSlots; ++k) {
+    const int x = threadIdx.x + k * NW * kWave;
+    spec_id[k] = x < spec_n ? bt_row[spec_lo + x] : 0;
+  }
 
   const SeqInfo si = seq_info(a, s);
   if (!si.ok) {
     if (j == 0 && h == 0 && threadIdx.x == 0) atomicExch(a.status, kDeviceContract);
     return;                           // the combine kernel writes NaN rows
   }
+  const int T = si.T;
+  const int R = a.G * T;
   const int st_begin = j * a.steps_per_seg;
   const int st_end = min(si.n_steps, st_begin + a.steps_per_seg);
-  if (st_begin >= st_end) return;     // empty segment; the combine skips it
+  if (st_begin >= st_end) {
+    // no key of this sequence falls in segment j: an empty partial, so the
+    // combine can read all S partials without knowing the sequence
+    if (threadIdx.x < R) {
+      const int r = threadIdx.x;
+      const size_t row = ((size_t)(si.b0 + r % T) * a.Hq + h * a.G + r / T) * a.S + j;
+      a.ws_ml[row * 2 + 0] = -INFINITY;
+      a.ws_ml[row * 2 + 1] = 0.f;
+    }
+    return;
+  }
 
   // Stage the segment's block ids in LDS.  Only pages holding a key in
   // [lo0, ctx) are checked and ever dereferenced.
   const int key_lo = si.base + st_begin * kKeysPerStep;
   const int blk_lo = key_lo / BS;
   const int blk_last = (min(si.ctx, si.base + st_end * kKeysPerStep) - 1) / BS;
-  const int32_t* bt_row = a.bt + (size_t)s * a.mbps;
   if (threadIdx.x == 0) s_bad = 0;
   __syncthreads();
-  for (int x = threadIdx.x; x <= blk_last - blk_lo; x += NW * kWave) {
-    const int b = blk_lo + x;
-    int id = 0;
-    if ((b + 1) * BS > si.lo0) {
-      id = bt_row[b];
-      if ((unsigned)id >= (unsigned)a.num_blocks) {
-        s_bad = 1;
-        id = 0;
+#pragma unroll
+  for (int k = 0; k < kSlots; ++k) {
+    const int x = threadIdx.x + k * NW * kWave;
+    if (x <= blk_last - blk_lo) {
+      const int b = blk_lo + x;
+      int id = 0;
+      if ((b + 1) * BS > si.lo0) {
+        id = a.window == 0 ? spec_id[k] : bt_row[b];
+        if ((unsigned)id >= (unsigned)a.num_blocks) {
+          s_bad = 1;
+          id = 0;
+        }
       }
+      s_bt[x] = id;
     }
-    s_bt[x] = id;
   }
 
   // Stacked rows: r = g*T + i for q head h*G + g and token b0 + i; rows past
   // G*T are zero padding that no one reads back.
-  const int T = si.T;
-  const int R = a.G * T;
   const bool row_ok = n16 < R;
   const int g = row_ok ? n16 / T : 0;
   const int i = row_ok ? n16 % T : T - 1;
   const int qh = h * a.G + g;
-  const int tok = si.b0 + i;
+  const int tok = si.b0 + i;                                  // padded rows: a real token
   const int hi_r = si.L + i + 1;                              // row's keys: [lo_r, hi_r)
   const int lo_r = a.window > 0 ? max(0, hi_r - a.window) : 0;
   const int lo_max = a.window > 0 ? max(0, si.ctx - a.window) : 0;
 
-  u32x4 qreg[DC];
+  // B operand of the QK product: lane (row, group q4) holds, for k-chunk c,
+  // the 8 d values the K sub-tile load puts in the same lane group:
+  // d = c*32 + q4*8 + 0..7 (u8: chunk 2*c2 + half: d = c2*64 + q4*16 + half*8 + 0..7).
+  u32x4 qreg[QC];
+  float qsum = 0.f;                                           // u8: sum of this lane's q values
   {
-    const char* qp = reinterpret_cast<const char*>(a.q) + (((size_t)tok * a.Hq + qh) * D + q4 * 8) * 2;
+    const char* qp = reinterpret_cast<const char*>(a.q) + ((size_t)tok * a.Hq + qh) * D * 2;
 #pragma unroll
-    for (int c = 0; c < DC; ++c) qreg[c] = row_ok ? ld16(qp + c * 64) : u32x4{0, 0, 0, 0};
+    for (int c = 0; c < QC; ++c) {
+      const int d0 = U8 ? (c / 2) * 64 + q4 * 16 + (c % 2) * 8 : c * 32 + q4 * 8;
+      const u32x4 v = ld16(qp + d0 * 2);
+      qreg[c] = row_ok ? v : u32x4{0, 0, 0, 0};
+      if constexpr (U8) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          if constexpr (QT == kF16) {
+            qsum += lo_f16(qreg[c][w]) + hi_f16(qreg[c][w]);
+          } else {
+            qsum += __builtin_bit_cast(float, qreg[c][w] << 16) +
+                    __builtin_bit_cast(float, qreg[c][w] & 0xffff0000u);
+          }
+        }
+      }
+    }
+  }
+  if constexpr (U8) {
+    qsum += __shfl_xor(qsum, 16, kWave);
+    qsum += __shfl_xor(qsum, 32, kWave);
   }
   __syncthreads();
 
   const char* kb = reinterpret_cast<const char*>(a.k);
   const char* vb = reinterpret_cast<const char*>(a.v);
-  const size_t tile_elems = (size_t)BS * D;                   // one (block, head) page
+  const char* kszb = reinterpret_cast<const char*>(a.ksz);
+  const char* vszb = reinterpret_cast<const char*>(a.vsz);
   const int Hkv = a.Hkv;
 
-  // Registers of one step: K rows for two 16-key QK tiles, V^T for DT d tiles.
-  auto load_step = [&](int st, u32x4 (&kr)[2][DC], u32x4 (&vr)[DT]) {
+  // Registers of one step (two 16-slot sub-tiles tau): K and V loads, and
+  // for u8 the (scale, zero point) pairs of this lane group's 4 keys.
+  struct Step {
+    u32x4 k[2][LK];
+    u32x4 v[2][LV];
+    u32x4 ks[2], vs[2];
+  };
+
+  // Every load is issued unconditionally: a sub-tile holding no key of
+  // [lo0, ctx) reads the segment's first page instead (always a valid
+  // address) and is masked out in compute_step.  Branch-free loads keep the
+  // outstanding-load count static, so the wait before a step's math covers
+  // that step's loads only, not the prefetch of the next one.
+  auto load_step = [&](int st, Step& r) {
     const int key0 = si.base + st * kKeysPerStep;
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      // QK tile tau: A row m = n16 holds step key (m/4)*8 + tau*4 + m%4, so
-      // the output lands in lane group q4 as keys q4*8 + tau*4 + (0..3).
-      const int t = key0 + (n16 >> 2) * 8 + tau * 4 + (n16 & 3);
-      const bool present = t >= si.lo0 && t < si.ctx;
-      const int phys = present ? s_bt[t / BS - blk_lo] : 0;
-      const char* p = kb + (((size_t)phys * Hkv + h) * tile_elems + (size_t)(t % BS) * D + q4 * 8) * 2;
+      const int t0 = key0 + tau * 16;                         // first key of the sub-tile
+      const bool present = t0 < si.ctx && t0 + 16 > si.lo0;
+      const int page = __builtin_amdgcn_readfirstlane(s_bt[present ? t0 / BS - blk_lo : 0]);
+      const int sub = present ? (t0 % BS) / 16 : 0;
+      const size_t tile = (((size_t)page * Hkv + h) * BS + (size_t)sub * 16) * D;   // elements
+      const char* kp = kb + tile * EB + lane * 16;
+      const char* vp = vb + tile * EB + lane * 16;
 #pragma unroll
-      for (int c = 0; c < DC; ++c) kr[tau][c] = present ? ld16(p + c * 64) : u32x4{0, 0, 0, 0};
+      for (int c = 0; c < LK; ++c) r.k[tau][c] = ld16_stream(kp + c * 1024);
+#pragma unroll
+      for (int c = 0; c < LV; ++c) r.v[tau][c] = ld16_stream(vp + c * 1024);
+      if constexpr (U8) {
+        const size_t srow = (((size_t)page * Hkv + h) * BS + (size_t)sub * 16 + q4 * 4) * 4;
+        r.ks[tau] = ld16_stream(kszb + srow);
+        r.vs[tau] = ld16_stream(vszb + srow);
+      }
     }
-    const int tv = key0 + q4 * 8;                             // this lane's 8 keys
-    const bool vpresent = tv < si.ctx && tv + 8 > si.lo0;
-    const int physv = vpresent ? s_bt[tv / BS - blk_lo] : 0;
-    const char* pv = vb + (((size_t)physv * Hkv + h) * tile_elems + (size_t)n16 * BS + (tv % BS)) * 2;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      vr[dt] = vpresent ? ld16(pv + (size_t)dt * 16 * BS * 2) : u32x4{0, 0, 0, 0};
   };
 
   f32x4 o[DT];
@@ -224,45 +353,54 @@ void pa_segment_fp(SegmentArgs a) {
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;            // running max (log2 units) of this lane's row
   float l_run = 0.f;                  // this lane's share of the running sum
+  float c_run = 0.f;                  // u8: this lane's share of sum p * s_v * zp_v
 
-  auto compute_step = [&](int st, u32x4 (&kr)[2][DC], u32x4 (&vr)[DT]) {
+  auto compute_step = [&](int st, Step& r) {
     const int key0 = si.base + st * kKeysPerStep;
-    f32x4 sacc[2];
+    // S^T for both sub-tiles: lane (row, q4) gets keys key0 + 16*tau + 4*q4 + 0..3
+    float sv[8];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      sacc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (U8) {
 #pragma unroll
-      for (int c = 0; c < DC; ++c) sacc[tau] = mfma32<KV>(kr[tau][c], qreg[c], sacc[tau]);
-    }
-    float sv[8];                      // keys key0 + q4*8 + e of row n16
+        for (int c2 = 0; c2 < LK; ++c2) {
+          const u32x4 w = r.k[tau][c2];
+          const u32x2 a0 = u8x4_to_16<QT>(w[0]), a1 = u8x4_to_16<QT>(w[1]);
+          const u32x2 a2 = u8x4_to_16<QT>(w[2]), a3 = u8x4_to_16<QT>(w[3]);
+          acc = mfma32<QT>(u32x4{a0[0], a0[1], a1[0], a1[1]}, qreg[2 * c2], acc);
+          acc = mfma32<QT>(u32x4{a2[0], a2[1], a3[0], a3[1]}, qreg[2 * c2 + 1], acc);
+        }
+        // q.(u - zp) * s = s * (q.u - zp * sum(q))
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sv[e] = sacc[e >> 2][e & 3] * a.scale_log2;
-
-    const bool interior = key0 >= lo_max && key0 + kKeysPerStep <= si.L + 1;
-    if (!interior) {
-      const int t0 = key0 + q4 * 8;
-      uint32_t keep[4];
+        for (int e = 0; e < 4; ++e) {
+          const float sk = lo_f16(r.ks[tau][e]), zk = hi_f16(r.ks[tau][e]);
+          sv[tau * 4 + e] = sk * (acc[e] - zk * qsum) * a.scale_log2;
+        }
+      } else {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int ta = t0 + 2 * w, tb = ta + 1;
-        keep[w] = ((ta >= si.lo0 && ta < si.ctx) ? 0x0000FFFFu : 0u) |
-                  ((tb >= si.lo0 && tb < si.ctx) ? 0xFFFF0000u : 0u);
+        for (int c = 0; c < QC; ++c) acc = mfma32<QT>(r.k[tau][c], qreg[c], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[tau * 4 + e] = acc[e] * a.scale_log2;
       }
+    }
+
+    // Keys outside [lo0, ctx) may hold anything, NaN included: their logits
+    // become -inf and, since 0 * NaN is not 0, their V (or u8 scale) never
+    // reaches the PV product.
+    const bool interior = key0 >= lo_max && key0 + kKeysPerStep <= si.L + 1;
+    bool kvalid[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kvalid[e] = true;
+    if (!interior) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int t = t0 + e;
+        const int t = key0 + (e >> 2) * 16 + q4 * 4 + (e & 3);
+        kvalid[e] = t >= si.lo0 && t < si.ctx;
         sv[e] = (t >= lo_r && t < hi_r) ? sv[e] : -INFINITY;
       }
-      // keys outside the sequence's readable range may hold anything, NaN
-      // included; their weight is 0 but 0 * NaN is not, so clear them
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        vr[dt][0] &= keep[0];
-        vr[dt][1] &= keep[1];
-        vr[dt][2] &= keep[2];
-        vr[dt][3] &= keep[3];
-      }
     }
+
     float mx = sv[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
@@ -280,38 +418,105 @@ void pa_segment_fp(SegmentArgs a) {
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    u32x4 pb_hi, pb_lo;
-    pack8_split<KV>(p, pb_hi, pb_lo);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      o[dt] *= alpha;
-      o[dt] = mfma32<KV>(vr[dt], pb_hi, o[dt]);
-      o[dt] = mfma32<KV>(vr[dt], pb_lo, o[dt]);
+    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+
+    if constexpr (U8) {
+      // (u - zp) * s folded: P' = p * s_v multiplies the exact codes, and
+      // sum(p * s_v * zp_v) is subtracted from every d at the end
+      float csum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = r.vs[e >> 2][e & 3];
+        const float sp = kvalid[e] ? p[e] * lo_f16(w) : 0.f;
+        csum += kvalid[e] ? sp * hi_f16(w) : 0.f;
+        p[e] = sp;
+      }
+      c_run = c_run * alpha + csum;
     }
+    u32x2 ph[2], pl[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+      split4<QT>(p[tau * 4 + 0], p[tau * 4 + 1], p[tau * 4 + 2], p[tau * 4 + 3], ph[tau], pl[tau]);
+    // PV.  The loaded V registers are never modified: in a boundary step the
+    // f16/bf16 V operand of a key outside [lo0, ctx) is cleared as it is
+    // consumed (u8 codes are finite; their P' is already 0).
+    auto pv = [&](auto masked) {
+      u32x2 vmask[2];
+      if constexpr (decltype(masked)::value) {
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+          vmask[tau][0] = (kvalid[tau * 4 + 0] ? 0x0000FFFFu : 0u) | (kvalid[tau * 4 + 1] ? 0xFFFF0000u : 0u);
+          vmask[tau][1] = (kvalid[tau * 4 + 2] ? 0x0000FFFFu : 0u) | (kvalid[tau * 4 + 3] ? 0xFFFF0000u : 0u);
+        }
+      }
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          u32x2 va;
+          if constexpr (U8) {
+            va = u8x4_to_16<QT>(r.v[tau][dt / 4][dt % 4]);
+          } else {
+            const u32x4 w = r.v[tau][dt / 2];
+            va = (dt % 2) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
+            if constexpr (decltype(masked)::value) va &= vmask[tau];
+          }
+          o[dt] = mfma16<QT>(va, ph[tau], o[dt]);
+          o[dt] = mfma16<QT>(va, pl[tau], o[dt]);
+        }
+      }
+    };
+    if (U8 || interior)
+      pv(std::false_type{});
+    else
+      pv(std::true_type{});
   };
 
-  {
+  // Steps st_begin + wave, + NW, ...  PF == 2: ping-pong between two register
+  // sets so the next step's loads are in flight while this step computes,
+  // with no register copies (a copy of a register still being loaded would
+  // wait).  PF == 1: one register set; the other wavefronts of the CU keep
+  // the memory system busy while this one computes.
+  if constexpr (PF == 1) {
+    Step ra;
+    for (int st = st_begin + wave; st < st_end; st += NW) {
+      load_step(st, ra);
+      compute_step(st, ra);
+    }
+  } else {
     int st = st_begin + wave;
-    u32x4 kr[2][DC], vr[DT];
-    if (st < st_end) load_step(st, kr, vr);
-    while (st < st_end) {
-      const int nx = st + NW;
-      u32x4 kn[2][DC], vn[DT];
-      if (nx < st_end) load_step(nx, kn, vn);
-      compute_step(st, kr, vr);
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-        for (int c = 0; c < DC; ++c) kr[tau][c] = kn[tau][c];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) vr[dt] = vn[dt];
-      st = nx;
+    if (st < st_end) {
+      Step ra, rb;
+      load_step(st, ra);
+      while (true) {
+        if (st + NW >= st_end) {
+          compute_step(st, ra);
+          break;
+        }
+        load_step(st + NW, rb);
+        compute_step(st, ra);
+        st += NW;
+        if (st + NW >= st_end) {
+          compute_step(st, rb);
+          break;
+        }
+        load_step(st + NW, ra);
+        compute_step(st, rb);
+        st += NW;
+      }
     }
   }
 
   // Row sums: each lane group holds a quarter of the keys.
   l_run += __shfl_xor(l_run, 16, kWave);
   l_run += __shfl_xor(l_run, 32, kWave);
+  if constexpr (U8) {
+    c_run += __shfl_xor(c_run, 16, kWave);
+    c_run += __shfl_xor(c_run, 32, kWave);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] -= c_run;
+  }
 
   // Merge the wavefronts of the workgroup: M = max_w m_w, then sum the
   // partials rescaled by 2^(m_w - M), in a fixed order (bitwise repeatable).
@@ -370,46 +575,72 @@ template <int D, int OUT>
 __global__ __launch_bounds__(256) void pa_combine(CombineArgs a) {
   constexpr int LPS = D / 4;                                  // threads per segment row
   constexpr int NSUB = 256 / LPS;                             // segment rows in flight
+  constexpr int K = 8;                                        // partials per thread per batch
   __shared__ float s_m[NSUB];
   __shared__ float s_den[NSUB];
   __shared__ __attribute__((aligned(16))) f32x4 s_acc[NSUB][LPS];
 
   const int pair = blockIdx.x;                                // token * Hq + q head
   const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
   const int sub = tid / LPS;
   const int col = tid % LPS;
   const int n = pair / a.Hq;
+  const int S = a.seg.S;
 
-  // sequence of token n (subsequence_begins is cumulative)
-  int s = 0;
-  while (s < a.seg.num_seqs && !(n < a.seg.sb[s + 1])) ++s;
-  bool ok = s < a.seg.num_seqs && n >= a.seg.sb[s];
-  int n_seg = 0;
-  if (ok) {
-    const SeqInfo si = seq_info(a.seg, s);
-    ok = si.ok;
-    n_seg = min(a.seg.S, (si.n_steps + a.seg.steps_per_seg - 1) / a.seg.steps_per_seg);
-  }
-  const float* ml = a.seg.ws_ml + (size_t)pair * a.seg.S * 2;
-  const float* op = a.seg.ws_o + (size_t)pair * a.seg.S * D + col * 4;
+  // first step of the sequence lookup (64 sequences per wavefront step)
+  const int nseq = a.seg.num_seqs;
+  const int sb_next = lane < nseq ? a.seg.sb[lane + 1] : 0;
+
+  // Every segment of a valid sequence wrote its partial (empty ones as
+  // (-inf, 0)), so these loads depend on nothing but the grid position.  They
+  // are unconditional (clamped index) so they all go out together.
+  const float* ml = a.seg.ws_ml + (size_t)pair * S * 2;
+  const float* op = a.seg.ws_o + (size_t)pair * S * D + col * 4;
   float m = -INFINITY, den = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   bool nan_seen = false;
-#pragma unroll 4
-  for (int jj = sub; jj < n_seg; jj += NSUB) {
-    const float mj = ml[jj * 2];
-    const float lj = ml[jj * 2 + 1];
-    const f32x4 oj = *reinterpret_cast<const f32x4*>(op + (size_t)jj * D);
-    nan_seen |= mj != mj;
-    const float m_new = fmaxf(m, mj);
-    const float base = m_new == -INFINITY ? 0.f : m_new;
-    const float sc = __builtin_amdgcn_exp2f(m - base);
-    const float f = __builtin_amdgcn_exp2f(mj - base);
-    den = den * sc + f * lj;
-    // a segment in which this row saw no key left its O slot unwritten
-    acc = mj == -INFINITY ? acc * sc : acc * sc + f * oj;
-    m = m_new;
+  for (int b = 0; b < S; b += NSUB * K) {
+    float mj[K], lj[K];
+    f32x4 oj[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int jj = b + sub + k * NSUB;
+      const int jc = jj < S ? jj : 0;
+      mj[k] = ml[jc * 2];
+      lj[k] = ml[jc * 2 + 1];
+      oj[k] = *reinterpret_cast<const f32x4*>(op + (size_t)jc * D);
+      mj[k] = jj < S ? mj[k] : -INFINITY;
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      nan_seen |= mj[k] != mj[k];
+      const float m_new = fmaxf(m, mj[k]);
+      const float base = m_new == -INFINITY ? 0.f : m_new;
+      const float sc = __builtin_amdgcn_exp2f(m - base);
+      const float f = __builtin_amdgcn_exp2f(mj[k] - base);
+      // a segment in which this row saw no key left its O slot unwritten
+      const f32x4 o = mj[k] == -INFINITY ? f32x4{0.f, 0.f, 0.f, 0.f} : oj[k];
+      den = den * sc + f * lj[k];
+      acc = acc * sc + f * o;
+      m = m_new;
+    }
   }
+
+  // sequence of token n: first s with n < subsequence_begins[s + 1]; then its
+  // contract check
+  int s = -1;
+  {
+    const unsigned long long hit = __ballot(lane < nseq && n < sb_next);
+    if (hit) s = __builtin_ctzll(hit);
+  }
+  for (int b = kWave; b < nseq && s < 0; b += kWave) {
+    const int k = b + lane;
+    const unsigned long long hit = __ballot(k < nseq && n < a.seg.sb[k + 1]);
+    if (hit) s = b + __builtin_ctzll(hit);
+  }
+  bool ok = s >= 0 && n >= a.seg.sb[s];
+  if (ok) ok = seq_info(a.seg, s).ok;
   if (col == 0) {
     s_m[sub] = m;
     s_den[sub] = den;
@@ -446,52 +677,55 @@ __global__ __launch_bounds__(256) void pa_combine(CombineArgs a) {
 // ---------------------------------------------------------------------------
 // Instances and launchers.
 // ---------------------------------------------------------------------------
-template <int KV, int D, int BS>
-static hipError_t launch_segment_fp(const SegmentArgs& a, dim3 grid, hipStream_t st,
-                                    hipEvent_t ev0, hipEvent_t ev1) {
-  constexpr int WPE = D >= 256 ? 1 : (D >= 128 ? 2 : 4);
+template <int QT, int KV, int D, int BS>
+static hipError_t launch_seg(const SegmentArgs& a, dim3 grid, hipStream_t st, hipEvent_t ev0,
+                             hipEvent_t ev1) {
+  constexpr int WPE = seg_config(KV, D).waves_per_simd;
+  constexpr int PF = seg_config(KV, D).prefetch;
   // with events, the dispatch itself timestamps the kernel's start and end
   if (ev0 || ev1)
-    hipExtLaunchKernelGGL((pa_segment_fp<KV, D, BS, kWavesPerGroup, WPE>), grid,
+    hipExtLaunchKernelGGL((pa_segment<QT, KV, D, BS, kWavesPerGroup, WPE, PF>), grid,
                           dim3(kWavesPerGroup * kWave), 0, st, ev0, ev1, 0, a);
   else
-    hipLaunchKernelGGL((pa_segment_fp<KV, D, BS, kWavesPerGroup, WPE>), grid,
+    hipLaunchKernelGGL((pa_segment<QT, KV, D, BS, kWavesPerGroup, WPE, PF>), grid,
                        dim3(kWavesPerGroup * kWave), 0, st, a);
   return hipGetLastError();
 }
 
-template <int KV, int D>
+template <int QT, int KV, int D>
 static hipError_t dispatch_bs(const SegmentArgs& a, int bs, dim3 grid, hipStream_t st,
                               hipEvent_t e0, hipEvent_t e1) {
   switch (bs) {
-    case 16: return launch_segment_fp<KV, D, 16>(a, grid, st, e0, e1);
-    case 32: return launch_segment_fp<KV, D, 32>(a, grid, st, e0, e1);
-    case 64: return launch_segment_fp<KV, D, 64>(a, grid, st, e0, e1);
+    case 16: return launch_seg<QT, KV, D, 16>(a, grid, st, e0, e1);
+    case 32: return launch_seg<QT, KV, D, 32>(a, grid, st, e0, e1);
+    case 64: return launch_seg<QT, KV, D, 64>(a, grid, st, e0, e1);
   }
   return hipErrorInvalidValue;
 }
 
-template <int KV>
+template <int QT, int KV>
 static hipError_t dispatch_d(const SegmentArgs& a, int D, int bs, dim3 grid, hipStream_t st,
                              hipEvent_t e0, hipEvent_t e1) {
   switch (D) {
-    case 64: return dispatch_bs<KV, 64>(a, bs, grid, st, e0, e1);
-    case 128: return dispatch_bs<KV, 128>(a, bs, grid, st, e0, e1);
-    case 256: return dispatch_bs<KV, 256>(a, bs, grid, st, e0, e1);
+    case 64: return dispatch_bs<QT, KV, 64>(a, bs, grid, st, e0, e1);
+    case 128: return dispatch_bs<QT, KV, 128>(a, bs, grid, st, e0, e1);
+    case 256: return dispatch_bs<QT, KV, 256>(a, bs, grid, st, e0, e1);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_segment(const SegmentArgs& a, int kv_dtype, int D, int bs, dim3 grid,
                           hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  if (kv_dtype == kF16) return dispatch_d<kF16>(a, D, bs, grid, st, e0, e1);
-  if (kv_dtype == kBF16) return dispatch_d<kBF16>(a, D, bs, grid, st, e0, e1);
+  if (kv_dtype == kF16) return dispatch_d<kF16, kF16>(a, D, bs, grid, st, e0, e1);
+  if (kv_dtype == kBF16) return dispatch_d<kBF16, kBF16>(a, D, bs, grid, st, e0, e1);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_segment_u8(const SegmentArgs&, int, int, int, dim3, hipStream_t, hipEvent_t,
-                             hipEvent_t) {
-  return hipErrorNotSupported;
+hipError_t launch_segment_u8(const SegmentArgs& a, int q_dtype, int D, int bs, dim3 grid,
+                             hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  if (q_dtype == kF16) return dispatch_d<kF16, kU8>(a, D, bs, grid, st, e0, e1);
+  if (q_dtype == kBF16) return dispatch_d<kBF16, kU8>(a, D, bs, grid, st, e0, e1);
+  return hipErrorInvalidValue;
 }
 
 template <int D>

@@ -1,6 +1,6 @@
 // membench.hip — libpa_membench.so: the two reference kernels the
 // measurements need next to the attention kernels.
-//   pa_membench_read: streams a buffer once with 16-byte loads (the HBM read
+//   pa_membench_read: streams a buffer once with 16-byte nontemporal loads (the HBM read
 //     ceiling the attention kernel's bandwidth is compared with).
 //   pa_membench_copy: copies a buffer of known size (calibrates the
 //     FETCH_SIZE / WRITE_SIZE counters into bytes).
@@ -16,7 +16,10 @@ __global__ __launch_bounds__(256) void membench_read(const u32x4* __restrict__ p
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   u32x4 acc = {0u, 0u, 0u, 0u};
   for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+    const u32x4 a = __builtin_nontemporal_load(p + i);
+    const u32x4 b = __builtin_nontemporal_load(p + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(p + i + 2 * stride);
+    const u32x4 d = __builtin_nontemporal_load(p + i + 3 * stride);
     acc ^= a ^ b ^ c ^ d;
   }
   for (; i < n16; i += stride) acc ^= p[i];

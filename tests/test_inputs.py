@@ -17,7 +17,9 @@ def test_config1_shape_and_permutation():
     c = pi.config1()
     assert c.num_blocks == 33                      # ceil((512 + 3) / 16)
     assert sorted(c.block_tables[0, :33].tolist()) == list(range(33))
-    assert c.k_cache.shape == (33, 1, 16, 64) and c.v_cache.shape == (33, 1, 64, 16)
+    assert c.k_cache.shape == (33, 1, 16, 64) and c.v_cache.shape == (33, 1, 16, 64)
+    kl, vl = c.logical_pages()
+    assert kl.shape == (33, 1, 16, 64) and vl.shape == (33, 1, 16, 64)
     assert c.q.shape == (3, 4, 64) and c.scale == 1.0 / 8.0
     assert c.max_context_len == 515 and c.subsequence_begins.tolist() == [0, 3]
 
@@ -50,7 +52,7 @@ def test_quantiser_bounds():
 
 
 def test_poisoning_marks_only_unread_slots():
-    c = pi.build_case([9], [37, 5], [3, 2], num_q_heads=2, num_kv_heads=1, head_dim=8,
+    c = pi.build_case([9], [37, 5], [3, 2], num_q_heads=2, num_kv_heads=1, head_dim=32,
                       block_size=16, q_dtype=pi.F16, kv_dtype=pi.F16, spare_blocks=2,
                       poison=True, sliding_window=0)
     for s, (L, T) in enumerate(zip(c.past_lens, c.Ts)):
@@ -58,15 +60,42 @@ def test_poisoning_marks_only_unread_slots():
         assert np.all(np.isfinite(k)) and np.all(np.isfinite(v))
         n = L + T
         last = c.block_tables[s, (n - 1) // 16]
-        tail = c.k_cache[last, :, n % 16 or 16:, :]
+        tail = c.logical_pages()[0][last, :, n % 16 or 16:, :]
         if n % 16:
             assert np.all(pi.f16_bits_to_f32(tail) != pi.f16_bits_to_f32(tail))   # NaN
-    w = pi.build_case([9], [70], [2], num_q_heads=2, num_kv_heads=1, head_dim=8, block_size=16,
+    w = pi.build_case([9], [70], [2], num_q_heads=2, num_kv_heads=1, head_dim=32, block_size=16,
                       q_dtype=pi.BF16, kv_dtype=pi.BF16, poison=True, sliding_window=20)
     k, v = w.logical_kv_f32(0)
     lo0 = 70 + 1 - 20
     assert np.all(np.isnan(k[:lo0])) and np.all(np.isfinite(k[lo0:]))
     assert np.all(np.isnan(v[:lo0])) and np.all(np.isfinite(v[lo0:]))
+
+
+def test_tiled_layout_operand_order():
+    """A wave load of 16 bytes per lane reads lane l's MFMA operand: K lane
+    (row m, group q) gets d = c*32 + q*8 .. +8 of slot m; V lane (d n, group q)
+    gets slots 4q .. 4q+3 of d-tiles 2p and 2p+1."""
+    D, bs = 64, 32
+    for u8 in (False,):
+        slot = np.arange(bs)[:, None] * 1000 + np.arange(D)[None, :]      # encodes (slot, d)
+        tk = pi.tile_k(slot[None], u8)[0]
+        tv = pi.tile_v(slot[None], u8)[0]
+        for tau in range(bs // 16):
+            for c in range(D // 32):
+                chunk = tk[((tau * (D // 32) + c) * 64) * 8:((tau * (D // 32) + c) * 64 + 64) * 8]
+                for lane in range(64):
+                    q, m = divmod(lane, 16)
+                    got = chunk[lane * 8:(lane + 1) * 8]
+                    want = [(tau * 16 + m) * 1000 + c * 32 + q * 8 + e for e in range(8)]
+                    assert got.tolist() == want
+            for p in range(D // 32):
+                chunk = tv[((tau * (D // 32) + p) * 64) * 8:((tau * (D // 32) + p) * 64 + 64) * 8]
+                for lane in range(64):
+                    q, n = divmod(lane, 16)
+                    got = chunk[lane * 8:(lane + 1) * 8]
+                    want = [(tau * 16 + 4 * q + j) * 1000 + (2 * p + half) * 16 + n
+                            for half in range(2) for j in range(4)]
+                    assert got.tolist() == want
 
 
 def test_kv_bytes_formula():

@@ -18,8 +18,12 @@ MUTANTS = [
     ("gqa_modulo_mapping", [("const int g = h / (Hq / Hkv);", "const int g = h % Hkv;")]),
     ("scale_dropped", [("z[t - lo] = a->scale * dot;", "z[t - lo] = dot;")]),
     ("window_one_short", [("lo = hi - a->sliding_window;", "lo = hi - a->sliding_window + 1;")]),
-    ("v_read_in_k_layout", [("const size_t vidx = ((blk * Hkv + g) * D + d) * bs + slot;",
-                             "const size_t vidx = row * D + d;")]),
+    ("v_read_in_k_layout", [("const size_t vidx = page + v_offset(slot, d, D, u8);",
+                             "const size_t vidx = page + k_offset(slot, d, D, u8);")]),
+    ("k_page_row_major", [("page + k_offset(slot, d, D, u8), row);",
+                           "page + (size_t)slot * D + d, row);")]),
+    ("v_slot_quads_swapped", [("return ((((st * (D / 32) + d / 32) * 4 + qq) * 16 + d % 16) * 2 + (d % 32) / 16) * 4 + slot % 4;",
+                               "return ((((st * (D / 32) + d / 32) * 4 + slot % 4) * 16 + d % 16) * 2 + (d % 32) / 16) * 4 + qq;")]),
     ("block_table_ignored", [("const size_t blk = (size_t)table[t / bs];",
                               "const size_t blk = (size_t)(t / bs);")]),
     ("slot_shifted", [("const int slot = t % bs;", "const int slot = (t + 1) % bs;")]),
@@ -36,7 +40,8 @@ MUTANTS = [
     ("bf16_shift", [("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;")]),
     ("q_head_major_layout", [("const size_t q_off = ((size_t)n * Hq + h) * D;",
                               "const size_t q_off = ((size_t)h * a->num_tokens + n) * D;")]),
-    ("k_dims_reversed", [("row * D + d, row);", "row * D + (D - 1 - d), row);")]),
+    ("k_dims_reversed", [("page + k_offset(slot, d, D, u8), row);",
+                          "page + k_offset(slot, D - 1 - d, D, u8), row);")]),
 ]
 
 PIN_ORDER = ["hand", "closed", "rows", "window", "gqa", "u8", "permutation", "ragged", "sdpa"]

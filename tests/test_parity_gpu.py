@@ -63,6 +63,29 @@ def test_swa_pair_global_and_window(L):
     _full(pi.config4(L, window=1024, poison=True))
 
 
+def test_u8_d256():
+    _full(pi.config3(32768, 3, poison=True))
+
+
+def test_u8_small_shapes():
+    rng = np.random.default_rng(91)
+    k = 0
+    for D in (64, 128, 256):
+        for bs in (16, 32, 64):
+            for qd in (pi.F16, pi.BF16):
+                G = int(rng.choice([1, 2, 4, 8]))
+                T = int(rng.integers(1, max(1, min(4, 16 // G)) + 1))
+                L = int(rng.choice([0, 5, 31, 32, 47, 200, int(rng.integers(0, 900))]))
+                W = int(rng.choice([0, 0, 3, 50]))
+                Hkv = int(rng.choice([1, 2]))
+                _full(pi.build_case([600, k], [L], [T], num_q_heads=G * Hkv, num_kv_heads=Hkv,
+                                    head_dim=D, block_size=bs, q_dtype=qd, kv_dtype=pi.U8,
+                                    sliding_window=W, spare_blocks=2, poison=True,
+                                    name=f"u8small_D{D}_bs{bs}_q{qd}_G{G}_T{T}_L{L}_W{W}"),
+                      rounding_aware=True)
+                k += 1
+
+
 def test_ragged_batch():
     _sampled(pi.config5(poison=True), n=160)
 
@@ -137,7 +160,8 @@ def _relabel(case, seed):
 
 def test_block_relabelling_is_bitwise_invisible():
     for case in (pi.config2(8192, 3), pi.config4(4096, window=1024, poison=True),
-                 pi.config5(rep=2, lo=100, hi=5000, poison=True)):
+                 pi.config5(rep=2, lo=100, hi=5000, poison=True),
+                 pi.config3(3000, 4, poison=True)):
         a = to_f64(run_gpu(case))
         b = to_f64(run_gpu(_relabel(case, 3)))
         assert np.array_equal(a, b), case.name
