@@ -15,6 +15,7 @@ constexpr int kMaxT = 4;             // verify rows per sequence
 constexpr int kWavesPerGroup = 4;    // wavefronts per segment workgroup
 constexpr int kMaxSegBlocks = 1040;  // LDS slots for a segment's block ids
 constexpr int kDeviceContract = 5;   // value of PA_ERR_DEVICE_CONTRACT
+constexpr float kRescaleLog2 = 8.f;  // softmax reference max moves only past this margin
 
 struct SegmentArgs {
   const void* q;
@@ -56,8 +57,8 @@ struct SegConfig {
   int prefetch;
 };
 constexpr SegConfig seg_config(int kv_dtype, int D) {
-  if (kv_dtype == kU8) return D >= 256 ? SegConfig{1, 2} : D >= 128 ? SegConfig{2, 2} : SegConfig{4, 1};
-  return D >= 256 ? SegConfig{1, 1} : D >= 128 ? SegConfig{3, 1} : SegConfig{4, 1};
+  if (kv_dtype == kU8) return D >= 256 ? SegConfig{2, 1} : D >= 128 ? SegConfig{2, 2} : SegConfig{4, 1};
+  return D >= 256 ? SegConfig{1, 1} : D >= 128 ? SegConfig{1, 2} : SegConfig{4, 1};
 }
 // Resident segment workgroups per CU (4 SIMDs per CU).
 constexpr int groups_per_cu(int kv_dtype, int D) {

@@ -123,17 +123,19 @@ __device__ __forceinline__ void split4(float p0, float p1, float p2, float p3, u
   }
 }
 
-// Four u8 codes (one dword) as four exact 16-bit values of the MFMA type.
-// f16: byte b placed under exponent 0x64 is the half 1024 + b; subtracting
-// 1024 is exact.  bf16 has too few mantissa bits for that trick and goes
-// through f32.
+// Four u8 codes (one dword) as four exact 16-bit values of the MFMA type,
+// offset by kU8Bias<QT>.  f16: byte b placed under exponent 0x64 is the half
+// 1024 + b, one byte permute per two codes; the 1024 is folded into the zero
+// point by the caller.  bf16 has too few mantissa bits for that and goes
+// through f32 without an offset.
+template <int QT>
+constexpr float kU8Bias = QT == kF16 ? 1024.f : 0.f;
+
 template <int QT>
 __device__ __forceinline__ u32x2 u8x4_to_16(uint32_t w) {
   if constexpr (QT == kF16) {
-    const f16x2 bias = {(_Float16)1024.f, (_Float16)1024.f};
-    const f16x2 a = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, w, 0x04010400u)) - bias;
-    const f16x2 b = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, w, 0x04030402u)) - bias;
-    return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+    return u32x2{__builtin_amdgcn_perm(0x64646464u, w, 0x04010400u),
+                 __builtin_amdgcn_perm(0x64646464u, w, 0x04030402u)};
   } else {
     bf16x4 h;
 #pragma unroll
@@ -221,8 +223,18 @@ void pa_segment(SegmentArgs a) {
 
   const SeqInfo si = seq_info(a, s);
   if (!si.ok) {
+    // A sequence that breaks the contract: its partials for this segment
+    // become NaN (for the tokens it claims that exist), so the combine turns
+    // its rows into NaN without re-checking the sequence.
     if (j == 0 && h == 0 && threadIdx.x == 0) atomicExch(a.status, kDeviceContract);
-    return;                           // the combine kernel writes NaN rows
+    const int t0 = min(max(si.b0, 0), a.num_tokens);
+    const int t1 = min(max(si.b0 + si.T, t0), a.num_tokens);
+    for (int x = threadIdx.x; x < (t1 - t0) * a.G; x += NW * kWave) {
+      const size_t row = ((size_t)(t0 + x / a.G) * a.Hq + h * a.G + x % a.G) * a.S + j;
+      a.ws_ml[row * 2 + 0] = NAN;
+      a.ws_ml[row * 2 + 1] = 0.f;
+    }
+    return;
   }
   const int T = si.T;
   const int R = a.G * T;
@@ -361,25 +373,31 @@ void pa_segment(SegmentArgs a) {
     float sv[8];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      // two interleaved accumulation chains: no MFMA waits on the one before
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
       if constexpr (U8) {
 #pragma unroll
         for (int c2 = 0; c2 < LK; ++c2) {
           const u32x4 w = r.k[tau][c2];
           const u32x2 a0 = u8x4_to_16<QT>(w[0]), a1 = u8x4_to_16<QT>(w[1]);
           const u32x2 a2 = u8x4_to_16<QT>(w[2]), a3 = u8x4_to_16<QT>(w[3]);
-          acc = mfma32<QT>(u32x4{a0[0], a0[1], a1[0], a1[1]}, qreg[2 * c2], acc);
-          acc = mfma32<QT>(u32x4{a2[0], a2[1], a3[0], a3[1]}, qreg[2 * c2 + 1], acc);
+          acc0 = mfma32<QT>(u32x4{a0[0], a0[1], a1[0], a1[1]}, qreg[2 * c2], acc0);
+          acc1 = mfma32<QT>(u32x4{a2[0], a2[1], a3[0], a3[1]}, qreg[2 * c2 + 1], acc1);
         }
-        // q.(u - zp) * s = s * (q.u - zp * sum(q))
+        const f32x4 acc = acc0 + acc1;
+        // q.(u - zp) * s = s * (q.(u + bias) - (zp + bias) * sum(q))
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float sk = lo_f16(r.ks[tau][e]), zk = hi_f16(r.ks[tau][e]);
+          const float sk = lo_f16(r.ks[tau][e]), zk = hi_f16(r.ks[tau][e]) + kU8Bias<QT>;
           sv[tau * 4 + e] = sk * (acc[e] - zk * qsum) * a.scale_log2;
         }
       } else {
 #pragma unroll
-        for (int c = 0; c < QC; ++c) acc = mfma32<QT>(r.k[tau][c], qreg[c], acc);
+        for (int c = 0; c < QC; c += 2) {
+          acc0 = mfma32<QT>(r.k[tau][c], qreg[c], acc0);
+          if (c + 1 < QC) acc1 = mfma32<QT>(r.k[tau][c + 1], qreg[c + 1], acc1);
+        }
+        const f32x4 acc = acc0 + acc1;
 #pragma unroll
         for (int e = 0; e < 4; ++e) sv[tau * 4 + e] = acc[e] * a.scale_log2;
       }
@@ -406,9 +424,21 @@ void pa_segment(SegmentArgs a) {
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
     mx = xor_max(mx, 16);
     mx = xor_max(mx, 32);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    // Lazy rescaling: weights are taken relative to a reference max m_run
+    // that only moves when a logit passes it by more than 2^kRescaleLog2, so
+    // weights stay <= 256 (exact in the hi/lo split) and the O rescale runs
+    // in few steps.  The branch is wave-uniform.
+    const bool need = mx > m_run + kRescaleLog2;
+    if (__any(need)) {
+      const float m_new = need ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      l_run *= alpha;
+      c_run *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float p[8];
     float psum = 0.f;
 #pragma unroll
@@ -416,23 +446,20 @@ void pa_segment(SegmentArgs a) {
       p[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
       psum += p[e];
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    l_run += psum;
 
     if constexpr (U8) {
-      // (u - zp) * s folded: P' = p * s_v multiplies the exact codes, and
-      // sum(p * s_v * zp_v) is subtracted from every d at the end
+      // (u - zp) * s folded: P' = p * s_v multiplies the (offset) codes, and
+      // sum(p * s_v * (zp_v + bias)) is subtracted from every d at the end
       float csum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t w = r.vs[e >> 2][e & 3];
         const float sp = kvalid[e] ? p[e] * lo_f16(w) : 0.f;
-        csum += kvalid[e] ? sp * hi_f16(w) : 0.f;
+        csum += kvalid[e] ? sp * (hi_f16(w) + kU8Bias<QT>) : 0.f;
         p[e] = sp;
       }
-      c_run = c_run * alpha + csum;
+      c_run += csum;
     }
     u32x2 ph[2], pl[2];
 #pragma unroll
@@ -450,21 +477,25 @@ void pa_segment(SegmentArgs a) {
           vmask[tau][1] = (kvalid[tau * 4 + 2] ? 0x0000FFFFu : 0u) | (kvalid[tau * 4 + 3] ? 0xFFFF0000u : 0u);
         }
       }
+      auto vop = [&](int tau, int dt) {
+        u32x2 va;
+        if constexpr (U8) {
+          va = u8x4_to_16<QT>(r.v[tau][dt / 4][dt % 4]);
+        } else {
+          const u32x4 w = r.v[tau][dt / 2];
+          va = (dt % 2) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
+          if constexpr (decltype(masked)::value) va &= vmask[tau];
+        }
+        return va;
+      };
+      // all hi products of a sub-tile, then all lo: consecutive MFMAs never
+      // update the same accumulator
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          u32x2 va;
-          if constexpr (U8) {
-            va = u8x4_to_16<QT>(r.v[tau][dt / 4][dt % 4]);
-          } else {
-            const u32x4 w = r.v[tau][dt / 2];
-            va = (dt % 2) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
-            if constexpr (decltype(masked)::value) va &= vmask[tau];
-          }
-          o[dt] = mfma16<QT>(va, ph[tau], o[dt]);
-          o[dt] = mfma16<QT>(va, pl[tau], o[dt]);
-        }
+        for (int dt = 0; dt < DT; ++dt) o[dt] = mfma16<QT>(vop(tau, dt), ph[tau], o[dt]);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] = mfma16<QT>(vop(tau, dt), pl[tau], o[dt]);
       }
     };
     if (U8 || interior)
@@ -555,7 +586,8 @@ void pa_segment(SegmentArgs a) {
       acc += f * *reinterpret_cast<const f32x4*>(&s_o[w][r][c4]);
       lsum += f * s_l[w][r];
     }
-    *reinterpret_cast<f32x4*>(&a.ws_o[row * D + c4]) = acc;
+    // partials are not re-read by this kernel: stream them out
+    __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(&a.ws_o[row * D + c4]));
     if (c4 == 0) {
       a.ws_ml[row * 2 + 0] = bad ? NAN : M;
       a.ws_ml[row * 2 + 1] = lsum;
@@ -588,9 +620,11 @@ __global__ __launch_bounds__(256) void pa_combine(CombineArgs a) {
   const int n = pair / a.Hq;
   const int S = a.seg.S;
 
-  // first step of the sequence lookup (64 sequences per wavefront step)
+  // subsequence_begins, 64 entries per lane step: its first chunk goes out
+  // with the partial loads
   const int nseq = a.seg.num_seqs;
   const int sb_next = lane < nseq ? a.seg.sb[lane + 1] : 0;
+  const int sb_this = lane < nseq ? a.seg.sb[lane] : 0;
 
   // Every segment of a valid sequence wrote its partial (empty ones as
   // (-inf, 0)), so these loads depend on nothing but the grid position.  They
@@ -627,20 +661,28 @@ __global__ __launch_bounds__(256) void pa_combine(CombineArgs a) {
     }
   }
 
-  // sequence of token n: first s with n < subsequence_begins[s + 1]; then its
-  // contract check
+  // subsequence_begins must start at 0, never decrease and end at
+  // num_tokens; then token n belongs to the first s with n < sb[s + 1].  A
+  // sequence that breaks the rest of the contract left NaN in its partials.
+  bool ok = true;
   int s = -1;
   {
+    ok &= !__any(lane < nseq && sb_this > sb_next);
+    ok &= __shfl(sb_this, 0, kWave) == 0;
+    if (nseq <= kWave) ok &= __shfl(sb_next, nseq - 1, kWave) == a.seg.num_tokens;
     const unsigned long long hit = __ballot(lane < nseq && n < sb_next);
     if (hit) s = __builtin_ctzll(hit);
   }
-  for (int b = kWave; b < nseq && s < 0; b += kWave) {
+  for (int b = kWave; b < nseq; b += kWave) {                 // more than 64 sequences
     const int k = b + lane;
-    const unsigned long long hit = __ballot(k < nseq && n < a.seg.sb[k + 1]);
-    if (hit) s = b + __builtin_ctzll(hit);
+    const int nx = k < nseq ? a.seg.sb[k + 1] : 0;
+    const int th = k < nseq ? a.seg.sb[k] : 0;
+    ok &= !__any(k < nseq && th > nx);
+    if (b + kWave >= nseq) ok &= __shfl(nx, nseq - 1 - b, kWave) == a.seg.num_tokens;
+    const unsigned long long hit = __ballot(k < nseq && n < nx);
+    if (s < 0 && hit) s = b + __builtin_ctzll(hit);
   }
-  bool ok = s >= 0 && n >= a.seg.sb[s];
-  if (ok) ok = seq_info(a.seg, s).ok;
+  ok &= s >= 0;
   if (col == 0) {
     s_m[sub] = m;
     s_den[sub] = den;

@@ -146,7 +146,9 @@ def test_plan_fills_the_gpu_at_batch_one(L, T):
     pl = plan(L + T, num_tokens=T)
     check_plan_covers(pl, L + T)
     wgs = pl["grid"][0] * pl["grid"][1] * pl["grid"][2]
-    assert wgs >= 256                                   # at least one workgroup per CU
+    # f16 D=128 segment workgroups run one per CU: the grid stays within one
+    # round of resident workgroups (no tail round) and still covers most CUs
+    assert 128 <= wgs <= 256
     assert pl["steps_per_segment"] % pl["waves_per_group"] == 0   # equal steps per wavefront
     rows = T * 32
     assert pl["workspace_bytes"] == 256 + -(-rows * pl["num_segments"] * 8 // 256) * 256 + \
