@@ -46,7 +46,13 @@ hipError_t launch_segment(const SegmentArgs& a, int kv_dtype, int D, int bs, dim
                           hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_segment_u8(const SegmentArgs& a, int q_dtype, int D, int bs, dim3 grid,
                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
-hipError_t launch_combine(const CombineArgs& a, int out_dtype, int D, dim3 grid, hipStream_t st);
+hipError_t launch_combine(const CombineArgs& a, int out_dtype, int D, int threads, dim3 grid,
+                          hipStream_t st);
+// Combine workgroup size: enough threads that each loads at most 8 of the S
+// partials of its (token, q head) row (one batch of loads), 256..1024.
+constexpr int combine_threads(int S, int D) {
+  return S * (D / 4) <= 256 * 8 ? 256 : S * (D / 4) <= 512 * 8 ? 512 : 1024;
+}
 
 // Per (cache dtype, head_dim): wavefronts per SIMD the segment kernel is
 // compiled for (its register budget, no spills) and the steps each

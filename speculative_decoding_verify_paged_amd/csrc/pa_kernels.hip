@@ -597,16 +597,17 @@ void pa_segment(SegmentArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Combine kernel: one workgroup per (token, q head).  Thread t owns d columns
+// Combine kernel: one workgroup per (token, q head), NT threads with NT sized
+// by the host so all S partials are loaded in one batch of K per thread.  Thread t owns d columns
 // [c4, c4 + 4) of the segments sub, sub + NSUB, ...; it merges them with the
 // same online rescaling as the segment kernel (every load independent of the
 // previous iteration's arithmetic, so they all go out at once), then the
 // NSUB partial states are merged through LDS in a fixed order.
 // ---------------------------------------------------------------------------
-template <int D, int OUT>
-__global__ __launch_bounds__(256) void pa_combine(CombineArgs a) {
+template <int D, int OUT, int NT>
+__global__ __launch_bounds__(NT) void pa_combine(CombineArgs a) {
   constexpr int LPS = D / 4;                                  // threads per segment row
-  constexpr int NSUB = 256 / LPS;                             // segment rows in flight
+  constexpr int NSUB = NT / LPS;                              // segment rows in flight
   constexpr int K = 8;                                        // partials per thread per batch
   __shared__ float s_m[NSUB];
   __shared__ float s_den[NSUB];
@@ -770,20 +771,32 @@ hipError_t launch_segment_u8(const SegmentArgs& a, int q_dtype, int D, int bs, d
   return hipErrorInvalidValue;
 }
 
-template <int D>
-static hipError_t launch_combine_d(const CombineArgs& a, int out_dtype, dim3 grid, hipStream_t st) {
+template <int D, int NT>
+static hipError_t launch_combine_nt(const CombineArgs& a, int out_dtype, dim3 grid, hipStream_t st) {
   if (out_dtype == kF16)
-    hipLaunchKernelGGL((pa_combine<D, kF16>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((pa_combine<D, kF16, NT>), grid, dim3(NT), 0, st, a);
   else
-    hipLaunchKernelGGL((pa_combine<D, kBF16>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((pa_combine<D, kBF16, NT>), grid, dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const CombineArgs& a, int out_dtype, int D, dim3 grid, hipStream_t st) {
+template <int D>
+static hipError_t launch_combine_d(const CombineArgs& a, int out_dtype, int threads, dim3 grid,
+                                   hipStream_t st) {
+  switch (threads) {
+    case 256: return launch_combine_nt<D, 256>(a, out_dtype, grid, st);
+    case 512: return launch_combine_nt<D, 512>(a, out_dtype, grid, st);
+    case 1024: return launch_combine_nt<D, 1024>(a, out_dtype, grid, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_combine(const CombineArgs& a, int out_dtype, int D, int threads, dim3 grid,
+                          hipStream_t st) {
   switch (D) {
-    case 64: return launch_combine_d<64>(a, out_dtype, grid, st);
-    case 128: return launch_combine_d<128>(a, out_dtype, grid, st);
-    case 256: return launch_combine_d<256>(a, out_dtype, grid, st);
+    case 64: return launch_combine_d<64>(a, out_dtype, threads, grid, st);
+    case 128: return launch_combine_d<128>(a, out_dtype, threads, grid, st);
+    case 256: return launch_combine_d<256>(a, out_dtype, threads, grid, st);
   }
   return hipErrorInvalidValue;
 }

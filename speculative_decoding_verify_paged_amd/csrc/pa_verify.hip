@@ -88,7 +88,7 @@ int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_ve
   pl->combine_grid[0] = (int32_t)rows;
   pl->combine_grid[1] = 1;
   pl->combine_grid[2] = 1;
-  pl->combine_threads = 256;
+  pl->combine_threads = pav::combine_threads((int)S, p->head_dim);
   const size_t ml_bytes = (size_t)rows * S * 2 * sizeof(float);
   const size_t o_bytes = (size_t)rows * S * p->head_dim * sizeof(float);
   pl->workspace_bytes = 256 + ((ml_bytes + 255) / 256) * 256 + o_bytes;
@@ -195,7 +195,7 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
   c.out = out;
   c.num_tokens = p->num_tokens;
   c.Hq = p->num_q_heads;
-  e = pav::launch_combine(c, p->q_dtype, p->head_dim, dim3(pl.combine_grid[0]), st);
+  e = pav::launch_combine(c, p->q_dtype, p->head_dim, pl.combine_threads, dim3(pl.combine_grid[0]), st);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
