@@ -95,7 +95,7 @@ typedef enum pa_dtype {
  * group * max T_s <= 16 enforced per sequence on the device, dtype pairs
  * (q, kv) = (f16, f16), (bf16, bf16), (f16, u8), (bf16, u8). */
 typedef struct pa_verify_params {
-  int32_t num_seqs;            /* sequences in the batch, >= 1 */
+  int32_t num_seqs;            /* sequences in the batch, 1 ..= 65535 */
   int32_t num_tokens;          /* == subsequence_begins[num_seqs], >= num_seqs */
   int32_t num_q_heads;         /* Hq */
   int32_t num_kv_heads;        /* Hkv, divides Hq */
@@ -122,11 +122,13 @@ typedef struct pa_verify_params {
  * what a call will launch. */
 typedef struct pa_verify_plan {
   int32_t num_segments;        /* S: KV segments per (sequence, KV head) */
-  int32_t steps_per_segment;   /* key steps of keys_per_step keys per segment */
+  int32_t steps_per_segment;   /* steps of keys_per_step keys in the longest segment; segment j
+                                  covers steps [j*N/S, (j+1)*N/S) of num_steps = N */
+  int32_t num_steps;           /* N: steps covering span */
   int32_t keys_per_step;       /* keys one wavefront consumes per loop iteration */
   int32_t span;                /* bound on keys any one sequence's rows touch */
   int32_t waves_per_group;     /* wavefronts per segment workgroup */
-  int32_t grid[3];             /* segment kernel grid: (S, Hkv, num_seqs) */
+  int32_t grid[3];             /* segment kernel grid: (Hkv, num_seqs, S); z = S-1-j */
   int32_t block_threads;       /* segment kernel workgroup size */
   int32_t combine_grid[3];     /* combine kernel grid */
   int32_t combine_threads;     /* combine kernel workgroup size */

@@ -31,7 +31,7 @@ struct SegmentArgs {
   int32_t* status;                   // sticky device status word
   int32_t num_seqs, num_tokens, Hq, Hkv, G;
   int32_t num_blocks, mbps, window, max_ctx;
-  int32_t S, steps_per_seg;
+  int32_t S, steps_per_seg, n_steps;   // segments; max steps of one segment; steps the host plans for
   float scale_log2;                  // scale * log2(e)
 };
 
@@ -55,22 +55,24 @@ constexpr int combine_threads(int S, int D) {
 }
 
 // Per (cache dtype, head_dim): wavefronts per SIMD the segment kernel is
-// compiled for (its register budget, no spills) and the steps each
-// wavefront keeps loaded (1: load then compute; 2: the next step's loads in
-// flight during this step's math).  The planner sizes the grid from it.
+// compiled for (its register budget, no spills), the steps each wavefront
+// keeps loaded (1: load then compute; 2: the next step's loads in flight
+// during this step's math), and the segment workgroups the planner puts on
+// each CU (at most the resident count, 4 SIMDs per CU).  u8 with D = 256
+// runs two wavefronts per SIMD for latency hiding but one workgroup per CU
+// in the plan: twice the segments only doubles the partials the combine
+// reads (measured on MI355X: no faster segment kernel, slower call).
 struct SegConfig {
   int waves_per_simd;
   int prefetch;
+  int groups_per_cu;
 };
 constexpr SegConfig seg_config(int kv_dtype, int D) {
-  if (kv_dtype == kU8) return D >= 256 ? SegConfig{2, 1} : D >= 128 ? SegConfig{2, 2} : SegConfig{4, 1};
-  return D >= 256 ? SegConfig{1, 1} : D >= 128 ? SegConfig{1, 2} : SegConfig{4, 1};
+  if (kv_dtype == kU8)
+    return D >= 256 ? SegConfig{2, 1, 1} : D >= 128 ? SegConfig{2, 2, 2} : SegConfig{4, 1, 4};
+  return D >= 256 ? SegConfig{1, 1, 1} : D >= 128 ? SegConfig{1, 2, 1} : SegConfig{4, 1, 4};
 }
-// Resident segment workgroups per CU (4 SIMDs per CU).
-constexpr int groups_per_cu(int kv_dtype, int D) {
-  return seg_config(kv_dtype, D).waves_per_simd * 4 / kWavesPerGroup > 0
-             ? seg_config(kv_dtype, D).waves_per_simd * 4 / kWavesPerGroup
-             : 1;
-}
+constexpr int groups_per_cu(int kv_dtype, int D) { return seg_config(kv_dtype, D).groups_per_cu; }
+static_assert(kWavesPerGroup == 4, "the table above assumes 4-wavefront workgroups");
 
 }  // namespace pav

@@ -33,9 +33,10 @@
 //   S^T[slot, r] = K[slot, :] . Q[r, :]    v_mfma_f32_16x16x32, A = one K load per 32 d,
 //                                           B = Q rows held in registers
 //   online softmax per row (lane-local, two cross-lane max steps)
-//   O^T[d, r] += V^T[d, slot] . P^T[slot, r]  v_mfma_f32_16x16x16, A = half a V load,
-//                                           B = the S^T accumulator itself after exp
-//                                           (hi + lo 16-bit parts)
+//   O^T[d, r] += V^T[d, key] . P^T[key, r]  v_mfma_f32_16x16x32 over all 32 keys,
+//                                           A = half of each sub-tile's V load,
+//                                           B = the S^T accumulators after exp
+//                                           (bf16: hi + lo parts)
 // Every lane owns one stacked row r = lane % 16 in all three products, so the
 // softmax state and its rescale never leave the lane.
 #include <hip/hip_ext.h>
@@ -83,43 +84,28 @@ __device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
   }
 }
 
-// 16x16x16: A and B hold 4 consecutive k values per lane.
+// The eight softmax weights of a lane — keys 4*q4 + 0..3 of sub-tile 0, then
+// of sub-tile 1 — as the B operand of a 16x16x32 product.  f16: one
+// round-to-nearest per weight (at most 2^-11 relative).  bf16 keeps only 8
+// bits, which costs up to 2^-9 of max|v| when a few keys dominate, so the
+// weights are split as hi = rne(p), lo = rne(p - hi) and PV runs on both.
 template <int QT>
-__device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
+__device__ __forceinline__ void pack_p(const float (&p)[8], u32x4& hi, u32x4& lo) {
   if constexpr (QT == kF16) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
-                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
-  } else {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
-                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
-  }
-}
-
-// Four softmax weights as two 16-bit MFMA operands, hi = rne16(p) and
-// lo = rne16(p - hi): PV runs on both, so the weights keep ~16 more bits than
-// one 16-bit rounding (bf16 alone would cost up to 2^-9 of max|v| when a few
-// keys dominate).
-template <int QT>
-__device__ __forceinline__ void split4(float p0, float p1, float p2, float p3, u32x2& hi, u32x2& lo) {
-  const float p[4] = {p0, p1, p2, p3};
-  if constexpr (QT == kF16) {
-    f16x4 h, l;
+    f16x8 h;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      h[e] = (_Float16)p[e];
-      l[e] = (_Float16)(p[e] - (float)h[e]);
-    }
-    hi = __builtin_bit_cast(u32x2, h);
-    lo = __builtin_bit_cast(u32x2, l);
+    for (int e = 0; e < 8; ++e) h[e] = (_Float16)p[e];
+    hi = __builtin_bit_cast(u32x4, h);
+    lo = u32x4{0, 0, 0, 0};
   } else {
-    bf16x4 h, l;
+    bf16x8 h, l;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < 8; ++e) {
       h[e] = (__bf16)p[e];
       l[e] = (__bf16)(p[e] - (float)h[e]);
     }
-    hi = __builtin_bit_cast(u32x2, h);
-    lo = __builtin_bit_cast(u32x2, l);
+    hi = __builtin_bit_cast(u32x4, h);
+    lo = __builtin_bit_cast(u32x4, l);
   }
 }
 
@@ -203,7 +189,10 @@ void pa_segment(SegmentArgs a) {
   const int wave = threadIdx.x / kWave;
   const int n16 = lane & 15;          // stacked query row owned by this lane
   const int q4 = lane >> 4;           // lane group
-  const int j = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  // Grid (Hkv, num_seqs, S), segments last and in reverse: the launch
+  // starts with the highest segments, which only the longest sequences of a
+  // ragged batch have, so their work is not left for the final round.
+  const int h = blockIdx.x, s = blockIdx.y, j = a.S - 1 - (int)blockIdx.z;
   const int32_t* bt_row = a.bt + (size_t)s * a.mbps;
 
   // Full-causal layers: segment j's block range does not depend on the
@@ -212,8 +201,12 @@ void pa_segment(SegmentArgs a) {
   // instead of two.  The loads stay inside the block-table row; ids of
   // blocks past the sequence are never used.
   constexpr int kSlots = (kMaxSegBlocks + NW * kWave - 1) / (NW * kWave);
+  // Segment j owns steps [j*N/S, (j+1)*N/S) of the N steps planned on the
+  // host: segment lengths differ by at most one step.
+  const int st_begin = (int)(((int64_t)j * a.n_steps) / a.S);
+  const int st_cap = (int)(((int64_t)(j + 1) * a.n_steps) / a.S);
   int spec_id[kSlots];
-  const int spec_lo = (j * a.steps_per_seg * kKeysPerStep) / BS;
+  const int spec_lo = (st_begin * kKeysPerStep) / BS;
   const int spec_n = a.window == 0 ? min(a.mbps - spec_lo, (a.steps_per_seg * kKeysPerStep) / BS + 1) : 0;
 #pragma unroll
   for (int k = 0; k < kSlots; ++k) {
@@ -238,8 +231,7 @@ void pa_segment(SegmentArgs a) {
   }
   const int T = si.T;
   const int R = a.G * T;
-  const int st_begin = j * a.steps_per_seg;
-  const int st_end = min(si.n_steps, st_begin + a.steps_per_seg);
+  const int st_end = min(si.n_steps, st_cap);
   if (st_begin >= st_end) {
     // no key of this sequence falls in segment j: an empty partial, so the
     // combine can read all S partials without knowing the sequence
@@ -299,7 +291,14 @@ void pa_segment(SegmentArgs a) {
       const int d0 = U8 ? (c / 2) * 64 + q4 * 16 + (c % 2) * 8 : c * 32 + q4 * 8;
       const u32x4 v = ld16(qp + d0 * 2);
       qreg[c] = row_ok ? v : u32x4{0, 0, 0, 0};
-      if constexpr (U8) {
+    }
+  }
+  // u8: the row sum of q, taken once the first KV loads are in flight so
+  // the Q loads' latency hides behind theirs.
+  auto finish_q = [&]() {
+    if constexpr (U8) {
+#pragma unroll
+      for (int c = 0; c < QC; ++c) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           if constexpr (QT == kF16) {
@@ -310,12 +309,10 @@ void pa_segment(SegmentArgs a) {
           }
         }
       }
+      qsum += __shfl_xor(qsum, 16, kWave);
+      qsum += __shfl_xor(qsum, 32, kWave);
     }
-  }
-  if constexpr (U8) {
-    qsum += __shfl_xor(qsum, 16, kWave);
-    qsum += __shfl_xor(qsum, 32, kWave);
-  }
+  };
   __syncthreads();
 
   const char* kb = reinterpret_cast<const char*>(a.k);
@@ -449,25 +446,29 @@ void pa_segment(SegmentArgs a) {
     l_run += psum;
 
     if constexpr (U8) {
-      // (u - zp) * s folded: P' = p * s_v multiplies the (offset) codes, and
-      // sum(p * s_v * (zp_v + bias)) is subtracted from every d at the end
+      // (u - zp) * s folded: the codes (offset by the bias) are multiplied
+      // by P' = p * s_v, and sum(P' * (zp_v + bias)) is subtracted from every
+      // d at the end.  With f16 weights the sum uses P' as rounded for the
+      // MFMA, so the bias cancels exactly.
       float csum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t w = r.vs[e >> 2][e & 3];
-        const float sp = kvalid[e] ? p[e] * lo_f16(w) : 0.f;
-        csum += kvalid[e] ? sp * (hi_f16(w) + kU8Bias<QT>) : 0.f;
+        float sp = kvalid[e] ? p[e] * lo_f16(w) : 0.f;
+        if constexpr (QT == kF16) sp = (float)(_Float16)sp;
+        csum += kvalid[e] ? sp * (hi_f16(w) + kU8Bias<QT>) : 0.f;   // zp of a key outside may be NaN
         p[e] = sp;
       }
       c_run += csum;
     }
-    u32x2 ph[2], pl[2];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
-      split4<QT>(p[tau * 4 + 0], p[tau * 4 + 1], p[tau * 4 + 2], p[tau * 4 + 3], ph[tau], pl[tau]);
-    // PV.  The loaded V registers are never modified: in a boundary step the
-    // f16/bf16 V operand of a key outside [lo0, ctx) is cleared as it is
-    // consumed (u8 codes are finite; their P' is already 0).
+    u32x4 pb_hi, pb_lo;
+    pack_p<QT>(p, pb_hi, pb_lo);
+    // PV, O^T[d, r] += V^T[d, key] P^T[key, r] with one 16x16x32 product per
+    // 16-wide d tile: the A operand of lane (d, q4) is V of keys 4*q4 + 0..3
+    // of both sub-tiles, the k order of the weights above.  The loaded V
+    // registers are never modified: in a boundary step the f16/bf16 V of a
+    // key outside [lo0, ctx) is cleared as it is consumed (u8 codes are
+    // finite; their P' is already 0).
     auto pv = [&](auto masked) {
       u32x2 vmask[2];
       if constexpr (decltype(masked)::value) {
@@ -477,25 +478,27 @@ void pa_segment(SegmentArgs a) {
           vmask[tau][1] = (kvalid[tau * 4 + 2] ? 0x0000FFFFu : 0u) | (kvalid[tau * 4 + 3] ? 0xFFFF0000u : 0u);
         }
       }
-      auto vop = [&](int tau, int dt) {
-        u32x2 va;
-        if constexpr (U8) {
-          va = u8x4_to_16<QT>(r.v[tau][dt / 4][dt % 4]);
-        } else {
-          const u32x4 w = r.v[tau][dt / 2];
-          va = (dt % 2) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
-          if constexpr (decltype(masked)::value) va &= vmask[tau];
+      auto vop = [&](int dt) {
+        u32x2 va[2];
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+          if constexpr (U8) {
+            va[tau] = u8x4_to_16<QT>(r.v[tau][dt / 4][dt % 4]);
+          } else {
+            const u32x4 w = r.v[tau][dt / 2];
+            va[tau] = (dt % 2) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
+            if constexpr (decltype(masked)::value) va[tau] &= vmask[tau];
+          }
         }
-        return va;
+        return u32x4{va[0][0], va[0][1], va[1][0], va[1][1]};
       };
-      // all hi products of a sub-tile, then all lo: consecutive MFMAs never
-      // update the same accumulator
 #pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
+      for (int dt = 0; dt < DT; ++dt) o[dt] = mfma32<QT>(vop(dt), pb_hi, o[dt]);
+      if constexpr (QT == kBF16) {
+        // all hi products, then all lo: consecutive MFMAs never update the
+        // same accumulator
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt] = mfma16<QT>(vop(tau, dt), ph[tau], o[dt]);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt] = mfma16<QT>(vop(tau, dt), pl[tau], o[dt]);
+        for (int dt = 0; dt < DT; ++dt) o[dt] = mfma32<QT>(vop(dt), pb_lo, o[dt]);
       }
     };
     if (U8 || interior)
@@ -511,15 +514,22 @@ void pa_segment(SegmentArgs a) {
   // the memory system busy while this one computes.
   if constexpr (PF == 1) {
     Step ra;
-    for (int st = st_begin + wave; st < st_end; st += NW) {
+    int st = st_begin + wave;
+    if (st < st_end) {
       load_step(st, ra);
+      finish_q();
       compute_step(st, ra);
+      for (st += NW; st < st_end; st += NW) {
+        load_step(st, ra);
+        compute_step(st, ra);
+      }
     }
   } else {
     int st = st_begin + wave;
     if (st < st_end) {
       Step ra, rb;
       load_step(st, ra);
+      finish_q();
       while (true) {
         if (st + NW >= st_end) {
           compute_step(st, ra);

@@ -23,6 +23,9 @@ using pav::kWavesPerGroup;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Upper bound on segment-kernel workgroups per resident slot (see make_plan).
+constexpr int64_t kMaxRounds = 8;
+
 bool is_pow2_in(int v, int lo, int hi) {
   if (v < lo || v > hi) return false;
   return (v & (v - 1)) == 0;
@@ -50,6 +53,7 @@ int validate(const pa_verify_params* p, int32_t max_ctx, bool u8_entry) {
   // sizes that index 32-bit device arithmetic stay in range
   if ((int64_t)p->num_blocks * p->num_kv_heads * p->block_size > INT32_MAX) return PA_ERR_UNSUPPORTED;
   if ((int64_t)p->num_tokens * p->num_q_heads > INT32_MAX / 4) return PA_ERR_UNSUPPORTED;
+  if (p->num_seqs > 65535 || p->num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;   // grid y, x limits
   return PA_OK;
 }
 
@@ -62,27 +66,33 @@ int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_ve
     span = std::min<int64_t>(span, (int64_t)p->sliding_window + pav::kMaxT - 1 + kKeysPerStep - 1);
   }
   const int64_t n_steps = cdiv(span, kKeysPerStep);
+  // a segment's block ids must fit the kernel's LDS staging buffer
   const int64_t max_sps = ((int64_t)(pav::kMaxSegBlocks - 2) * bs) / kKeysPerStep;
-  int64_t sps;
+  int64_t S;
   if (p->num_segments > 0) {
-    sps = cdiv(n_steps, std::min<int64_t>(p->num_segments, n_steps));
+    S = p->num_segments;
   } else {
-    // enough workgroups to fill every CU at the occupancy the kernels are
-    // built for, with an equal number of steps per wavefront
+    // Enough segments that one sequence of max_context_len keys alone
+    // covers every resident workgroup slot of the GPU (every CU busy at
+    // batch 1, and in a ragged batch the longest sequence is not left to a
+    // few CUs), but at most kMaxRounds rounds of workgroups in all.
     const int64_t groups = (int64_t)num_cus * pav::groups_per_cu(p->kv_dtype, p->head_dim);
-    const int64_t s0 = std::max<int64_t>(1, cdiv(groups, (int64_t)p->num_kv_heads * p->num_seqs));
-    sps = cdiv(n_steps, s0 * kWavesPerGroup) * kWavesPerGroup;
+    const int64_t pairs = (int64_t)p->num_kv_heads * p->num_seqs;
+    S = cdiv(groups, p->num_kv_heads);
+    S = std::min(S, std::max<int64_t>(cdiv(groups, pairs), kMaxRounds * groups / pairs));
   }
-  sps = std::max<int64_t>(1, std::min(sps, max_sps));
-  const int64_t S = cdiv(n_steps, sps);
+  S = std::max<int64_t>(std::min(S, n_steps), cdiv(n_steps, max_sps));
+  if (S > 65535) return PA_ERR_UNSUPPORTED;           // grid z limit
+  const int64_t sps = cdiv(n_steps, S);               // longest segment; the others are >= sps - 1
   pl->num_segments = (int32_t)S;
   pl->steps_per_segment = (int32_t)sps;
+  pl->num_steps = (int32_t)n_steps;
   pl->keys_per_step = kKeysPerStep;
   pl->span = (int32_t)span;
   pl->waves_per_group = kWavesPerGroup;
-  pl->grid[0] = (int32_t)S;
-  pl->grid[1] = p->num_kv_heads;
-  pl->grid[2] = p->num_seqs;
+  pl->grid[0] = p->num_kv_heads;
+  pl->grid[1] = p->num_seqs;
+  pl->grid[2] = (int32_t)S;
   pl->block_threads = kWavesPerGroup * 64;
   const int64_t rows = (int64_t)p->num_tokens * p->num_q_heads;
   pl->combine_grid[0] = (int32_t)rows;
@@ -92,7 +102,6 @@ int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_ve
   const size_t ml_bytes = (size_t)rows * S * 2 * sizeof(float);
   const size_t o_bytes = (size_t)rows * S * p->head_dim * sizeof(float);
   pl->workspace_bytes = 256 + ((ml_bytes + 255) / 256) * 256 + o_bytes;
-  (void)num_cus;
   return PA_OK;
 }
 
@@ -179,6 +188,7 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
   a.max_ctx = max_ctx;
   a.S = pl.num_segments;
   a.steps_per_seg = pl.steps_per_segment;
+  a.n_steps = pl.num_steps;
   a.scale_log2 = scale * 1.4426950408889634f;
 
   hipStream_t st = static_cast<hipStream_t>(p->stream);

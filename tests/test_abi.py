@@ -135,9 +135,14 @@ def check_plan_covers(pl, max_ctx, window=0, nseq=1, hkv=8, bs=16):
     span = max_ctx if not window else min(max_ctx, window + 3 + 31)
     assert pl["span"] == span
     steps = -(-span // pl["keys_per_step"])
-    assert pl["num_segments"] * pl["steps_per_segment"] >= steps
-    assert (pl["num_segments"] - 1) * pl["steps_per_segment"] < steps      # no empty tail segment
-    assert pl["grid"] == [pl["num_segments"], hkv, nseq]
+    S = pl["num_segments"]
+    assert pl["num_steps"] == steps and 1 <= S <= steps
+    # segment j covers [j*N/S, (j+1)*N/S): a partition of the steps into
+    # non-empty segments whose lengths differ by at most one
+    lens = [(j + 1) * steps // S - j * steps // S for j in range(S)]
+    assert sum(lens) == steps and min(lens) >= 1 and max(lens) - min(lens) <= 1
+    assert pl["steps_per_segment"] == max(lens)
+    assert pl["grid"] == [hkv, nseq, S]
     assert pl["steps_per_segment"] * pl["keys_per_step"] // bs + 2 <= 1040
 
 
@@ -146,13 +151,25 @@ def test_plan_fills_the_gpu_at_batch_one(L, T):
     pl = plan(L + T, num_tokens=T)
     check_plan_covers(pl, L + T)
     wgs = pl["grid"][0] * pl["grid"][1] * pl["grid"][2]
-    # f16 D=128 segment workgroups run one per CU: the grid stays within one
-    # round of resident workgroups (no tail round) and still covers most CUs
-    assert 128 <= wgs <= 256
-    assert pl["steps_per_segment"] % pl["waves_per_group"] == 0   # equal steps per wavefront
+    # f16 D=128 segment workgroups run one per CU: one workgroup for every CU,
+    # and no second round of workgroups
+    assert wgs == 256
     rows = T * 32
     assert pl["workspace_bytes"] == 256 + -(-rows * pl["num_segments"] * 8 // 256) * 256 + \
         rows * pl["num_segments"] * 128 * 4
+
+
+def test_plan_ragged_batch_gives_the_longest_sequence_the_gpu():
+    # 8 sequences up to 32k: every sequence is cut into enough segments that
+    # the longest one alone covers the 256 workgroup slots
+    pl = plan(32235, num_seqs=8, num_tokens=22, max_blocks_per_seq=2015, num_blocks=6000)
+    check_plan_covers(pl, 32235, nseq=8)
+    assert pl["num_segments"] == 32
+    # a large batch is capped at 8 rounds of workgroups
+    pl = plan(32771, num_seqs=64, num_tokens=64 * 3, max_blocks_per_seq=2049, num_blocks=64 * 2049)
+    check_plan_covers(pl, 32771, nseq=64)
+    assert pl["num_segments"] == 4
+    assert pl["grid"][0] * pl["grid"][1] * pl["grid"][2] <= 8 * 256
 
 
 def test_plan_window_and_forced_segments():
