@@ -174,9 +174,31 @@ def _check(t, name, dtype=None, ndim=None, device=None):
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
 
 
+class PreparedCall:
+    """One forward call with its arguments checked and marshalled once.
+    Calling it enqueues the call again with the same pointers and sizes;
+    only the stream and the profiling events may change.  The tensors it was
+    prepared from must stay alive and unmoved."""
+
+    def __init__(self, fn, args, params, out, keep):
+        self._fn, self._args, self._params, self.out = fn, args, params, out
+        self._pref = ctypes.byref(params)
+        self._keep = keep
+
+    def __call__(self, stream: Optional[int] = None, prof_events=None):
+        p = self._params
+        if stream is not None:
+            p.stream = stream or None
+        p.prof_event_begin, p.prof_event_end = prof_events if prof_events else (None, None)
+        rc = self._fn(*self._args, self._pref)
+        if rc != PA_OK:
+            raise PaVerifyError(rc)
+        return self.out
+
+
 def _call(u8, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
           subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
-          ws, stream, prof_events):
+          ws, stream, prof_events, prepare=False):
     torch = _torch()
     dev = q.device
     _check(q, "q", ndim=3, device=dev)
@@ -230,16 +252,20 @@ def _call(u8, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_le
         params.prof_event_end = prof_events[1]
     L = lib()
     if u8:
-        rc = L.pa_verify_forward_u8(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                    k_scale_zp.data_ptr(), v_scale_zp.data_ptr(),
-                                    block_tables.data_ptr(), past_lens.data_ptr(),
-                                    subsequence_begins.data_ptr(), int(max_context_len),
-                                    float(scale), out.data_ptr(), ctypes.byref(params))
+        fn = L.pa_verify_forward_u8
+        args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), k_scale_zp.data_ptr(),
+                v_scale_zp.data_ptr(), block_tables.data_ptr(), past_lens.data_ptr(),
+                subsequence_begins.data_ptr(), int(max_context_len), float(scale), out.data_ptr())
     else:
-        rc = L.pa_verify_forward(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                 block_tables.data_ptr(), past_lens.data_ptr(),
-                                 subsequence_begins.data_ptr(), int(max_context_len),
-                                 float(scale), out.data_ptr(), ctypes.byref(params))
+        fn = L.pa_verify_forward
+        args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+                past_lens.data_ptr(), subsequence_begins.data_ptr(), int(max_context_len),
+                float(scale), out.data_ptr())
+    if prepare:
+        keep = (q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
+                subsequence_begins, out, ws)
+        return PreparedCall(fn, args, params, out, keep)
+    rc = fn(*args, ctypes.byref(params))
     if rc != PA_OK:
         raise PaVerifyError(rc)
     return out
@@ -288,3 +314,23 @@ def pa_verify_read_status(device=None) -> int:
     if rc != PA_OK:
         raise PaVerifyError(rc)
     return int(st.value)
+
+
+def prepare_forward(q, k_cache, v_cache, block_tables, past_lens, subsequence_begins,
+                    max_context_len: int, scale: float, out=None, *, sliding_window: int = 0,
+                    num_segments: int = 0, workspace=None, stream: Optional[int] = None):
+    """pa_verify_forward's checks and marshalling done once: returns a
+    PreparedCall that enqueues the same call each time it is called."""
+    return _call(False, q, k_cache, v_cache, None, None, block_tables, past_lens,
+                 subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
+                 workspace, stream, None, prepare=True)
+
+
+def prepare_forward_u8(q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
+                       subsequence_begins, max_context_len: int, scale: float, out=None, *,
+                       sliding_window: int = 0, num_segments: int = 0, workspace=None,
+                       stream: Optional[int] = None):
+    """pa_verify_forward_u8's checks and marshalling done once (see prepare_forward)."""
+    return _call(True, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
+                 subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
+                 workspace, stream, None, prepare=True)

@@ -250,3 +250,30 @@ def test_graph_capture_replays_match_eager():
         for e, o in zip(eager, outs):
             assert np.array_equal(e, to_f64(o)), rep
     assert pav.pa_verify_read_status() == pav.PA_OK
+
+
+def test_prepared_call_matches_the_plain_call():
+    """A call marshalled once and enqueued repeatedly (on another stream
+    too) gives the plain call's output bit for bit."""
+    import torch
+    import speculative_decoding_verify_paged_amd as pav
+    from gpu_util import to_device
+    for case in (pi.config2(8192, 3), pi.config3(2048, 2)):
+        dev = to_device(case)
+        want = to_f64(run_gpu(case, dev))
+        out = torch.empty_like(dev["q"])
+        if case.kv_dtype == pi.U8:
+            pc = pav.prepare_forward_u8(dev["q"], dev["k_cache"], dev["v_cache"], dev["k_scale_zp"],
+                                        dev["v_scale_zp"], dev["block_tables"], dev["past_lens"],
+                                        dev["subsequence_begins"], case.max_context_len, case.scale, out)
+        else:
+            pc = pav.prepare_forward(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                                     dev["past_lens"], dev["subsequence_begins"], case.max_context_len,
+                                     case.scale, out)
+        side = torch.cuda.Stream()
+        for st in (None, side.cuda_stream, None):
+            out.fill_(float("nan"))
+            torch.cuda.synchronize()
+            pc(stream=st)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_f64(out), want), case.name
