@@ -41,7 +41,8 @@ class _Args(ctypes.Structure):
         ("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
         ("k_scale_zp", ctypes.c_void_p), ("v_scale_zp", ctypes.c_void_p),
         ("block_tables", ctypes.c_void_p), ("past_lens", ctypes.c_void_p),
-        ("subsequence_begins", ctypes.c_void_p), ("pairs", ctypes.c_void_p),
+        ("subsequence_begins", ctypes.c_void_p), ("tree_mask", ctypes.c_void_p),
+        ("pairs", ctypes.c_void_p),
         ("num_pairs", ctypes.c_int64), ("num_threads", ctypes.c_int32),
     ]
 
@@ -72,7 +73,8 @@ class Oracle:
     def run(self, *, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, block_size,
             num_blocks, max_blocks_per_seq, sliding_window, max_context_len, q_dtype, kv_dtype,
             scale, q, k_cache, v_cache, block_tables, past_lens, subsequence_begins,
-            k_scale_zp=None, v_scale_zp=None, pairs=None, threads=0, **_ignored):
+            k_scale_zp=None, v_scale_zp=None, tree_mask=None, pairs=None, threads=0,
+            **_ignored):
         """Return (status, out).  out is fp64 [num_tokens, Hq, D] or [len(pairs), D]."""
         keep = []
 
@@ -89,7 +91,7 @@ class Oracle:
                   q_dtype, kv_dtype, float(scale),
                   ptr(q), ptr(k_cache), ptr(v_cache), ptr(k_scale_zp), ptr(v_scale_zp),
                   ptr(block_tables, np.int32), ptr(past_lens, np.int32),
-                  ptr(subsequence_begins, np.int32), ptr(pairs_arr),
+                  ptr(subsequence_begins, np.int32), ptr(tree_mask, np.uint32), ptr(pairs_arr),
                   0 if pairs_arr is None else pairs_arr.shape[0], int(threads))
         rows = num_tokens * num_q_heads if pairs_arr is None else pairs_arr.shape[0]
         out = np.full((rows, head_dim), np.nan, dtype=np.float64)
@@ -118,7 +120,8 @@ def case_fields(case) -> dict:
                 kv_dtype=case.kv_dtype, scale=case.scale, q=case.q, k_cache=case.k_cache,
                 v_cache=case.v_cache, k_scale_zp=case.k_scale_zp, v_scale_zp=case.v_scale_zp,
                 block_tables=case.block_tables, past_lens=case.past_lens,
-                subsequence_begins=case.subsequence_begins)
+                subsequence_begins=case.subsequence_begins,
+                tree_mask=getattr(case, "tree_mask", None))
 
 
 _default: Optional[Oracle] = None

@@ -20,6 +20,13 @@
  *    "Observation 3".  Reading: W counts the token itself.
  *  - Grouped-query attention: q head h reads KV head h / (Hq / Hkv).  The
  *    pages only name "GQA read-once"; consecutive grouping is the reading.
+ *  - Tree verify (optional): the new tokens of a sequence form a tree of
+ *    drafts and row i sees the cached past plus the new tokens its mask
+ *    names — its ancestors — instead of all earlier ones: OpenVINO #38153
+ *    "Performance issue description" (the neighbouring tree-mask verify case)
+ *    and "The 140x Performance Gap" (a tree of draft tokens verified in one
+ *    pass).  Reading: bit j of row i's mask admits new token j; bit i (the
+ *    token itself) is always admitted; no sliding window with a tree.
  *  - Softmax is taken over scale * q.k, two passes (max, then exp-sum), no
  *    segmentation, no online rescaling: the segmented GPU reduction must
  *    reach the same value up to rounding order (vLLM article "speculative
@@ -118,6 +125,7 @@ static int check_args(const pa_oracle_args* a) {
       !a->subsequence_begins)
     return PA_ORACLE_ERR_ARG;
   if (a->kv_dtype == PA_ORACLE_U8 && (!a->k_scale_zp || !a->v_scale_zp)) return PA_ORACLE_ERR_ARG;
+  if (a->tree_mask && a->sliding_window > 0) return PA_ORACLE_ERR_ARG;
   if (a->subsequence_begins[0] != 0 || a->subsequence_begins[a->num_seqs] != a->num_tokens)
     return PA_ORACLE_ERR_META;
   for (int s = 0; s < a->num_seqs; ++s) {
@@ -136,17 +144,31 @@ static int check_args(const pa_oracle_args* a) {
   return PA_ORACLE_OK;
 }
 
+/* Does query token i (of a sequence with past_len L and T new tokens) see
+ * cache position t?  Causal rows: t in [lo, L + i + 1).  Tree rows: every
+ * past position, and new token j = t - L when bit j of the row's mask is set
+ * or j == i. */
+static int visible(const pa_oracle_args* a, int n, int i, int L, int T, int lo, int t) {
+  if (t < lo) return 0;
+  if (!a->tree_mask) return t < L + i + 1;
+  if (t < L) return 1;
+  const int j = t - L;
+  if (j >= T) return 0;
+  return j == i || ((a->tree_mask[n] >> j) & 1u);
+}
+
 /* out[row][:] for query token n, q head h: the definition, two-pass softmax. */
 static void attend_one(const pa_oracle_args* a, int n, int h, double* z, double* out_row) {
   const int D = a->head_dim, bs = a->block_size, Hq = a->num_q_heads, Hkv = a->num_kv_heads;
   int s = 0;
   while (!(a->subsequence_begins[s] <= n && n < a->subsequence_begins[s + 1])) ++s;
   const int i = n - a->subsequence_begins[s];      /* index of the token inside its sequence */
+  const int T = a->subsequence_begins[s + 1] - a->subsequence_begins[s];
   const int L = a->past_lens[s];
-  const int hi = L + i + 1;                         /* keys [lo, hi) */
+  const int hi = a->tree_mask ? L + T : L + i + 1;  /* candidate keys [lo, hi) */
   int lo = 0;
   if (a->sliding_window > 0) {
-    lo = hi - a->sliding_window;
+    lo = L + i + 1 - a->sliding_window;
     if (lo < 0) lo = 0;
   }
   const int g = h / (Hq / Hkv);                     /* KV head serving q head h */
@@ -158,6 +180,7 @@ static void attend_one(const pa_oracle_args* a, int n, int h, double* z, double*
   /* pass 1: logits and their max */
   double m = -INFINITY;
   for (int t = lo; t < hi; ++t) {
+    if (!visible(a, n, i, L, T, lo, t)) continue;
     const size_t blk = (size_t)table[t / bs];
     const int slot = t % bs;
     const size_t row = (blk * Hkv + g) * bs + slot; /* index of (blk, g, slot) */
@@ -173,6 +196,7 @@ static void attend_one(const pa_oracle_args* a, int n, int h, double* z, double*
   double Z = 0.0;
   for (int d = 0; d < D; ++d) out_row[d] = 0.0;
   for (int t = lo; t < hi; ++t) {
+    if (!visible(a, n, i, L, T, lo, t)) continue;
     const double w = exp(z[t - lo] - m);
     Z += w;
     const size_t blk = (size_t)table[t / bs];

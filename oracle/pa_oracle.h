@@ -23,6 +23,9 @@ typedef struct pa_oracle_args {
   const int32_t* block_tables;        /* [num_seqs][max_blocks_per_seq] */
   const int32_t* past_lens;           /* [num_seqs] */
   const int32_t* subsequence_begins;  /* [num_seqs + 1] */
+  const uint32_t* tree_mask;          /* optional [num_tokens]: bit j of token b0 + i lets row
+                                         i see new token j of its sequence (bit i implied);
+                                         NULL = causal rows; needs sliding_window == 0 */
   const int32_t* pairs;               /* optional [num_pairs][2] (token, q head) subset */
   int64_t num_pairs;
   int32_t num_threads;                /* 0 = all online host cores */

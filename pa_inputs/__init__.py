@@ -193,6 +193,7 @@ class Case:
     block_tables: np.ndarray      # int32 [num_seqs, max_blocks_per_seq]
     past_lens: np.ndarray         # int32 [num_seqs]
     subsequence_begins: np.ndarray  # int32 [num_seqs + 1]
+    tree_mask: Optional[np.ndarray] = None  # uint32 [num_tokens] (tree verify), None = causal
 
     @property
     def Ts(self) -> List[int]:
@@ -273,14 +274,38 @@ def _store_pool(x, kv_dtype):
     return f32_to_bits(x, kv_dtype), None
 
 
+def tree_masks(parents: Sequence[Sequence[int]]) -> np.ndarray:
+    """The ABI's tree-mask words for draft trees given by parent indices:
+    parents[s][j] is the parent of new token j of sequence s (-1: a root,
+    attached to the cached past; otherwise an earlier token of the same
+    sequence).  Word of token j: bit j plus its parent's word."""
+    out = []
+    for par in parents:
+        words = []
+        for j, p in enumerate(par):
+            assert -1 <= p < j
+            words.append((1 << j) | (words[p] if p >= 0 else 0))
+        out.extend(words)
+    return np.asarray(out, dtype=np.uint32)
+
+
+def random_parents(rng: np.random.Generator, T: int) -> List[int]:
+    """A random draft tree over T new tokens: token 0 is a root, token j > 0
+    hangs under a uniformly drawn earlier token or, with probability 1/(j+1),
+    starts another root."""
+    return [-1] + [int(rng.integers(-1, j)) for j in range(1, T)]
+
+
 def build_case(seed: Sequence[int], past_lens: Sequence[int], Ts: Sequence[int], *,
                num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
                q_dtype: int = F16, kv_dtype: int = F16, sliding_window: int = 0,
                spare_blocks: int = 0, poison: bool = False,
                scale: Optional[float] = None, max_blocks_per_seq: Optional[int] = None,
                max_context_len: Optional[int] = None, name: str = "case",
-               rng: Optional[np.random.Generator] = None) -> Case:
-    """Build one call's inputs following the module recipe."""
+               rng: Optional[np.random.Generator] = None, tree: bool = False) -> Case:
+    """Build one call's inputs following the module recipe.  tree=True adds
+    a random draft tree per sequence (drawn after everything else, so the
+    other arrays are those of the same case without a tree)."""
     if rng is None:
         rng = np.random.default_rng(list(seed))
     past_lens = [int(x) for x in past_lens]
@@ -323,6 +348,7 @@ def build_case(seed: Sequence[int], past_lens: Sequence[int], Ts: Sequence[int],
     del k_log
     v_cache = tile_v(v_log, u8).reshape(v_log.shape)
     del v_log
+    tm = tree_masks([random_parents(rng, T) for T in Ts]) if tree else None
 
     return Case(name=name, num_seqs=num_seqs, num_tokens=num_tokens,
                 num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
@@ -331,7 +357,8 @@ def build_case(seed: Sequence[int], past_lens: Sequence[int], Ts: Sequence[int],
                 scale=float(scale if scale is not None else 1.0 / math.sqrt(head_dim)),
                 max_context_len=int(max_context_len), q=q, k_cache=k_cache, v_cache=v_cache,
                 k_scale_zp=k_sz, v_scale_zp=v_sz, block_tables=bt,
-                past_lens=np.asarray(past_lens, dtype=np.int32), subsequence_begins=sb)
+                past_lens=np.asarray(past_lens, dtype=np.int32), subsequence_begins=sb,
+                tree_mask=tm)
 
 
 def _poison(k, v, ksz, vsz, kv_dtype, bt, past_lens, Ts, bs, W, spare):

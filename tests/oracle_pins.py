@@ -22,6 +22,11 @@ What pins what:
   * gqa         — G > 1 equals G = 1 with each KV head duplicated.
   * u8          — the u8 path equals the fp64 path fed the dequantised values.
   * ragged      — a ragged batch equals each sequence run alone.
+  * tree        — tree verify against torch SDPA with a dense mask built by
+                  walking each draft tree's parent pointers; the chain tree
+                  equals the causal rows bitwise; a mask without the row's own
+                  bit changes nothing; causal rows with up to 16 new tokens
+                  against SDPA.
 """
 from __future__ import annotations
 
@@ -80,8 +85,10 @@ def run_ok(orc, **f):
     return out
 
 
-def sdpa_reference(case):
-    """torch SDPA (fp64, CPU) per sequence, mask from the key-limit rule."""
+def sdpa_reference(case, parents=None):
+    """torch SDPA (fp64, CPU) per sequence, mask from the key-limit rule, or,
+    given parents[s][j] (draft-tree parent of new token j, -1 for a root),
+    from each row's ancestors found by walking the parent pointers."""
     import torch
     import torch.nn.functional as F
     G = case.num_q_heads // case.num_kv_heads
@@ -100,6 +107,13 @@ def sdpa_reference(case):
         qs = qf[sb[s]:sb[s + 1]].transpose(1, 0, 2)        # [Hq, T, D]
         mask = np.zeros((T, L + T), dtype=bool)
         for i in range(T):
+            if parents is not None:
+                mask[i, :L] = True
+                j = i
+                while j >= 0:
+                    mask[i, L + j] = True
+                    j = parents[s][j]
+                continue
             hi = L + i + 1
             lo = max(0, hi - case.sliding_window) if case.sliding_window > 0 else 0
             mask[i, lo:hi] = True
@@ -341,8 +355,38 @@ def pin_ragged(orc):
             assert np.array_equal(one, full[sb[s]:sb[s + 1]]), (case.name, s)
 
 
+def pin_tree(orc):
+    rng = np.random.default_rng(17)
+    for c in range(24):
+        G = int(rng.choice([1, 2, 4]))
+        Hkv = int(rng.choice([1, 2]))
+        kv = int(rng.choice([pi.F16, pi.BF16, pi.U8]))
+        D = 64 if kv == pi.U8 else int(rng.choice([32, 64]))
+        num_seqs = int(rng.choice([1, 1, 2]))
+        Ls = rng.integers(0, 200, size=num_seqs).tolist()
+        Ts = rng.integers(1, 17, size=num_seqs).tolist()
+        case = pi.build_case([400, c], Ls, Ts, num_q_heads=G * Hkv, num_kv_heads=Hkv,
+                             head_dim=D, block_size=int(rng.choice([16, 32])),
+                             q_dtype=pi.BF16 if kv == pi.BF16 else pi.F16, kv_dtype=kv,
+                             spare_blocks=1, poison=True, name=f"tree{c}")
+        causal = orc.forward(case)
+        err = np.max(np.abs(causal - sdpa_reference(case)))
+        assert err <= 1e-12, f"{case.name} causal: max err {err}"
+        parents = [pi.random_parents(rng, T) for T in Ts]
+        words = pi.tree_masks(parents)
+        got = orc.forward(case, tree_mask=words)
+        err = np.max(np.abs(got - sdpa_reference(case, parents)))
+        assert np.all(np.isfinite(got)) and err <= 1e-12, f"{case.name}: max err {err}"
+        # the row's own bit is implied
+        own = np.concatenate([1 << np.arange(T, dtype=np.uint32) for T in Ts])
+        assert np.array_equal(orc.forward(case, tree_mask=words & ~own), got), case.name
+        # a chain of drafts is the causal case
+        chain = pi.tree_masks([list(range(-1, T - 1)) for T in Ts])
+        assert np.array_equal(orc.forward(case, tree_mask=chain), causal), case.name
+
+
 ALL_PINS = {
     "sdpa": pin_sdpa, "hand": pin_hand, "closed": pin_closed, "rows": pin_rows,
     "permutation": pin_permutation, "window": pin_window, "gqa": pin_gqa, "u8": pin_u8,
-    "ragged": pin_ragged,
+    "ragged": pin_ragged, "tree": pin_tree,
 }

@@ -13,11 +13,19 @@ from oracle_pins import ALL_PINS
 
 # (name, [(text in pa_oracle.c, replacement), ...])
 MUTANTS = [
-    ("key_limit_off_by_one", [("const int hi = L + i + 1;", "const int hi = L + i;")]),
+    ("key_limit_off_by_one", [("if (!a->tree_mask) return t < L + i + 1;",
+                               "if (!a->tree_mask) return t < L + i;")]),
     ("row_index_dropped", [("const int i = n - a->subsequence_begins[s];", "const int i = 0;")]),
     ("gqa_modulo_mapping", [("const int g = h / (Hq / Hkv);", "const int g = h % Hkv;")]),
     ("scale_dropped", [("z[t - lo] = a->scale * dot;", "z[t - lo] = dot;")]),
-    ("window_one_short", [("lo = hi - a->sliding_window;", "lo = hi - a->sliding_window + 1;")]),
+    ("window_one_short", [("lo = L + i + 1 - a->sliding_window;", "lo = L + i + 2 - a->sliding_window;")]),
+    ("tree_bit_shifted", [("return j == i || ((a->tree_mask[n] >> j) & 1u);",
+                           "return j == i || ((a->tree_mask[n] >> (j + 1)) & 1u);")]),
+    ("tree_self_not_implied", [("return j == i || ((a->tree_mask[n] >> j) & 1u);",
+                                "return ((a->tree_mask[n] >> j) & 1u);")]),
+    ("tree_hides_the_past", [("if (t < L) return 1;", "if (t < L) return 0;")]),
+    ("tree_first_row_mask", [("return j == i || ((a->tree_mask[n] >> j) & 1u);",
+                              "return j == i || ((a->tree_mask[n - i] >> j) & 1u);")]),
     ("v_read_in_k_layout", [("const size_t vidx = page + v_offset(slot, d, D, u8);",
                              "const size_t vidx = page + k_offset(slot, d, D, u8);")]),
     ("k_page_row_major", [("page + k_offset(slot, d, D, u8), row);",
@@ -44,7 +52,7 @@ MUTANTS = [
                           "page + k_offset(slot, D - 1 - d, D, u8), row);")]),
 ]
 
-PIN_ORDER = ["hand", "closed", "rows", "window", "gqa", "u8", "permutation", "ragged", "sdpa"]
+PIN_ORDER = ["hand", "closed", "rows", "window", "gqa", "u8", "permutation", "ragged", "sdpa", "tree"]
 
 
 def _source():
