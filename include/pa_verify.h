@@ -4,7 +4,7 @@
  *
  * What the operation computes.  A batch holds num_seqs sequences.  Sequence s
  * brings T_s = subsequence_begins[s+1] - subsequence_begins[s] new query
- * tokens (1 <= T_s <= 4) on top of past_len L_s = past_lens[s] cached tokens.
+ * tokens (1 <= T_s <= 16) on top of past_len L_s = past_lens[s] cached tokens.
  * The paged KV cache already holds all L_s + T_s tokens of the sequence.  New
  * token i (0-based within its sequence) attends to cache positions
  * [lo_i, L_s + i + 1), with lo_i = 0 for a full-causal layer and
@@ -14,6 +14,9 @@
  *     out[n, h, :] = sum_t softmax_t(scale * <q[n, h, :], k_t>) * v_t
  *
  * over those positions, where KV head floor(h / (Hq / Hkv)) serves q head h.
+ * Tree verify (params->tree_mask) replaces the causal rule among the new
+ * tokens: row i sees every past position and the new tokens its mask word
+ * names (its ancestors in the draft tree) plus itself.
  *
  * Sources (cited by page title and section):
  *  - The per-token key limit past_len + i + 1, the op metadata (past_lens,
@@ -29,6 +32,10 @@
  *  - The sliding window of 1024 and page size 64 of the SWA-hybrid model:
  *    SGLang discussion #36314 "FROZEN_KV_MTP slower than no-spec on Gemma 4
  *    (SWA hybrid)", sections "Environment" and "Observation 3".
+ *  - Tree-mask verify with up to 9-16 draft tokens as the neighbouring case:
+ *    OpenVINO issue #38153, "Performance issue description" (#34644), and
+ *    "The 140x Performance Gap" (magik.net), section "The Real Discovery"
+ *    (a draft tree of 9 queries verified in one pass).
  *  - Graph replay must stay intact (no allocation, no host sync in a call):
  *    the same vLLM article, torch-profiler trace passage (hipGraphLaunch).
  *
@@ -60,7 +67,7 @@
  *
  * Errors.  Host-checkable problems return a nonzero pa_status before anything
  * is enqueued and leave `out` untouched.  Problems that only the device can see
- * (T_s outside [1,4], L_s < 0, L_s + T_s > max_context_len, a physical block id
+ * (T_s outside [1, max_query_len], L_s < 0, L_s + T_s > max_context_len, a physical block id
  * outside [0, num_blocks), non-monotone subsequence_begins) set the sticky
  * device status word PA_ERR_DEVICE_CONTRACT in the workspace and make the
  * affected sequence's output rows NaN; pa_verify_read_status reports it.
@@ -91,9 +98,11 @@ typedef enum pa_dtype {
 } pa_dtype;
 
 /* Sizes and options of one call.  Supported: head_dim in {64, 128, 256},
- * block_size in {16, 32, 64}, group size Hq/Hkv in {1, 2, 4, 8} with
- * group * max T_s <= 16 enforced per sequence on the device, dtype pairs
- * (q, kv) = (f16, f16), (bf16, bf16), (f16, u8), (bf16, u8). */
+ * block_size in {16, 32, 64}, group size G = Hq/Hkv in {1, 2, 4, 8}, dtype
+ * pairs (q, kv) = (f16, f16), (bf16, bf16), (f16, u8), (bf16, u8), and up to
+ * 16 new tokens per sequence with G * max_query_len <= 64 stacked rows
+ * (<= 32 for head_dim 256); T_s <= max_query_len is checked per sequence on
+ * the device. */
 typedef struct pa_verify_params {
   int32_t num_seqs;            /* sequences in the batch, 1 ..= 65535 */
   int32_t num_tokens;          /* == subsequence_begins[num_seqs], >= num_seqs */
@@ -107,6 +116,9 @@ typedef struct pa_verify_params {
   int32_t num_segments;        /* 0 = planner decides; > 0 forces the segment count (clamped) */
   int32_t q_dtype;             /* pa_dtype of q and out: PA_F16 or PA_BF16 */
   int32_t kv_dtype;            /* pa_dtype of the caches: q_dtype, or PA_U8 (u8 entry point) */
+  int32_t max_query_len;       /* bound on T_s, 1..16; 0 = min(4, num_tokens - num_seqs + 1).
+                                  Sizes the kernel's row blocks (G * bound rows, in blocks
+                                  of 16), so pass the real bound (the draft length) */
   void* workspace;             /* device scratch >= pa_verify_workspace_bytes; its first 4 bytes
                                   are the sticky device status word: zero them once at allocation */
   size_t workspace_bytes;
@@ -115,6 +127,12 @@ typedef struct pa_verify_params {
   void* prof_event_end;        /* optional hipEvent_t stamped when the segment kernel ends; both
                                   are set by the kernel's own dispatch (hipExtLaunchKernel),
                                   so their elapsed time is the kernel's duration */
+  const void* tree_mask;       /* optional device uint32 [num_tokens]: tree verify.  Bit j of
+                                  the word of token b_s + i lets that row see new token j of
+                                  sequence s (cache position L_s + j) instead of the causal
+                                  rule; the row's own bit is implied, bits >= T_s are ignored,
+                                  every past position stays visible.  NULL = causal rows.
+                                  Requires sliding_window == 0 (else PA_ERR_UNSUPPORTED) */
 } pa_verify_params;
 
 /* The launch plan, a pure function of host scalars: segment count S, keys per
@@ -125,6 +143,7 @@ typedef struct pa_verify_plan {
   int32_t steps_per_segment;   /* steps of keys_per_step keys in the longest segment; segment j
                                   covers steps [j*N/S, (j+1)*N/S) of num_steps = N */
   int32_t num_steps;           /* N: steps covering span */
+  int32_t row_blocks;          /* 16-row blocks of stacked query rows the kernel is built with */
   int32_t keys_per_step;       /* keys one wavefront consumes per loop iteration */
   int32_t span;                /* bound on keys any one sequence's rows touch */
   int32_t waves_per_group;     /* wavefronts per segment workgroup */

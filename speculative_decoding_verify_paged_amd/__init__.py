@@ -39,16 +39,18 @@ class PaVerifyParams(ctypes.Structure):
         ("num_blocks", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
         ("sliding_window", ctypes.c_int32), ("num_segments", ctypes.c_int32),
         ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+        ("max_query_len", ctypes.c_int32),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
         ("prof_event_begin", ctypes.c_void_p), ("prof_event_end", ctypes.c_void_p),
+        ("tree_mask", ctypes.c_void_p),
     ]
 
 
 class PaVerifyPlan(ctypes.Structure):
     _fields_ = [
         ("num_segments", ctypes.c_int32), ("steps_per_segment", ctypes.c_int32),
-        ("num_steps", ctypes.c_int32),
+        ("num_steps", ctypes.c_int32), ("row_blocks", ctypes.c_int32),
         ("keys_per_step", ctypes.c_int32), ("span", ctypes.c_int32),
         ("waves_per_group", ctypes.c_int32), ("grid", ctypes.c_int32 * 3),
         ("block_threads", ctypes.c_int32), ("combine_grid", ctypes.c_int32 * 3),
@@ -104,12 +106,13 @@ def pa_verify_status_string(code: int) -> str:
 
 def make_params(*, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, block_size,
                 num_blocks, max_blocks_per_seq, q_dtype, kv_dtype, sliding_window=0,
-                num_segments=0, workspace=0, workspace_bytes=0, stream=0,
-                prof_event_begin=0, prof_event_end=0) -> PaVerifyParams:
+                num_segments=0, max_query_len=0, workspace=0, workspace_bytes=0, stream=0,
+                prof_event_begin=0, prof_event_end=0, tree_mask=0) -> PaVerifyParams:
     return PaVerifyParams(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, block_size,
                           num_blocks, max_blocks_per_seq, sliding_window, num_segments,
-                          q_dtype, kv_dtype, workspace or None, workspace_bytes, stream or None,
-                          prof_event_begin or None, prof_event_end or None)
+                          q_dtype, kv_dtype, max_query_len, workspace or None, workspace_bytes,
+                          stream or None, prof_event_begin or None, prof_event_end or None,
+                          tree_mask or None)
 
 
 def pa_verify_make_plan(params: PaVerifyParams, max_context_len: int, num_cus: int) -> dict:
@@ -198,7 +201,7 @@ class PreparedCall:
 
 def _call(u8, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
           subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
-          ws, stream, prof_events, prepare=False):
+          ws, stream, prof_events, prepare=False, max_query_len=0, tree_mask=None):
     torch = _torch()
     dev = q.device
     _check(q, "q", ndim=3, device=dev)
@@ -230,11 +233,16 @@ def _call(u8, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_le
         _check(out, "out", dtype=q.dtype, device=dev)
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
+    if tree_mask is not None:
+        _check(tree_mask, "tree_mask", ndim=1, device=dev)
+        if tree_mask.dtype not in (torch.int32, torch.uint32) or tree_mask.shape[0] != num_tokens:
+            raise ValueError("tree_mask must be a 32-bit integer tensor of num_tokens words")
     params = make_params(num_seqs=num_seqs, num_tokens=num_tokens, num_q_heads=Hq,
                          num_kv_heads=Hkv, head_dim=D, block_size=bs, num_blocks=nb,
                          max_blocks_per_seq=block_tables.shape[1], q_dtype=_dtype_code(q),
                          kv_dtype=_dtype_code(k_cache), sliding_window=int(sliding_window),
-                         num_segments=int(num_segments))
+                         num_segments=int(num_segments), max_query_len=int(max_query_len),
+                         tree_mask=0 if tree_mask is None else tree_mask.data_ptr())
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     params.stream = stream or None
@@ -263,7 +271,7 @@ def _call(u8, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_le
                 float(scale), out.data_ptr())
     if prepare:
         keep = (q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
-                subsequence_begins, out, ws)
+                subsequence_begins, out, ws, tree_mask)
         return PreparedCall(fn, args, params, out, keep)
     rc = fn(*args, ctypes.byref(params))
     if rc != PA_OK:
@@ -274,7 +282,7 @@ def _call(u8, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_le
 def pa_verify_forward(q, k_cache, v_cache, block_tables, past_lens, subsequence_begins,
                       max_context_len: int, scale: float, out=None, *, sliding_window: int = 0,
                       num_segments: int = 0, workspace=None, stream: Optional[int] = None,
-                      prof_events=None):
+                      prof_events=None, max_query_len: int = 0, tree_mask=None):
     """Paged verify attention over an f16/bf16 cache; returns ``out``.
 
     q [num_tokens, Hq, D]; k_cache, v_cache [nb, Hkv, bs, D] with each page's
@@ -282,20 +290,24 @@ def pa_verify_forward(q, k_cache, v_cache, block_tables, past_lens, subsequence_
     block_tables [num_seqs, max_blocks_per_seq], past_lens [num_seqs],
     subsequence_begins [num_seqs + 1] (int32, device).  ``stream`` is a raw
     hipStream_t (default: torch's current stream); ``prof_events`` is an
-    optional pair of raw hipEvent_t recorded around the segment kernel."""
+    optional pair of raw hipEvent_t recorded around the segment kernel.
+    ``max_query_len`` bounds the new tokens per sequence (0: derived from
+    num_tokens and num_seqs); ``tree_mask`` is an optional int32/uint32
+    device tensor [num_tokens] of draft-tree visibility words."""
     return _call(False, q, k_cache, v_cache, None, None, block_tables, past_lens,
                  subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
-                 workspace, stream, prof_events)
+                 workspace, stream, prof_events, max_query_len=max_query_len, tree_mask=tree_mask)
 
 
 def pa_verify_forward_u8(q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
                          subsequence_begins, max_context_len: int, scale: float, out=None, *,
                          sliding_window: int = 0, num_segments: int = 0, workspace=None,
-                         stream: Optional[int] = None, prof_events=None):
+                         stream: Optional[int] = None, prof_events=None, max_query_len: int = 0,
+                         tree_mask=None):
     """The same over a u8 cache with f16 (scale, zero point) per token per KV head."""
     return _call(True, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
                  subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
-                 workspace, stream, prof_events)
+                 workspace, stream, prof_events, max_query_len=max_query_len, tree_mask=tree_mask)
 
 
 def pa_verify_read_status(device=None) -> int:
@@ -318,19 +330,22 @@ def pa_verify_read_status(device=None) -> int:
 
 def prepare_forward(q, k_cache, v_cache, block_tables, past_lens, subsequence_begins,
                     max_context_len: int, scale: float, out=None, *, sliding_window: int = 0,
-                    num_segments: int = 0, workspace=None, stream: Optional[int] = None):
+                    num_segments: int = 0, workspace=None, stream: Optional[int] = None,
+                    max_query_len: int = 0, tree_mask=None):
     """pa_verify_forward's checks and marshalling done once: returns a
     PreparedCall that enqueues the same call each time it is called."""
     return _call(False, q, k_cache, v_cache, None, None, block_tables, past_lens,
                  subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
-                 workspace, stream, None, prepare=True)
+                 workspace, stream, None, prepare=True, max_query_len=max_query_len,
+                 tree_mask=tree_mask)
 
 
 def prepare_forward_u8(q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
                        subsequence_begins, max_context_len: int, scale: float, out=None, *,
                        sliding_window: int = 0, num_segments: int = 0, workspace=None,
-                       stream: Optional[int] = None):
+                       stream: Optional[int] = None, max_query_len: int = 0, tree_mask=None):
     """pa_verify_forward_u8's checks and marshalling done once (see prepare_forward)."""
     return _call(True, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
                  subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
-                 workspace, stream, None, prepare=True)
+                 workspace, stream, None, prepare=True, max_query_len=max_query_len,
+                 tree_mask=tree_mask)

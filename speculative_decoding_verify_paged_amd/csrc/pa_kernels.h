@@ -10,8 +10,8 @@ namespace pav {
 enum : int { kF16 = 0, kBF16 = 1, kU8 = 2 };
 
 constexpr int kKeysPerStep = 32;     // keys one wavefront consumes per iteration
-constexpr int kRows = 16;            // stacked query rows per MFMA tile (G * T <= 16)
-constexpr int kMaxT = 4;             // verify rows per sequence
+constexpr int kRows = 16;            // stacked query rows per MFMA tile (one row block)
+constexpr int kMaxT = 16;            // verify rows per sequence (tree-mask words are 16 bits used)
 constexpr int kWavesPerGroup = 4;    // wavefronts per segment workgroup
 constexpr int kMaxSegBlocks = 1040;  // LDS slots for a segment's block ids
 constexpr int kDeviceContract = 5;   // value of PA_ERR_DEVICE_CONTRACT
@@ -26,11 +26,13 @@ struct SegmentArgs {
   const int32_t* bt;
   const int32_t* past_lens;
   const int32_t* sb;
+  const uint32_t* tree;              // optional [num_tokens] tree-mask words; null = causal rows
   float* ws_o;                       // [num_tokens, Hq, S, D] unnormalised partial outputs
   float* ws_ml;                      // [num_tokens, Hq, S, 2] (max in log2 units, sum)
   int32_t* status;                   // sticky device status word
   int32_t num_seqs, num_tokens, Hq, Hkv, G;
   int32_t num_blocks, mbps, window, max_ctx;
+  int32_t max_q;                     // bound on T_s the host planned for (<= kMaxT)
   int32_t S, steps_per_seg, n_steps;   // segments; max steps of one segment; steps the host plans for
   float scale_log2;                  // scale * log2(e)
 };
@@ -42,9 +44,13 @@ struct CombineArgs {
 };
 
 // ev0/ev1: optional events timestamped by the segment kernel's own dispatch
-hipError_t launch_segment(const SegmentArgs& a, int kv_dtype, int D, int bs, dim3 grid,
-                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
-hipError_t launch_segment_u8(const SegmentArgs& a, int q_dtype, int D, int bs, dim3 grid,
+// rb: 16-row blocks of stacked query rows (1 to max_row_blocks).
+// One function per cache dtype, each in its own translation unit.
+hipError_t launch_segment_f16(const SegmentArgs& a, int D, int bs, int rb, dim3 grid,
+                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_segment_bf16(const SegmentArgs& a, int D, int bs, int rb, dim3 grid,
+                               hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_segment_u8(const SegmentArgs& a, int q_dtype, int D, int bs, int rb, dim3 grid,
                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_combine(const CombineArgs& a, int out_dtype, int D, int threads, dim3 grid,
                           hipStream_t st);
@@ -54,25 +60,35 @@ constexpr int combine_threads(int S, int D) {
   return S * (D / 4) <= 256 * 8 ? 256 : S * (D / 4) <= 512 * 8 ? 512 : 1024;
 }
 
-// Per (cache dtype, head_dim): wavefronts per SIMD the segment kernel is
-// compiled for (its register budget, no spills), the steps each wavefront
-// keeps loaded (1: load then compute; 2: the next step's loads in flight
-// during this step's math), and the segment workgroups the planner puts on
-// each CU (at most the resident count, 4 SIMDs per CU).  u8 with D = 256
-// runs two wavefronts per SIMD for latency hiding but one workgroup per CU
-// in the plan: twice the segments only doubles the partials the combine
-// reads (measured on MI355X: no faster segment kernel, slower call).
+// Per (cache dtype, head_dim, row blocks): wavefronts per SIMD the segment
+// kernel is compiled for (its register budget, no spills), the steps each
+// wavefront keeps loaded (1: load then compute; 2: the next step's loads in
+// flight during this step's math), and the segment workgroups the planner
+// puts on each CU (at most the resident count, 4 SIMDs per CU).  u8 with
+// D = 256 runs two wavefronts per SIMD for latency hiding but one workgroup
+// per CU in the plan: twice the segments only doubles the partials the
+// combine reads (measured on MI355X: no faster segment kernel, slower call).
+// More than one row block needs the whole register file of one wavefront
+// per SIMD (and its LDS merge buffer allows one workgroup per CU).
 struct SegConfig {
   int waves_per_simd;
   int prefetch;
   int groups_per_cu;
 };
-constexpr SegConfig seg_config(int kv_dtype, int D) {
+constexpr SegConfig seg_config(int kv_dtype, int D, int rb) {
+  if (rb > 1) return SegConfig{1, 1, 1};
   if (kv_dtype == kU8)
-    return D >= 256 ? SegConfig{2, 1, 1} : D >= 128 ? SegConfig{2, 2, 2} : SegConfig{4, 1, 4};
+    return D >= 256 ? SegConfig{2, 1, 1} : D >= 128 ? SegConfig{1, 2, 1} : SegConfig{4, 1, 4};
   return D >= 256 ? SegConfig{1, 1, 1} : D >= 128 ? SegConfig{1, 2, 1} : SegConfig{4, 1, 4};
 }
-constexpr int groups_per_cu(int kv_dtype, int D) { return seg_config(kv_dtype, D).groups_per_cu; }
+constexpr int groups_per_cu(int kv_dtype, int D, int rb) { return seg_config(kv_dtype, D, rb).groups_per_cu; }
+static_assert(kWavesPerGroup == 4, "the table above assumes 4-wavefront workgroups");
+// Row blocks built per (cache dtype, head_dim): each adds D/4 accumulator
+// and D/8 query registers per lane and 16 * (D + 4) * 16 B of LDS; these are
+// the largest counts that compile without register spills.
+constexpr int max_row_blocks(int kv_dtype, int D) {
+  return D <= 64 ? 4 : D <= 128 ? 3 : kv_dtype == kU8 ? 2 : 1;
+}
 static_assert(kWavesPerGroup == 4, "the table above assumes 4-wavefront workgroups");
 
 }  // namespace pav

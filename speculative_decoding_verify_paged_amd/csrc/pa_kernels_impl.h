@@ -1,4 +1,5 @@
-// pa_kernels.hip — gfx950 kernels of paged verify attention.
+// pa_kernels_impl.h — gfx950 kernels of paged verify attention (device code
+// shared by the per-dtype translation units pa_segment_*.hip and pa_combine.hip).
 //
 // Two kernels per call:
 //   1. pa_segment: one workgroup per (KV segment j, KV head, sequence).  Its
@@ -39,6 +40,8 @@
 //                                           (bf16: hi + lo parts)
 // Every lane owns one stacked row r = lane % 16 in all three products, so the
 // softmax state and its rescale never leave the lane.
+#pragma once
+
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -149,14 +152,15 @@ struct SeqInfo {
   bool ok;
 };
 
-__device__ __forceinline__ SeqInfo seq_info(const SegmentArgs& a, int s) {
+// rows: stacked query rows the kernel instance holds (G * T must fit).
+__device__ __forceinline__ SeqInfo seq_info(const SegmentArgs& a, int s, int rows) {
   SeqInfo q;
   q.b0 = a.sb[s];
   const int b1 = a.sb[s + 1];
   q.T = b1 - q.b0;
   q.L = a.past_lens[s];
-  q.ok = q.b0 >= 0 && b1 <= a.num_tokens && q.T >= 1 && q.T <= kMaxT && q.L >= 0 &&
-         (int64_t)q.L + q.T <= a.max_ctx && a.G * q.T <= kRows;
+  q.ok = q.b0 >= 0 && b1 <= a.num_tokens && q.T >= 1 && q.T <= a.max_q && q.L >= 0 &&
+         (int64_t)q.L + q.T <= a.max_ctx && a.G * q.T <= rows;
   q.ctx = q.L + q.T;
   q.lo0 = a.window > 0 ? max(0, q.L + 1 - a.window) : 0;
   q.base = (q.lo0 / kKeysPerStep) * kKeysPerStep;
@@ -166,9 +170,11 @@ __device__ __forceinline__ SeqInfo seq_info(const SegmentArgs& a, int s) {
 
 // ---------------------------------------------------------------------------
 // Segment kernel.  QT: dtype of q (and of the MFMA operands); KV: cache dtype
-// (QT, or kU8 for codes with per-token f16 scale and zero point).
+// (QT, or kU8 for codes with per-token f16 scale and zero point); RB: 16-row
+// blocks of stacked query rows (G * T <= 16 * RB): each K/V operand a step
+// loads (and, for u8, converts) feeds one MFMA per row block.
 // ---------------------------------------------------------------------------
-template <int QT, int KV, int D, int BS, int NW, int WPE, int PF>
+template <int QT, int KV, int D, int BS, int NW, int WPE, int PF, int RB>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE)))
 void pa_segment(SegmentArgs a) {
   constexpr bool U8 = KV == kU8;
@@ -178,16 +184,17 @@ void pa_segment(SegmentArgs a) {
   constexpr int LV = LK;                          // 1 KB V loads per sub-tile
   constexpr int DT = D / 16;                      // 16-wide d tiles of O^T
   constexpr int OSTRIDE = D + 4;                  // padded LDS row of the merge buffer
+  constexpr int ROWS = kRows * RB;                // stacked rows this instance holds
   static_assert(BS % 16 == 0 && kKeysPerStep == 32, "two 16-slot sub-tiles per step");
   __shared__ int s_bt[kMaxSegBlocks];
-  __shared__ float s_m[NW][kRows];
-  __shared__ float s_l[NW][kRows];
-  __shared__ __attribute__((aligned(16))) float s_o[NW][kRows][OSTRIDE];
+  __shared__ float s_m[NW][ROWS];
+  __shared__ float s_l[NW][ROWS];
+  __shared__ __attribute__((aligned(16))) float s_o[NW][ROWS][OSTRIDE];
   __shared__ int s_bad;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int n16 = lane & 15;          // stacked query row owned by this lane
+  const int n16 = lane & 15;          // stacked query row owned by this lane (in each row block)
   const int q4 = lane >> 4;           // lane group
   // Grid (Hkv, num_seqs, S), segments last and in reverse: the launch
   // starts with the highest segments, which only the longest sequences of a
@@ -214,7 +221,7 @@ void pa_segment(SegmentArgs a) {
     spec_id[k] = x < spec_n ? bt_row[spec_lo + x] : 0;
   }
 
-  const SeqInfo si = seq_info(a, s);
+  const SeqInfo si = seq_info(a, s, ROWS);
   if (!si.ok) {
     // A sequence that breaks the contract: its partials for this segment
     // become NaN (for the tokens it claims that exist), so the combine turns
@@ -268,29 +275,53 @@ void pa_segment(SegmentArgs a) {
     }
   }
 
-  // Stacked rows: r = g*T + i for q head h*G + g and token b0 + i; rows past
-  // G*T are zero padding that no one reads back.
-  const bool row_ok = n16 < R;
-  const int g = row_ok ? n16 / T : 0;
-  const int i = row_ok ? n16 % T : T - 1;
-  const int qh = h * a.G + g;
-  const int tok = si.b0 + i;                                  // padded rows: a real token
-  const int hi_r = si.L + i + 1;                              // row's keys: [lo_r, hi_r)
-  const int lo_r = a.window > 0 ? max(0, hi_r - a.window) : 0;
+  // Stacked rows: r = g*T + i for q head h*G + g and token b0 + i; lane row
+  // n16 of row block rb is r = 16*rb + n16.  Rows past G*T are padding that
+  // no one reads back (they compute on a real token's q, so stay finite).
+  // Row r sees cache position t when t >= lo_r and, for t >= L (the new
+  // tokens), bit t - L of its mask vis_r is set: causal rows see new tokens
+  // 0..i; a tree row sees the tokens its word names, itself always.
+  bool row_ok[RB];
+  int qh[RB], tok[RB], lo_r[RB];
+  uint32_t vis_r[RB];
+  const uint32_t tmask = T >= 32 ? 0xffffffffu : (1u << T) - 1u;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = rb * kRows + n16;
+    row_ok[rb] = r < R;
+    const int g = row_ok[rb] ? r / T : 0;
+    const int i = row_ok[rb] ? r % T : T - 1;
+    qh[rb] = h * a.G + g;
+    tok[rb] = si.b0 + i;                                      // padded rows: a real token
+    lo_r[rb] = a.window > 0 ? max(0, si.L + i + 1 - a.window) : 0;
+    vis_r[rb] = (2u << i) - 1u;                               // causal: tokens 0..i
+  }
+  if (a.tree) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int i = tok[rb] - si.b0;
+      vis_r[rb] = (a.tree[tok[rb]] & tmask) | (1u << i);
+    }
+  }
   const int lo_max = a.window > 0 ? max(0, si.ctx - a.window) : 0;
+  // a step is interior when every row sees all of its keys: past keys only
+  // for tree rows; for causal rows key L too (row 0 sees it)
+  const int all_see = si.L + (a.tree ? 0 : 1);
 
   // B operand of the QK product: lane (row, group q4) holds, for k-chunk c,
   // the 8 d values the K sub-tile load puts in the same lane group:
   // d = c*32 + q4*8 + 0..7 (u8: chunk 2*c2 + half: d = c2*64 + q4*16 + half*8 + 0..7).
-  u32x4 qreg[QC];
-  float qsum = 0.f;                                           // u8: sum of this lane's q values
-  {
-    const char* qp = reinterpret_cast<const char*>(a.q) + ((size_t)tok * a.Hq + qh) * D * 2;
+  u32x4 qreg[RB][QC];
+  float qsum[RB];                                             // u8: sum of this lane's q values
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    qsum[rb] = 0.f;
+    const char* qp = reinterpret_cast<const char*>(a.q) + ((size_t)tok[rb] * a.Hq + qh[rb]) * D * 2;
 #pragma unroll
     for (int c = 0; c < QC; ++c) {
       const int d0 = U8 ? (c / 2) * 64 + q4 * 16 + (c % 2) * 8 : c * 32 + q4 * 8;
       const u32x4 v = ld16(qp + d0 * 2);
-      qreg[c] = row_ok ? v : u32x4{0, 0, 0, 0};
+      qreg[rb][c] = row_ok[rb] ? v : u32x4{0, 0, 0, 0};
     }
   }
   // u8: the row sum of q, taken once the first KV loads are in flight so
@@ -298,19 +329,22 @@ void pa_segment(SegmentArgs a) {
   auto finish_q = [&]() {
     if constexpr (U8) {
 #pragma unroll
-      for (int c = 0; c < QC; ++c) {
+      for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          if constexpr (QT == kF16) {
-            qsum += lo_f16(qreg[c][w]) + hi_f16(qreg[c][w]);
-          } else {
-            qsum += __builtin_bit_cast(float, qreg[c][w] << 16) +
-                    __builtin_bit_cast(float, qreg[c][w] & 0xffff0000u);
+        for (int c = 0; c < QC; ++c) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            if constexpr (QT == kF16) {
+              qsum[rb] += lo_f16(qreg[rb][c][w]) + hi_f16(qreg[rb][c][w]);
+            } else {
+              qsum[rb] += __builtin_bit_cast(float, qreg[rb][c][w] << 16) +
+                          __builtin_bit_cast(float, qreg[rb][c][w] & 0xffff0000u);
+            }
           }
         }
+        qsum[rb] += __shfl_xor(qsum[rb], 16, kWave);
+        qsum[rb] += __shfl_xor(qsum[rb], 32, kWave);
       }
-      qsum += __shfl_xor(qsum, 16, kWave);
-      qsum += __shfl_xor(qsum, 32, kWave);
     }
   };
   __syncthreads();
@@ -357,53 +391,75 @@ void pa_segment(SegmentArgs a) {
     }
   };
 
-  f32x4 o[DT];
+  f32x4 o[RB][DT];
+  float m_run[RB];                    // running max (log2 units) of this lane's row
+  float l_run[RB];                    // this lane's share of the running sum
+  float c_run[RB];                    // u8: this lane's share of sum p * s_v * zp_v
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;            // running max (log2 units) of this lane's row
-  float l_run = 0.f;                  // this lane's share of the running sum
-  float c_run = 0.f;                  // u8: this lane's share of sum p * s_v * zp_v
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[rb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.f;
+    c_run[rb] = 0.f;
+  }
 
   auto compute_step = [&](int st, Step& r) {
     const int key0 = si.base + st * kKeysPerStep;
     // S^T for both sub-tiles: lane (row, q4) gets keys key0 + 16*tau + 4*q4 + 0..3
-    float sv[8];
+    float sv[RB][8];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      // two interleaved accumulation chains: no MFMA waits on the one before
-      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+      // two interleaved accumulation chains per row block: no MFMA waits on
+      // the one before
+      f32x4 acc0[RB], acc1[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) acc0[rb] = acc1[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (U8) {
 #pragma unroll
         for (int c2 = 0; c2 < LK; ++c2) {
           const u32x4 w = r.k[tau][c2];
           const u32x2 a0 = u8x4_to_16<QT>(w[0]), a1 = u8x4_to_16<QT>(w[1]);
           const u32x2 a2 = u8x4_to_16<QT>(w[2]), a3 = u8x4_to_16<QT>(w[3]);
-          acc0 = mfma32<QT>(u32x4{a0[0], a0[1], a1[0], a1[1]}, qreg[2 * c2], acc0);
-          acc1 = mfma32<QT>(u32x4{a2[0], a2[1], a3[0], a3[1]}, qreg[2 * c2 + 1], acc1);
+          const u32x4 k0 = {a0[0], a0[1], a1[0], a1[1]}, k1 = {a2[0], a2[1], a3[0], a3[1]};
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            acc0[rb] = mfma32<QT>(k0, qreg[rb][2 * c2], acc0[rb]);
+            acc1[rb] = mfma32<QT>(k1, qreg[rb][2 * c2 + 1], acc1[rb]);
+          }
         }
-        const f32x4 acc = acc0 + acc1;
         // q.(u - zp) * s = s * (q.(u + bias) - (zp + bias) * sum(q))
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float sk = lo_f16(r.ks[tau][e]), zk = hi_f16(r.ks[tau][e]) + kU8Bias<QT>;
-          sv[tau * 4 + e] = sk * (acc[e] - zk * qsum) * a.scale_log2;
+        for (int rb = 0; rb < RB; ++rb) {
+          const f32x4 acc = acc0[rb] + acc1[rb];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float sk = lo_f16(r.ks[tau][e]), zk = hi_f16(r.ks[tau][e]) + kU8Bias<QT>;
+            sv[rb][tau * 4 + e] = sk * (acc[e] - zk * qsum[rb]) * a.scale_log2;
+          }
         }
       } else {
 #pragma unroll
         for (int c = 0; c < QC; c += 2) {
-          acc0 = mfma32<QT>(r.k[tau][c], qreg[c], acc0);
-          if (c + 1 < QC) acc1 = mfma32<QT>(r.k[tau][c + 1], qreg[c + 1], acc1);
-        }
-        const f32x4 acc = acc0 + acc1;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sv[tau * 4 + e] = acc[e] * a.scale_log2;
+          for (int rb = 0; rb < RB; ++rb) {
+            acc0[rb] = mfma32<QT>(r.k[tau][c], qreg[rb][c], acc0[rb]);
+            if (c + 1 < QC) acc1[rb] = mfma32<QT>(r.k[tau][c + 1], qreg[rb][c + 1], acc1[rb]);
+          }
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const f32x4 acc = acc0[rb] + acc1[rb];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sv[rb][tau * 4 + e] = acc[e] * a.scale_log2;
+        }
       }
     }
 
     // Keys outside [lo0, ctx) may hold anything, NaN included: their logits
     // become -inf and, since 0 * NaN is not 0, their V (or u8 scale) never
     // reaches the PV product.
-    const bool interior = key0 >= lo_max && key0 + kKeysPerStep <= si.L + 1;
+    const bool interior = key0 >= lo_max && key0 + kKeysPerStep <= all_see;
     bool kvalid[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) kvalid[e] = true;
@@ -412,63 +468,70 @@ void pa_segment(SegmentArgs a) {
       for (int e = 0; e < 8; ++e) {
         const int t = key0 + (e >> 2) * 16 + q4 * 4 + (e & 3);
         kvalid[e] = t >= si.lo0 && t < si.ctx;
-        sv[e] = (t >= lo_r && t < hi_r) ? sv[e] : -INFINITY;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const bool seen = t >= lo_r[rb] && (t < si.L || (t < si.ctx && ((vis_r[rb] >> (t - si.L)) & 1u)));
+          sv[rb][e] = seen ? sv[rb][e] : -INFINITY;
+        }
       }
     }
 
-    float mx = sv[0];
+    u32x4 pb_hi[RB], pb_lo[RB];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-    mx = xor_max(mx, 16);
-    mx = xor_max(mx, 32);
-    // Lazy rescaling: weights are taken relative to a reference max m_run
-    // that only moves when a logit passes it by more than 2^kRescaleLog2, so
-    // weights stay <= 256 (exact in the hi/lo split) and the O rescale runs
-    // in few steps.  The branch is wave-uniform.
-    const bool need = mx > m_run + kRescaleLog2;
-    if (__any(need)) {
-      const float m_new = need ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+    for (int rb = 0; rb < RB; ++rb) {
+      float mx = sv[rb][0];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-      l_run *= alpha;
-      c_run *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float p[8];
-    float psum = 0.f;
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[rb][e]);
+      mx = xor_max(mx, 16);
+      mx = xor_max(mx, 32);
+      // Lazy rescaling: weights are taken relative to a reference max m_run
+      // that only moves when a logit passes it by more than 2^kRescaleLog2,
+      // so weights stay <= 256 and the O rescale runs in few steps.  The
+      // branch is wave-uniform.
+      const bool need = mx > m_run[rb] + kRescaleLog2;
+      if (__any(need)) {
+        const float m_new = need ? mx : m_run[rb];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - (m_new == -INFINITY ? 0.f : m_new));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
-      psum += p[e];
-    }
-    l_run += psum;
-
-    if constexpr (U8) {
-      // (u - zp) * s folded: the codes (offset by the bias) are multiplied
-      // by P' = p * s_v, and sum(P' * (zp_v + bias)) is subtracted from every
-      // d at the end.  With f16 weights the sum uses P' as rounded for the
-      // MFMA, so the bias cancels exactly.
-      float csum = 0.f;
+        for (int dt = 0; dt < DT; ++dt) o[rb][dt] *= alpha;
+        l_run[rb] *= alpha;
+        c_run[rb] *= alpha;
+        m_run[rb] = m_new;
+      }
+      const float m_use = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
+      float p[8];
+      float psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t w = r.vs[e >> 2][e & 3];
-        float sp = kvalid[e] ? p[e] * lo_f16(w) : 0.f;
-        if constexpr (QT == kF16) sp = (float)(_Float16)sp;
-        csum += kvalid[e] ? sp * (hi_f16(w) + kU8Bias<QT>) : 0.f;   // zp of a key outside may be NaN
-        p[e] = sp;
+        p[e] = __builtin_amdgcn_exp2f(sv[rb][e] - m_use);
+        psum += p[e];
       }
-      c_run += csum;
+      l_run[rb] += psum;
+
+      if constexpr (U8) {
+        // (u - zp) * s folded: the codes (offset by the bias) are multiplied
+        // by P' = p * s_v, and sum(P' * (zp_v + bias)) is subtracted from
+        // every d at the end.  With f16 weights the sum uses P' as rounded
+        // for the MFMA, so the bias cancels exactly.
+        float csum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t w = r.vs[e >> 2][e & 3];
+          float sp = kvalid[e] ? p[e] * lo_f16(w) : 0.f;
+          if constexpr (QT == kF16) sp = (float)(_Float16)sp;
+          csum += kvalid[e] ? sp * (hi_f16(w) + kU8Bias<QT>) : 0.f;   // zp of a key outside may be NaN
+          p[e] = sp;
+        }
+        c_run[rb] += csum;
+      }
+      pack_p<QT>(p, pb_hi[rb], pb_lo[rb]);
     }
-    u32x4 pb_hi, pb_lo;
-    pack_p<QT>(p, pb_hi, pb_lo);
     // PV, O^T[d, r] += V^T[d, key] P^T[key, r] with one 16x16x32 product per
-    // 16-wide d tile: the A operand of lane (d, q4) is V of keys 4*q4 + 0..3
-    // of both sub-tiles, the k order of the weights above.  The loaded V
-    // registers are never modified: in a boundary step the f16/bf16 V of a
-    // key outside [lo0, ctx) is cleared as it is consumed (u8 codes are
-    // finite; their P' is already 0).
+    // 16-wide d tile and row block: the A operand of lane (d, q4) is V of
+    // keys 4*q4 + 0..3 of both sub-tiles, the k order of the weights above.
+    // The loaded V registers are never modified: in a boundary step the
+    // f16/bf16 V of a key outside [lo0, ctx) is cleared as it is consumed
+    // (u8 codes are finite; their P' is already 0).
     auto pv = [&](auto masked) {
       u32x2 vmask[2];
       if constexpr (decltype(masked)::value) {
@@ -493,12 +556,20 @@ void pa_segment(SegmentArgs a) {
         return u32x4{va[0][0], va[0][1], va[1][0], va[1][1]};
       };
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] = mfma32<QT>(vop(dt), pb_hi, o[dt]);
+      for (int dt = 0; dt < DT; ++dt) {
+        const u32x4 va = vop(dt);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[rb][dt] = mfma32<QT>(va, pb_hi[rb], o[rb][dt]);
+      }
       if constexpr (QT == kBF16) {
         // all hi products, then all lo: consecutive MFMAs never update the
         // same accumulator
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt] = mfma32<QT>(vop(dt), pb_lo, o[dt]);
+        for (int dt = 0; dt < DT; ++dt) {
+          const u32x4 va = vop(dt);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) o[rb][dt] = mfma32<QT>(va, pb_lo[rb], o[rb][dt]);
+        }
       }
     };
     if (U8 || interior)
@@ -549,25 +620,28 @@ void pa_segment(SegmentArgs a) {
     }
   }
 
-  // Row sums: each lane group holds a quarter of the keys.
-  l_run += __shfl_xor(l_run, 16, kWave);
-  l_run += __shfl_xor(l_run, 32, kWave);
-  if constexpr (U8) {
-    c_run += __shfl_xor(c_run, 16, kWave);
-    c_run += __shfl_xor(c_run, 32, kWave);
+  // Row sums: each lane group holds a quarter of the keys.  Then merge the
+  // wavefronts of the workgroup: M = max_w m_w, then sum the partials
+  // rescaled by 2^(m_w - M), in a fixed order (bitwise repeatable).
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] -= c_run;
-  }
-
-  // Merge the wavefronts of the workgroup: M = max_w m_w, then sum the
-  // partials rescaled by 2^(m_w - M), in a fixed order (bitwise repeatable).
-  if (q4 == 0) {
-    s_m[wave][n16] = m_run;
-    s_l[wave][n16] = l_run;
-  }
+  for (int rb = 0; rb < RB; ++rb) {
+    l_run[rb] += __shfl_xor(l_run[rb], 16, kWave);
+    l_run[rb] += __shfl_xor(l_run[rb], 32, kWave);
+    if constexpr (U8) {
+      c_run[rb] += __shfl_xor(c_run[rb], 16, kWave);
+      c_run[rb] += __shfl_xor(c_run[rb], 32, kWave);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-    *reinterpret_cast<f32x4*>(&s_o[wave][n16][dt * 16 + q4 * 4]) = o[dt];
+      for (int dt = 0; dt < DT; ++dt) o[rb][dt] -= c_run[rb];
+    }
+    const int r = rb * kRows + n16;
+    if (q4 == 0) {
+      s_m[wave][r] = m_run[rb];
+      s_l[wave][r] = l_run[rb];
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<f32x4*>(&s_o[wave][r][dt * 16 + q4 * 4]) = o[rb][dt];
+  }
   __syncthreads();
 
   const bool bad = s_bad != 0;
@@ -607,206 +681,57 @@ void pa_segment(SegmentArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Combine kernel: one workgroup per (token, q head), NT threads with NT sized
-// by the host so all S partials are loaded in one batch of K per thread.  Thread t owns d columns
-// [c4, c4 + 4) of the segments sub, sub + NSUB, ...; it merges them with the
-// same online rescaling as the segment kernel (every load independent of the
-// previous iteration's arithmetic, so they all go out at once), then the
-// NSUB partial states are merged through LDS in a fixed order.
+// Launchers: one instance per (q dtype, cache dtype, D, block size, row
+// blocks); each pa_segment_*.hip instantiates one cache dtype.
 // ---------------------------------------------------------------------------
-template <int D, int OUT, int NT>
-__global__ __launch_bounds__(NT) void pa_combine(CombineArgs a) {
-  constexpr int LPS = D / 4;                                  // threads per segment row
-  constexpr int NSUB = NT / LPS;                              // segment rows in flight
-  constexpr int K = 8;                                        // partials per thread per batch
-  __shared__ float s_m[NSUB];
-  __shared__ float s_den[NSUB];
-  __shared__ __attribute__((aligned(16))) f32x4 s_acc[NSUB][LPS];
-
-  const int pair = blockIdx.x;                                // token * Hq + q head
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int sub = tid / LPS;
-  const int col = tid % LPS;
-  const int n = pair / a.Hq;
-  const int S = a.seg.S;
-
-  // subsequence_begins, 64 entries per lane step: its first chunk goes out
-  // with the partial loads
-  const int nseq = a.seg.num_seqs;
-  const int sb_next = lane < nseq ? a.seg.sb[lane + 1] : 0;
-  const int sb_this = lane < nseq ? a.seg.sb[lane] : 0;
-
-  // Every segment of a valid sequence wrote its partial (empty ones as
-  // (-inf, 0)), so these loads depend on nothing but the grid position.  They
-  // are unconditional (clamped index) so they all go out together.
-  const float* ml = a.seg.ws_ml + (size_t)pair * S * 2;
-  const float* op = a.seg.ws_o + (size_t)pair * S * D + col * 4;
-  float m = -INFINITY, den = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  bool nan_seen = false;
-  for (int b = 0; b < S; b += NSUB * K) {
-    float mj[K], lj[K];
-    f32x4 oj[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int jj = b + sub + k * NSUB;
-      const int jc = jj < S ? jj : 0;
-      mj[k] = ml[jc * 2];
-      lj[k] = ml[jc * 2 + 1];
-      oj[k] = *reinterpret_cast<const f32x4*>(op + (size_t)jc * D);
-      mj[k] = jj < S ? mj[k] : -INFINITY;
-    }
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      nan_seen |= mj[k] != mj[k];
-      const float m_new = fmaxf(m, mj[k]);
-      const float base = m_new == -INFINITY ? 0.f : m_new;
-      const float sc = __builtin_amdgcn_exp2f(m - base);
-      const float f = __builtin_amdgcn_exp2f(mj[k] - base);
-      // a segment in which this row saw no key left its O slot unwritten
-      const f32x4 o = mj[k] == -INFINITY ? f32x4{0.f, 0.f, 0.f, 0.f} : oj[k];
-      den = den * sc + f * lj[k];
-      acc = acc * sc + f * o;
-      m = m_new;
-    }
-  }
-
-  // subsequence_begins must start at 0, never decrease and end at
-  // num_tokens; then token n belongs to the first s with n < sb[s + 1].  A
-  // sequence that breaks the rest of the contract left NaN in its partials.
-  bool ok = true;
-  int s = -1;
-  {
-    ok &= !__any(lane < nseq && sb_this > sb_next);
-    ok &= __shfl(sb_this, 0, kWave) == 0;
-    if (nseq <= kWave) ok &= __shfl(sb_next, nseq - 1, kWave) == a.seg.num_tokens;
-    const unsigned long long hit = __ballot(lane < nseq && n < sb_next);
-    if (hit) s = __builtin_ctzll(hit);
-  }
-  for (int b = kWave; b < nseq; b += kWave) {                 // more than 64 sequences
-    const int k = b + lane;
-    const int nx = k < nseq ? a.seg.sb[k + 1] : 0;
-    const int th = k < nseq ? a.seg.sb[k] : 0;
-    ok &= !__any(k < nseq && th > nx);
-    if (b + kWave >= nseq) ok &= __shfl(nx, nseq - 1 - b, kWave) == a.seg.num_tokens;
-    const unsigned long long hit = __ballot(k < nseq && n < nx);
-    if (s < 0 && hit) s = b + __builtin_ctzll(hit);
-  }
-  ok &= s >= 0;
-  if (col == 0) {
-    s_m[sub] = m;
-    s_den[sub] = den;
-  }
-  s_acc[sub][col] = acc;
-  const bool bad = __syncthreads_or(nan_seen || !ok);
-  if (bad && tid == 0) atomicExch(a.seg.status, kDeviceContract);
-  if (tid >= LPS) return;
-  float M = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < NSUB; ++k) M = fmaxf(M, s_m[k]);
-  f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  float dsum = 0.f;
-#pragma unroll
-  for (int k = 0; k < NSUB; ++k) {
-    const float f = s_m[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[k] - M);
-    num += f * s_acc[k][tid];
-    dsum += f * s_den[k];
-  }
-  float res[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) res[k] = bad ? NAN : num[k] / dsum;
-  if constexpr (OUT == kF16) {
-    _Float16* out = reinterpret_cast<_Float16*>(a.out) + (size_t)pair * D + tid * 4;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) out[k] = (_Float16)res[k];
-  } else {
-    __bf16* out = reinterpret_cast<__bf16*>(a.out) + (size_t)pair * D + tid * 4;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) out[k] = (__bf16)res[k];
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Instances and launchers.
-// ---------------------------------------------------------------------------
-template <int QT, int KV, int D, int BS>
-static hipError_t launch_seg(const SegmentArgs& a, dim3 grid, hipStream_t st, hipEvent_t ev0,
-                             hipEvent_t ev1) {
-  constexpr int WPE = seg_config(KV, D).waves_per_simd;
-  constexpr int PF = seg_config(KV, D).prefetch;
+template <int QT, int KV, int D, int BS, int RB>
+hipError_t launch_seg(const SegmentArgs& a, dim3 grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  constexpr SegConfig c = seg_config(KV, D, RB);
+  constexpr auto kern = pa_segment<QT, KV, D, BS, kWavesPerGroup, c.waves_per_simd, c.prefetch, RB>;
   // with events, the dispatch itself timestamps the kernel's start and end
   if (ev0 || ev1)
-    hipExtLaunchKernelGGL((pa_segment<QT, KV, D, BS, kWavesPerGroup, WPE, PF>), grid,
-                          dim3(kWavesPerGroup * kWave), 0, st, ev0, ev1, 0, a);
+    hipExtLaunchKernelGGL(kern, grid, dim3(kWavesPerGroup * kWave), 0, st, ev0, ev1, 0, a);
   else
-    hipLaunchKernelGGL((pa_segment<QT, KV, D, BS, kWavesPerGroup, WPE, PF>), grid,
-                       dim3(kWavesPerGroup * kWave), 0, st, a);
+    hipLaunchKernelGGL(kern, grid, dim3(kWavesPerGroup * kWave), 0, st, a);
   return hipGetLastError();
 }
 
+template <int QT, int KV, int D, int BS>
+hipError_t dispatch_rb(const SegmentArgs& a, int rb, dim3 grid, hipStream_t st, hipEvent_t e0,
+                       hipEvent_t e1) {
+  switch (rb) {
+    case 1: return launch_seg<QT, KV, D, BS, 1>(a, grid, st, e0, e1);
+    case 2:
+      if constexpr (max_row_blocks(KV, D) >= 2) return launch_seg<QT, KV, D, BS, 2>(a, grid, st, e0, e1);
+      break;
+    case 3:
+      if constexpr (max_row_blocks(KV, D) >= 3) return launch_seg<QT, KV, D, BS, 3>(a, grid, st, e0, e1);
+      break;
+    case 4:
+      if constexpr (max_row_blocks(KV, D) >= 4) return launch_seg<QT, KV, D, BS, 4>(a, grid, st, e0, e1);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int QT, int KV, int D>
-static hipError_t dispatch_bs(const SegmentArgs& a, int bs, dim3 grid, hipStream_t st,
-                              hipEvent_t e0, hipEvent_t e1) {
+hipError_t dispatch_bs(const SegmentArgs& a, int bs, int rb, dim3 grid, hipStream_t st,
+                       hipEvent_t e0, hipEvent_t e1) {
   switch (bs) {
-    case 16: return launch_seg<QT, KV, D, 16>(a, grid, st, e0, e1);
-    case 32: return launch_seg<QT, KV, D, 32>(a, grid, st, e0, e1);
-    case 64: return launch_seg<QT, KV, D, 64>(a, grid, st, e0, e1);
+    case 16: return dispatch_rb<QT, KV, D, 16>(a, rb, grid, st, e0, e1);
+    case 32: return dispatch_rb<QT, KV, D, 32>(a, rb, grid, st, e0, e1);
+    case 64: return dispatch_rb<QT, KV, D, 64>(a, rb, grid, st, e0, e1);
   }
   return hipErrorInvalidValue;
 }
 
 template <int QT, int KV>
-static hipError_t dispatch_d(const SegmentArgs& a, int D, int bs, dim3 grid, hipStream_t st,
-                             hipEvent_t e0, hipEvent_t e1) {
+hipError_t dispatch_d(const SegmentArgs& a, int D, int bs, int rb, dim3 grid, hipStream_t st,
+                      hipEvent_t e0, hipEvent_t e1) {
   switch (D) {
-    case 64: return dispatch_bs<QT, KV, 64>(a, bs, grid, st, e0, e1);
-    case 128: return dispatch_bs<QT, KV, 128>(a, bs, grid, st, e0, e1);
-    case 256: return dispatch_bs<QT, KV, 256>(a, bs, grid, st, e0, e1);
-  }
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_segment(const SegmentArgs& a, int kv_dtype, int D, int bs, dim3 grid,
-                          hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  if (kv_dtype == kF16) return dispatch_d<kF16, kF16>(a, D, bs, grid, st, e0, e1);
-  if (kv_dtype == kBF16) return dispatch_d<kBF16, kBF16>(a, D, bs, grid, st, e0, e1);
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_segment_u8(const SegmentArgs& a, int q_dtype, int D, int bs, dim3 grid,
-                             hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  if (q_dtype == kF16) return dispatch_d<kF16, kU8>(a, D, bs, grid, st, e0, e1);
-  if (q_dtype == kBF16) return dispatch_d<kBF16, kU8>(a, D, bs, grid, st, e0, e1);
-  return hipErrorInvalidValue;
-}
-
-template <int D, int NT>
-static hipError_t launch_combine_nt(const CombineArgs& a, int out_dtype, dim3 grid, hipStream_t st) {
-  if (out_dtype == kF16)
-    hipLaunchKernelGGL((pa_combine<D, kF16, NT>), grid, dim3(NT), 0, st, a);
-  else
-    hipLaunchKernelGGL((pa_combine<D, kBF16, NT>), grid, dim3(NT), 0, st, a);
-  return hipGetLastError();
-}
-
-template <int D>
-static hipError_t launch_combine_d(const CombineArgs& a, int out_dtype, int threads, dim3 grid,
-                                   hipStream_t st) {
-  switch (threads) {
-    case 256: return launch_combine_nt<D, 256>(a, out_dtype, grid, st);
-    case 512: return launch_combine_nt<D, 512>(a, out_dtype, grid, st);
-    case 1024: return launch_combine_nt<D, 1024>(a, out_dtype, grid, st);
-  }
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_combine(const CombineArgs& a, int out_dtype, int D, int threads, dim3 grid,
-                          hipStream_t st) {
-  switch (D) {
-    case 64: return launch_combine_d<64>(a, out_dtype, threads, grid, st);
-    case 128: return launch_combine_d<128>(a, out_dtype, threads, grid, st);
-    case 256: return launch_combine_d<256>(a, out_dtype, threads, grid, st);
+    case 64: return dispatch_bs<QT, KV, 64>(a, bs, rb, grid, st, e0, e1);
+    case 128: return dispatch_bs<QT, KV, 128>(a, bs, rb, grid, st, e0, e1);
+    case 256: return dispatch_bs<QT, KV, 256>(a, bs, rb, grid, st, e0, e1);
   }
   return hipErrorInvalidValue;
 }

@@ -25,10 +25,21 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Upper bound on segment-kernel workgroups per resident slot (see make_plan).
 constexpr int64_t kMaxRounds = 8;
+// T_s bound when the caller gives none (max_query_len == 0).
+constexpr int64_t kDefaultQueryLen = 4;
 
 bool is_pow2_in(int v, int lo, int hi) {
   if (v < lo || v > hi) return false;
   return (v & (v - 1)) == 0;
+}
+
+// Bound on the new tokens of one sequence: max_query_len when given, else
+// the classic verify bound of 4 (or fewer when num_tokens and num_seqs
+// allow no more).
+int64_t query_bound(const pa_verify_params* p) {
+  const int64_t t = p->max_query_len > 0 ? p->max_query_len
+                                         : std::min<int64_t>(kDefaultQueryLen, (int64_t)p->num_tokens - p->num_seqs + 1);
+  return std::max<int64_t>(1, std::min<int64_t>(t, pav::kMaxT));
 }
 
 // Host-checkable contract.  u8_entry selects which entry point is asking.
@@ -54,7 +65,19 @@ int validate(const pa_verify_params* p, int32_t max_ctx, bool u8_entry) {
   if ((int64_t)p->num_blocks * p->num_kv_heads * p->block_size > INT32_MAX) return PA_ERR_UNSUPPORTED;
   if ((int64_t)p->num_tokens * p->num_q_heads > INT32_MAX / 4) return PA_ERR_UNSUPPORTED;
   if (p->num_seqs > 65535 || p->num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;   // grid y, x limits
+  if (p->max_query_len < 0) return PA_ERR_INVALID_ARG;
+  if (p->max_query_len > pav::kMaxT) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)G * query_bound(p) > (int64_t)pav::kRows * pav::max_row_blocks(p->kv_dtype, p->head_dim))
+    return PA_ERR_UNSUPPORTED;
+  if (p->tree_mask && p->sliding_window > 0) return PA_ERR_UNSUPPORTED;
   return PA_OK;
+}
+
+// 16-row blocks of the segment kernel for these params: enough for
+// G * (bound on T_s) stacked rows.
+int row_blocks(const pa_verify_params* p) {
+  const int64_t rows = (int64_t)(p->num_q_heads / p->num_kv_heads) * query_bound(p);
+  return (int)std::max<int64_t>(1, cdiv(rows, pav::kRows));
 }
 
 int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_verify_plan* pl) {
@@ -63,7 +86,7 @@ int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_ve
   if (p->sliding_window > 0) {
     // rows of one sequence read at most W + T - 1 keys; the first step is
     // aligned down to a step boundary
-    span = std::min<int64_t>(span, (int64_t)p->sliding_window + pav::kMaxT - 1 + kKeysPerStep - 1);
+    span = std::min<int64_t>(span, (int64_t)p->sliding_window + query_bound(p) - 1 + kKeysPerStep - 1);
   }
   const int64_t n_steps = cdiv(span, kKeysPerStep);
   // a segment's block ids must fit the kernel's LDS staging buffer
@@ -76,7 +99,8 @@ int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_ve
     // covers every resident workgroup slot of the GPU (every CU busy at
     // batch 1, and in a ragged batch the longest sequence is not left to a
     // few CUs), but at most kMaxRounds rounds of workgroups in all.
-    const int64_t groups = (int64_t)num_cus * pav::groups_per_cu(p->kv_dtype, p->head_dim);
+    const int64_t groups =
+        (int64_t)num_cus * pav::groups_per_cu(p->kv_dtype, p->head_dim, row_blocks(p));
     const int64_t pairs = (int64_t)p->num_kv_heads * p->num_seqs;
     S = cdiv(groups, p->num_kv_heads);
     S = std::min(S, std::max<int64_t>(cdiv(groups, pairs), kMaxRounds * groups / pairs));
@@ -87,6 +111,7 @@ int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_ve
   pl->num_segments = (int32_t)S;
   pl->steps_per_segment = (int32_t)sps;
   pl->num_steps = (int32_t)n_steps;
+  pl->row_blocks = row_blocks(p);
   pl->keys_per_step = kKeysPerStep;
   pl->span = (int32_t)span;
   pl->waves_per_group = kWavesPerGroup;
@@ -174,6 +199,7 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
   a.bt = bt;
   a.past_lens = past_lens;
   a.sb = sb;
+  a.tree = static_cast<const uint32_t*>(p->tree_mask);
   a.status = reinterpret_cast<int32_t*>(ws);
   a.ws_ml = reinterpret_cast<float*>(ws + 256);
   a.ws_o = reinterpret_cast<float*>(ws + 256 + ml_bytes);
@@ -186,6 +212,7 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
   a.mbps = p->max_blocks_per_seq;
   a.window = p->sliding_window;
   a.max_ctx = max_ctx;
+  a.max_q = (int32_t)query_bound(p);
   a.S = pl.num_segments;
   a.steps_per_seg = pl.steps_per_segment;
   a.n_steps = pl.num_steps;
@@ -195,9 +222,14 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
   hipEvent_t e0 = static_cast<hipEvent_t>(p->prof_event_begin);
   hipEvent_t e1 = static_cast<hipEvent_t>(p->prof_event_end);
   const dim3 grid(pl.grid[0], pl.grid[1], pl.grid[2]);
-  hipError_t e =
-      u8_entry ? pav::launch_segment_u8(a, p->q_dtype, p->head_dim, p->block_size, grid, st, e0, e1)
-               : pav::launch_segment(a, p->kv_dtype, p->head_dim, p->block_size, grid, st, e0, e1);
+  const int rb = pl.row_blocks;
+  hipError_t e;
+  if (u8_entry)
+    e = pav::launch_segment_u8(a, p->q_dtype, p->head_dim, p->block_size, rb, grid, st, e0, e1);
+  else if (p->kv_dtype == PA_F16)
+    e = pav::launch_segment_f16(a, p->head_dim, p->block_size, rb, grid, st, e0, e1);
+  else
+    e = pav::launch_segment_bf16(a, p->head_dim, p->block_size, rb, grid, st, e0, e1);
   if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
   if (e != hipSuccess) return PA_ERR_HIP;
   pav::CombineArgs c;

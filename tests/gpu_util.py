@@ -33,18 +33,24 @@ def to_device(case: pi.Case, device="cuda"):
     if case.kv_dtype == pi.U8:
         d["k_scale_zp"] = _t(case.k_scale_zp, torch.float16, device)
         d["v_scale_zp"] = _t(case.v_scale_zp, torch.float16, device)
+    if getattr(case, "tree_mask", None) is not None:
+        d["tree_mask"] = torch.from_numpy(case.tree_mask.view(np.int32)).to(device)
     return d
 
 
 def run_gpu(case: pi.Case, dev=None, *, num_segments=0, out=None, max_context_len=None,
-            sync=True, **kw):
-    """Call the library on the case; returns the output tensor (device)."""
+            max_query_len=None, sync=True, **kw):
+    """Call the library on the case; returns the output tensor (device).
+    max_query_len defaults to the case's largest T; a case with a tree mask
+    runs as tree verify."""
     import torch
     import speculative_decoding_verify_paged_amd as pav
     if dev is None:
         dev = to_device(case)
     mcl = case.max_context_len if max_context_len is None else max_context_len
-    common = dict(sliding_window=case.sliding_window, num_segments=num_segments, **kw)
+    mql = max(case.Ts) if max_query_len is None else max_query_len
+    common = dict(sliding_window=case.sliding_window, num_segments=num_segments,
+                  max_query_len=mql, tree_mask=dev.get("tree_mask"), **kw)
     if case.kv_dtype == pi.U8:
         o = pav.pa_verify_forward_u8(dev["q"], dev["k_cache"], dev["v_cache"], dev["k_scale_zp"],
                                      dev["v_scale_zp"], dev["block_tables"], dev["past_lens"],

@@ -41,8 +41,10 @@ def test_struct_layout_matches_header():
 #include <stdio.h>
 #include "{HEADER}"
 int main(void) {{
-  printf("%zu %zu %zu %zu %zu\\n", sizeof(pa_verify_params), offsetof(pa_verify_params, workspace),
-         offsetof(pa_verify_params, stream), sizeof(pa_verify_plan),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(pa_verify_params),
+         offsetof(pa_verify_params, workspace), offsetof(pa_verify_params, stream),
+         offsetof(pa_verify_params, max_query_len), offsetof(pa_verify_params, tree_mask),
+         sizeof(pa_verify_plan), offsetof(pa_verify_plan, row_blocks),
          offsetof(pa_verify_plan, workspace_bytes));
   return 0;
 }}
@@ -55,8 +57,9 @@ int main(void) {{
         out = subprocess.run([os.path.join(d, "t")], capture_output=True, text=True).stdout.split()
     got = [int(x) for x in out]
     want = [ctypes.sizeof(pav.PaVerifyParams), pav.PaVerifyParams.workspace.offset,
-            pav.PaVerifyParams.stream.offset, ctypes.sizeof(pav.PaVerifyPlan),
-            pav.PaVerifyPlan.workspace_bytes.offset]
+            pav.PaVerifyParams.stream.offset, pav.PaVerifyParams.max_query_len.offset,
+            pav.PaVerifyParams.tree_mask.offset, ctypes.sizeof(pav.PaVerifyPlan),
+            pav.PaVerifyPlan.row_blocks.offset, pav.PaVerifyPlan.workspace_bytes.offset]
     assert got == want
 
 
@@ -96,6 +99,11 @@ def call(p, max_ctx=32771, u8=False, null=None):
     (dict(num_q_heads=128, num_kv_heads=8), pav.PA_ERR_UNSUPPORTED),  # G = 16
     (dict(kv_dtype=pav.PA_BF16), pav.PA_ERR_UNSUPPORTED),      # (f16, bf16) pair
     (dict(q_dtype=pav.PA_U8, kv_dtype=pav.PA_U8), pav.PA_ERR_UNSUPPORTED),
+    (dict(max_query_len=-1), pav.PA_ERR_INVALID_ARG),
+    (dict(max_query_len=17), pav.PA_ERR_UNSUPPORTED),          # beyond 16 new tokens
+    (dict(max_query_len=13), pav.PA_ERR_UNSUPPORTED),          # G=4: 52 rows > 48 at D=128
+    (dict(head_dim=256, max_query_len=5), pav.PA_ERR_UNSUPPORTED),   # 20 rows > 16 at D=256
+    (dict(tree_mask=FAKE, sliding_window=64), pav.PA_ERR_UNSUPPORTED),
 ])
 def test_host_errors(over, code):
     assert call(params(**over)) == code
@@ -131,8 +139,8 @@ def plan(max_ctx, cus=256, **over):
     return pav.pa_verify_make_plan(params(**over), max_ctx, cus)
 
 
-def check_plan_covers(pl, max_ctx, window=0, nseq=1, hkv=8, bs=16):
-    span = max_ctx if not window else min(max_ctx, window + 3 + 31)
+def check_plan_covers(pl, max_ctx, window=0, nseq=1, hkv=8, bs=16, tq=4):
+    span = max_ctx if not window else min(max_ctx, window + tq - 1 + 31)
     assert pl["span"] == span
     steps = -(-span // pl["keys_per_step"])
     S = pl["num_segments"]
@@ -172,11 +180,26 @@ def test_plan_ragged_batch_gives_the_longest_sequence_the_gpu():
     assert pl["grid"][0] * pl["grid"][1] * pl["grid"][2] <= 8 * 256
 
 
+@pytest.mark.parametrize("over,rb", [
+    (dict(), 1),                                               # G=4, T <= 3: 12 rows
+    (dict(num_tokens=8, max_query_len=4), 1),                  # 16 rows
+    (dict(num_tokens=8, max_query_len=8), 2),                  # 32 rows
+    (dict(num_tokens=12, max_query_len=12), 3),                # 48 rows
+    (dict(num_q_heads=64, num_tokens=4), 2),                   # G=8, default bound 4
+    (dict(head_dim=64, num_tokens=16, max_query_len=16), 4),   # 64 rows at D=64
+    (dict(head_dim=256, num_q_heads=16, num_kv_heads=4, kv_dtype=pav.PA_U8, num_tokens=8,
+          max_query_len=8), 2),                                # u8 D=256: 32 rows
+])
+def test_plan_row_blocks(over, rb):
+    pl = plan(32771, **over)
+    assert pl["row_blocks"] == rb
+
+
 def test_plan_window_and_forced_segments():
     pl = plan(51202, num_q_heads=32, num_kv_heads=16, head_dim=256, block_size=64,
               num_blocks=801, max_blocks_per_seq=801, sliding_window=1024, num_tokens=2,
               q_dtype=pav.PA_BF16, kv_dtype=pav.PA_BF16)
-    check_plan_covers(pl, 51202, window=1024, hkv=16, bs=64)
+    check_plan_covers(pl, 51202, window=1024, hkv=16, bs=64, tq=2)
     min_s = -(-1025 // ((1040 - 2) * 16 // 32))     # LDS block-id limit per segment
     for S in (1, 2, 7, 63, 5000):
         pl = plan(32771, num_segments=S)

@@ -199,7 +199,7 @@ def test_device_contract_violations_give_nan_and_status():
     bad.subsequence_begins = np.array([0, 2, 7], np.int32)
     bad.q = np.concatenate([base.q, base.q[:2]], axis=0)
     bad.num_tokens = 7
-    got = to_f64(run_gpu(bad))
+    got = to_f64(run_gpu(bad, max_query_len=4))
     assert pav.pa_verify_read_status() == pav.PA_ERR_DEVICE_CONTRACT
     assert np.all(np.isnan(got[2:]))
     assert np.max(np.abs(got[:2] - ref[:2])) <= 2e-3
@@ -217,6 +217,11 @@ def test_device_contract_violations_give_nan_and_status():
     got = to_f64(run_gpu(base, max_context_len=250))
     assert pav.pa_verify_read_status() == pav.PA_ERR_DEVICE_CONTRACT
     assert np.all(np.isnan(got[:2]))
+    # more new tokens than the max_query_len the call was planned for
+    got = to_f64(run_gpu(base, max_query_len=2))
+    assert pav.pa_verify_read_status() == pav.PA_ERR_DEVICE_CONTRACT
+    assert np.all(np.isnan(got[2:]))
+    assert np.max(np.abs(got[:2] - ref[:2])) <= 2e-3
 
 
 def test_graph_capture_replays_match_eager():
@@ -277,3 +282,70 @@ def test_prepared_call_matches_the_plain_call():
             pc(stream=st)
             torch.cuda.synchronize()
             assert np.array_equal(to_f64(out), want), case.name
+
+
+# ---------------------------------------------------------------------------
+# More than 16 stacked rows (several 16-row MFMA blocks) and tree verify
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T", [5, 8, 12])
+def test_wide_T_gqa4_d128(T):
+    """8k context, GQA 4, D 128: 20, 32 and 48 stacked rows (2, 2, 3 row blocks)."""
+    _full(pi.build_case([2, 8192, T, 0], [8192], [T], num_q_heads=32, num_kv_heads=8,
+                        head_dim=128, block_size=16, poison=True, name=f"wide_d128_T{T}"))
+
+
+def test_wide_T_other_shapes():
+    for k, (D, G, T, kv, qd, bs) in enumerate([
+            (64, 4, 16, pi.BF16, pi.BF16, 32),      # 64 rows: 4 row blocks
+            (64, 8, 6, pi.F16, pi.F16, 64),         # 48 rows
+            (128, 8, 4, pi.BF16, pi.BF16, 16),      # 32 rows at G = 8
+            (256, 2, 8, pi.BF16, pi.BF16, 64),      # 16 rows, head 256 (one block)
+            (256, 4, 8, pi.U8, pi.F16, 16),         # u8 head 256: 32 rows
+            (128, 4, 9, pi.U8, pi.F16, 32)]):       # u8, 36 rows
+        case = pi.build_case([700, k], [int(1000 + 333 * k)], [T], num_q_heads=G * 2,
+                             num_kv_heads=2, head_dim=D, block_size=bs, q_dtype=qd, kv_dtype=kv,
+                             spare_blocks=2, poison=True, name=f"wide_D{D}_G{G}_T{T}_kv{kv}")
+        _full(case)
+
+
+def test_wide_T_ragged_and_short():
+    rng = np.random.default_rng(123)
+    for rep in range(3):
+        Ls = rng.integers(0, 2500, size=5).tolist()
+        Ts = rng.integers(1, 11, size=5).tolist()
+        case = pi.build_case([710, rep], Ls, Ts, num_q_heads=16, num_kv_heads=4, head_dim=128,
+                             block_size=16, q_dtype=pi.BF16, kv_dtype=pi.BF16, spare_blocks=3,
+                             poison=True, name=f"wide_ragged{rep}")
+        _full(case, rounding_aware=True)
+
+
+@pytest.mark.parametrize("T", [4, 9, 16])
+def test_tree_verify(T):
+    """Random draft trees: rows see the past and their ancestors."""
+    G = 4 if T <= 12 else 2
+    case = pi.build_case([720, T], [8000], [T], num_q_heads=8 * G, num_kv_heads=8,
+                         head_dim=128, block_size=16, poison=True, tree=True,
+                         name=f"tree_T{T}")
+    _full(case)
+
+
+def test_tree_verify_shapes():
+    for k, (D, G, T, kv, qd, bs, Ls) in enumerate([
+            (64, 2, 16, pi.F16, pi.F16, 16, [0, 40, 700]),
+            (128, 4, 9, pi.BF16, pi.BF16, 32, [3000]),
+            (256, 2, 8, pi.BF16, pi.BF16, 64, [5, 2000]),
+            (256, 4, 8, pi.U8, pi.F16, 16, [1500]),
+            (128, 8, 5, pi.U8, pi.BF16, 64, [31, 900])]):
+        case = pi.build_case([730, k], Ls, [T] * len(Ls), num_q_heads=G * 2, num_kv_heads=2,
+                             head_dim=D, block_size=bs, q_dtype=qd, kv_dtype=kv, spare_blocks=2,
+                             poison=True, tree=True, name=f"tree_D{D}_G{G}_T{T}_kv{kv}")
+        _full(case, rounding_aware=True)
+
+
+def test_chain_tree_is_bitwise_causal():
+    for case in (pi.config2(8192, 4, rep=3), pi.config3(3000, 3, rep=3)):
+        causal = to_f64(run_gpu(case))
+        chain = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+        chain.tree_mask = pi.tree_masks([list(range(-1, T - 1)) for T in case.Ts])
+        assert np.array_equal(to_f64(run_gpu(chain)), causal), case.name
+
