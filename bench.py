@@ -41,6 +41,7 @@ def workloads():
     return {
         "gqa4_d128_f16_L32768": lambda T: pi.config2(32768, T),
         "gqa4_d128_f16_L8192": lambda T: pi.config2(8192, T),
+        "gqa4_d128_f16_L32768_tree": lambda T: pi.config2(32768, T, tree=True),
         "u8kv_d256_L32768": lambda T: pi.config3(32768, T),
         "swa_pair_global_L32768": lambda T: pi.config4(32768, window=0, T=T),
         "swa_pair_global_L51200": lambda T: pi.config4(51200, window=0, T=T),
@@ -99,16 +100,18 @@ class Runner:
         # the C call, so eager launches keep pace with the GPU
         c = case
         self.prepared = []
+        opts = dict(sliding_window=c.sliding_window, max_query_len=max(c.Ts),
+                    tree_mask=self.dev.get("tree_mask"))
         for d in self.pools:
             if c.kv_dtype == 2:
                 pc = pav.prepare_forward_u8(d["q"], d["k_cache"], d["v_cache"], d["k_scale_zp"],
                                             d["v_scale_zp"], d["block_tables"], d["past_lens"],
                                             d["subsequence_begins"], c.max_context_len, c.scale,
-                                            self.out, sliding_window=c.sliding_window)
+                                            self.out, **opts)
             else:
                 pc = pav.prepare_forward(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
                                          d["past_lens"], d["subsequence_begins"], c.max_context_len,
-                                         c.scale, self.out, sliding_window=c.sliding_window)
+                                         c.scale, self.out, **opts)
             self.prepared.append(pc)
 
     def call(self, i, prof=None, stream=None):
@@ -260,7 +263,7 @@ def main():
 
     t1 = None
     if not args.no_t1 and args.T != 1 and args.workload.startswith("gqa4"):
-        case1 = mk(1)
+        case1 = workloads()[args.workload.replace("_tree", "")](1)
         run1 = Runner(case1)
         us1, _ = run1.time_graph(args.steps, args.warmup, args.repeats)
         _, us1_kernel, _ = run1.time(args.steps, args.warmup, args.repeats)
@@ -291,6 +294,7 @@ def main():
                    "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads,
                    "head_dim": case.head_dim, "block_size": case.block_size,
                    "sliding_window": case.sliding_window, "kv_dtype": dtype,
+                   "tree_verify": case.tree_mask is not None,
                    "kv_bytes_per_call": kv, "pool_copies": copies},
         "us_per_call": round(us, 3),
         "us_per_call_spread": [round(x, 3) for x in spread],

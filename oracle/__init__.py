@@ -57,6 +57,21 @@ def build(src: str = SRC, out: str = LIB, extra_flags=()) -> str:
     return out
 
 
+class _AppendArgs(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32), ("new_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("k_scale_zp", ctypes.c_void_p), ("v_scale_zp", ctypes.c_void_p),
+        ("block_tables", ctypes.c_void_p), ("past_lens", ctypes.c_void_p),
+        ("subsequence_begins", ctypes.c_void_p),
+    ]
+
+
 class Oracle:
     """A loaded oracle library (the default one, or a test-built variant)."""
 
@@ -66,6 +81,43 @@ class Oracle:
         self.lib.pa_oracle_forward.argtypes = [ctypes.POINTER(_Args), ctypes.c_void_p]
         self.lib.pa_oracle_forward.restype = ctypes.c_int
         self.lib.pa_oracle_num_threads.restype = ctypes.c_int
+        self.lib.pa_oracle_kv_append.argtypes = [ctypes.POINTER(_AppendArgs)]
+        self.lib.pa_oracle_kv_append.restype = ctypes.c_int
+        self.lib.pa_oracle_quantize_row.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                                    ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.pa_oracle_quantize_row.restype = None
+
+    def quantize_row(self, x):
+        """(codes uint8 [D], scale f16 bits, zero-point f16 bits) of one float32 row."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        codes = np.zeros(x.shape[0], np.uint8)
+        sb = np.zeros(1, np.uint16)
+        zb = np.zeros(1, np.uint16)
+        self.lib.pa_oracle_quantize_row(x.ctypes.data, x.shape[0], codes.ctypes.data,
+                                        sb.ctypes.data, zb.ctypes.data)
+        return codes, int(sb[0]), int(zb[0])
+
+    def kv_append(self, case, k_new, v_new, new_dtype):
+        """Copies of the case's caches (and u8 scale/zero-point arrays) with the
+        new tokens written at positions past_len + i: (status, k, v, ksz, vsz)."""
+        k = np.array(case.k_cache, copy=True)
+        v = np.array(case.v_cache, copy=True)
+        u8 = case.kv_dtype == U8
+        ksz = np.array(case.k_scale_zp, copy=True) if u8 else None
+        vsz = np.array(case.v_scale_zp, copy=True) if u8 else None
+        kn = np.ascontiguousarray(k_new)
+        vn = np.ascontiguousarray(v_new)
+        bt = np.ascontiguousarray(case.block_tables, np.int32)
+        pl = np.ascontiguousarray(case.past_lens, np.int32)
+        sb = np.ascontiguousarray(case.subsequence_begins, np.int32)
+        a = _AppendArgs(case.num_seqs, case.num_tokens, case.num_kv_heads, case.head_dim,
+                        case.block_size, case.num_blocks, case.max_blocks_per_seq, new_dtype,
+                        case.kv_dtype, kn.ctypes.data, vn.ctypes.data, k.ctypes.data, v.ctypes.data,
+                        None if ksz is None else ksz.ctypes.data,
+                        None if vsz is None else vsz.ctypes.data,
+                        bt.ctypes.data, pl.ctypes.data, sb.ctypes.data)
+        st = self.lib.pa_oracle_kv_append(ctypes.byref(a))
+        return int(st), k, v, ksz, vsz
 
     def num_threads(self) -> int:
         return int(self.lib.pa_oracle_num_threads())

@@ -271,3 +271,150 @@ int pa_oracle_forward(const pa_oracle_args* a, double* out) {
   }
   return bad ? PA_ORACLE_ERR_ARG : PA_ORACLE_OK;
 }
+
+/* ---------------------------------------------------------------------------
+ * Appending the new tokens, with u8 quantisation for a u8 cache.
+ *
+ * The cache holds u8 KV with f16 compute (OpenVINO #38153, "Step-by-step
+ * reproduction"), quantised per token per KV head, asymmetric, with an f16
+ * scale and an f16 zero point.  The pages fix no formula; the reading taken:
+ * over the row's D values in fp32,
+ *     scale = (max - min) / 255,  rounded to f16 -> s
+ *     zero point = -min / s,      rounded to f16 -> z
+ *     code = clamp(round_half_even(x / s + z), 0, 255)
+ * every step an IEEE fp32 operation; a constant row (max == min), or one
+ * whose scale rounds to 0 in f16, takes s = 1 and z = f16(-min).
+ * ------------------------------------------------------------------------- */
+
+/* float32 -> IEEE binary16 bits, round to nearest even (finite inputs; values
+ * beyond the f16 range become infinity). */
+static uint16_t f32_to_f16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  const uint32_t a = u & 0x7fffffffu;
+  if (a >= 0x7f800000u) return (uint16_t)(sign | 0x7c00u | (a > 0x7f800000u ? 0x200u : 0u));
+  const double v = (double)fabsf(f);              /* exact */
+  if (v >= 65520.0) return (uint16_t)(sign | 0x7c00u);   /* rounds past the largest finite */
+  /* scale so that one unit is the f16 spacing at v, round half to even */
+  int e;
+  frexp(v, &e);                                   /* v = m * 2^e, m in [0.5, 1) */
+  int q = e - 11;                                 /* spacing 2^(e-11) for normals */
+  if (q < -24) q = -24;                           /* subnormal spacing */
+  const double t = ldexp(v, -q);
+  double r = floor(t);
+  const double frac = t - r;
+  if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+  const double rv = ldexp(r, q);                  /* rounded value, exact */
+  if (rv == 0.0) return sign;
+  int e2;
+  frexp(rv, &e2);
+  if (e2 - 1 < -14) return (uint16_t)(sign | (uint16_t)ldexp(rv, 24));   /* subnormal */
+  const int exp16 = e2 - 1 + 15;
+  const uint32_t man = (uint32_t)(ldexp(rv, 11 - e2) - 1024.0);
+  return (uint16_t)(sign | (uint16_t)(exp16 << 10) | (uint16_t)man);
+}
+
+static float f16_to_f32(uint16_t b) { return (float)dec_f16(b); }
+
+void pa_oracle_quantize_row(const float* x, int D, uint8_t* codes, uint16_t* scale_bits,
+                            uint16_t* zp_bits) {
+  float mn = x[0], mx = x[0];
+  for (int d = 1; d < D; ++d) {
+    if (x[d] < mn) mn = x[d];
+    if (x[d] > mx) mx = x[d];
+  }
+  uint16_t sb = 0x3c00u;                          /* 1.0 */
+  uint16_t zb;
+  const float range = mx - mn;
+  const uint16_t s_try = f32_to_f16(range / 255.0f);
+  if (mx != mn && s_try != 0) {
+    sb = s_try;
+    zb = f32_to_f16(-mn / f16_to_f32(sb));
+  } else {
+    zb = f32_to_f16(-mn);
+  }
+  const float s = f16_to_f32(sb), z = f16_to_f32(zb);
+  for (int d = 0; d < D; ++d) {
+    const float y = x[d] / s + z;
+    float r = rintf(y);                           /* default mode: nearest, ties to even */
+    if (r < 0.0f) r = 0.0f;
+    if (r > 255.0f) r = 255.0f;
+    codes[d] = (uint8_t)r;
+  }
+  *scale_bits = sb;
+  *zp_bits = zb;
+}
+
+int pa_oracle_kv_append(const pa_oracle_append_args* a) {
+  if (!a || !a->k_new || !a->v_new || !a->k_cache || !a->v_cache || !a->block_tables ||
+      !a->past_lens || !a->subsequence_begins)
+    return PA_ORACLE_ERR_ARG;
+  const int u8 = a->kv_dtype == PA_ORACLE_U8;
+  if (a->new_dtype != PA_ORACLE_F16 && a->new_dtype != PA_ORACLE_BF16) return PA_ORACLE_ERR_ARG;
+  if (!u8 && a->kv_dtype != a->new_dtype) return PA_ORACLE_ERR_ARG;
+  if (u8 && (!a->k_scale_zp || !a->v_scale_zp)) return PA_ORACLE_ERR_ARG;
+  const int D = a->head_dim, bs = a->block_size, Hkv = a->num_kv_heads;
+  if (bs % 16 != 0 || D % (u8 ? 64 : 32) != 0) return PA_ORACLE_ERR_ARG;
+  if (a->subsequence_begins[0] != 0 || a->subsequence_begins[a->num_seqs] != a->num_tokens)
+    return PA_ORACLE_ERR_META;
+  float* row = (float*)malloc(sizeof(float) * (size_t)D);
+  uint8_t* codes = (uint8_t*)malloc((size_t)D);
+  if (!row || !codes) {
+    free(row);
+    free(codes);
+    return PA_ORACLE_ERR_ARG;
+  }
+  int rc = PA_ORACLE_OK;
+  for (int s = 0; s < a->num_seqs && rc == PA_ORACLE_OK; ++s) {
+    const int b0 = a->subsequence_begins[s], T = a->subsequence_begins[s + 1] - b0;
+    const int L = a->past_lens[s];
+    if (T < 0 || L < 0) {
+      rc = PA_ORACLE_ERR_META;
+      break;
+    }
+    for (int i = 0; i < T; ++i) {
+      const int pos = L + i;
+      if (pos / bs >= a->max_blocks_per_seq) {
+        rc = PA_ORACLE_ERR_META;
+        break;
+      }
+      const int blk = a->block_tables[(size_t)s * a->max_blocks_per_seq + pos / bs];
+      if (blk < 0 || blk >= a->num_blocks) {
+        rc = PA_ORACLE_ERR_META;
+        break;
+      }
+      const int slot = pos % bs;
+      for (int g = 0; g < Hkv; ++g) {
+        const size_t src = ((size_t)(b0 + i) * Hkv + g) * D;
+        const size_t page = ((size_t)blk * Hkv + g) * (size_t)bs * D;
+        const size_t srow = ((size_t)blk * Hkv + g) * bs + slot;
+        for (int kv = 0; kv < 2; ++kv) {
+          const uint16_t* in = (const uint16_t*)(kv ? a->v_new : a->k_new);
+          void* cache = kv ? a->v_cache : a->k_cache;
+          if (!u8) {
+            for (int d = 0; d < D; ++d) {
+              const size_t off = page + (kv ? v_offset(slot, d, D, 0) : k_offset(slot, d, D, 0));
+              ((uint16_t*)cache)[off] = in[src + d];
+            }
+            continue;
+          }
+          for (int d = 0; d < D; ++d) row[d] = (float)dec_elem(in, src + d, a->new_dtype);
+          uint16_t sb, zb;
+          pa_oracle_quantize_row(row, D, codes, &sb, &zb);
+          for (int d = 0; d < D; ++d) {
+            const size_t off = page + (kv ? v_offset(slot, d, D, 1) : k_offset(slot, d, D, 1));
+            ((uint8_t*)cache)[off] = codes[d];
+          }
+          uint16_t* sz = kv ? a->v_scale_zp : a->k_scale_zp;
+          sz[2 * srow + 0] = sb;
+          sz[2 * srow + 1] = zb;
+        }
+      }
+    }
+  }
+  free(row);
+  free(codes);
+  return rc;
+}
+

@@ -22,6 +22,10 @@ What pins what:
   * gqa         — G > 1 equals G = 1 with each KV head duplicated.
   * u8          — the u8 path equals the fp64 path fed the dequantised values.
   * ragged      — a ragged batch equals each sequence run alone.
+  * append      — writing the new tokens: the C quantiser against the input
+                  generator's numpy one (bit for bit) and hand rows; f16/bf16
+                  appends restore a blanked cache exactly; u8 appends hold
+                  each row's codes and (scale, zero point) within half a step.
   * tree        — tree verify against torch SDPA with a dense mask built by
                   walking each draft tree's parent pointers; the chain tree
                   equals the causal rows bitwise; a mask without the row's own
@@ -385,8 +389,97 @@ def pin_tree(orc):
         assert np.array_equal(orc.forward(case, tree_mask=chain), causal), case.name
 
 
+def _blank_new_tokens(case, rng):
+    """The new tokens' K/V as [num_tokens, Hkv, D] codes taken from the case's
+    cache, and a copy of the case whose cache holds other values there."""
+    u8 = case.kv_dtype == pi.U8
+    kl, vl = case.logical_pages()
+    bs = case.block_size
+    shape = (case.num_tokens, case.num_kv_heads, case.head_dim)
+    kn = np.zeros(shape, kl.dtype)
+    vn = np.zeros(shape, vl.dtype)
+    kb, vb = kl.copy(), vl.copy()
+    for s in range(case.num_seqs):
+        L, b0 = int(case.past_lens[s]), int(case.subsequence_begins[s])
+        for i in range(case.Ts[s]):
+            blk = case.block_tables[s, (L + i) // bs]
+            slot = (L + i) % bs
+            kn[b0 + i], vn[b0 + i] = kl[blk, :, slot], vl[blk, :, slot]
+            kb[blk, :, slot] = rng.integers(0, 1 << 14, size=kb[blk, :, slot].shape)
+            vb[blk, :, slot] = rng.integers(0, 1 << 14, size=vb[blk, :, slot].shape)
+    blank = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+    blank.k_cache = pi.tile_k(kb, u8).reshape(case.k_cache.shape)
+    blank.v_cache = pi.tile_v(vb, u8).reshape(case.v_cache.shape)
+    return kn, vn, blank
+
+
+def pin_append(orc):
+    rng = np.random.default_rng(23)
+    # the quantiser: the generator's independent numpy version of the same
+    # reading, bit for bit, on rows of many scales, constant rows included
+    for t in range(400):
+        D = int(rng.choice([64, 128, 256]))
+        x = (rng.standard_normal(D) * rng.choice([1e-4, 0.1, 1.0, 50.0, 3000.0])).astype(np.float32)
+        if t % 40 == 0:
+            x[:] = x[0]
+        x = x.astype(np.float16).astype(np.float32)
+        c, sb, zb = orc.quantize_row(x)
+        u, s16, z16 = pi.quantize_u8(x[None])
+        assert np.array_equal(c, u[0]) and sb == int(s16[0]) and zb == int(z16[0]), t
+    # hand rows: the integers 0..255 are their own codes (scale 1, zero point
+    # -0.0 = -min); a constant row maps to code 0 with zero point -c
+    c, sb, zb = orc.quantize_row(np.arange(256, dtype=np.float32))
+    assert np.array_equal(c, np.arange(256)) and sb == 0x3C00 and zb == 0x8000
+    c, sb, zb = orc.quantize_row(np.full(64, 3.5, np.float32))
+    assert np.all(c == 0) and sb == 0x3C00 and zb == 0xC300          # -3.5
+    # f16/bf16 caches: appending the new tokens' values restores the cache
+    # exactly, and the attention over it
+    for k, (kv, D, bs) in enumerate([(pi.F16, 64, 16), (pi.BF16, 128, 32), (pi.F16, 32, 64)]):
+        case = pi.build_case([800, k], [37, 0, 70], [3, 4, 1], num_q_heads=4, num_kv_heads=2,
+                             head_dim=D, block_size=bs, q_dtype=kv, kv_dtype=kv, spare_blocks=2)
+        kn, vn, blank = _blank_new_tokens(case, rng)
+        st, k2, v2, _, _ = orc.kv_append(blank, kn, vn, kv)
+        assert st == 0
+        assert np.array_equal(k2, case.k_cache) and np.array_equal(v2, case.v_cache), k
+        done = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+        done.k_cache, done.v_cache = k2, v2
+        assert np.array_equal(orc.forward(done), orc.forward(case)), k
+    # u8 caches: each appended row holds the codes of its f16 values, its
+    # (scale, zero point) and nothing else changes
+    for k, (D, bs) in enumerate([(64, 16), (128, 32), (256, 16)]):
+        case = pi.build_case([810, k], [20, 300], [4, 2], num_q_heads=4, num_kv_heads=2,
+                             head_dim=D, block_size=bs, q_dtype=pi.F16, kv_dtype=pi.U8,
+                             spare_blocks=1)
+        T = case.num_tokens
+        kf = rng.standard_normal((T, 2, D)).astype(np.float16)
+        vf = (rng.standard_normal((T, 2, D)) * 4).astype(np.float16)
+        st, k2, v2, ks2, vs2 = orc.kv_append(case, kf.view(np.uint16), vf.view(np.uint16), pi.F16)
+        assert st == 0
+        kl0, vl0 = case.logical_pages()
+        flat = (case.num_blocks, 2, bs * D)
+        kl = pi.untile_k(k2.reshape(flat), bs, D, True)
+        vl = pi.untile_v(v2.reshape(flat), bs, D, True)
+        touched = np.zeros((case.num_blocks, 2, bs), bool)
+        for s_ in range(case.num_seqs):
+            L, b0 = int(case.past_lens[s_]), int(case.subsequence_begins[s_])
+            for i in range(case.Ts[s_]):
+                blk, slot = case.block_tables[s_, (L + i) // bs], (L + i) % bs
+                touched[blk, :, slot] = True
+                for g in range(2):
+                    for new, lg, sz in ((kf, kl, ks2), (vf, vl, vs2)):
+                        u, sb_, zb_ = pi.quantize_u8(new[b0 + i, g].astype(np.float32)[None])
+                        assert np.array_equal(lg[blk, g, slot], u[0])
+                        assert sz[blk, g, slot, 0] == sb_[0] and sz[blk, g, slot, 1] == zb_[0]
+                        sc = float(pi.f16_bits_to_f32(sb_)[0])
+                        zp = float(pi.f16_bits_to_f32(zb_)[0])
+                        deq = (u[0].astype(np.float64) - zp) * sc
+                        assert np.max(np.abs(deq - new[b0 + i, g].astype(np.float64))) <= 0.51 * sc
+        assert np.array_equal(kl[~touched], kl0[~touched]) and np.array_equal(vl[~touched], vl0[~touched])
+        assert np.array_equal(ks2[~touched], case.k_scale_zp[~touched])
+
+
 ALL_PINS = {
     "sdpa": pin_sdpa, "hand": pin_hand, "closed": pin_closed, "rows": pin_rows,
     "permutation": pin_permutation, "window": pin_window, "gqa": pin_gqa, "u8": pin_u8,
-    "ragged": pin_ragged, "tree": pin_tree,
+    "ragged": pin_ragged, "tree": pin_tree, "append": pin_append,
 }

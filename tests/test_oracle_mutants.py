@@ -24,6 +24,14 @@ MUTANTS = [
     ("tree_self_not_implied", [("return j == i || ((a->tree_mask[n] >> j) & 1u);",
                                 "return ((a->tree_mask[n] >> j) & 1u);")]),
     ("tree_hides_the_past", [("if (t < L) return 1;", "if (t < L) return 0;")]),
+    ("quantise_floor", [("float r = rintf(y);", "float r = floorf(y);")]),
+    ("quantise_no_clamp", [("if (r > 255.0f) r = 255.0f;", "if (r > 255.0f) r = r - 256.0f;")]),
+    ("quantise_zp_sign", [("zb = f32_to_f16(-mn / f16_to_f32(sb));", "zb = f32_to_f16(mn / f16_to_f32(sb));")]),
+    ("quantise_scale_unrounded", [("const float s = f16_to_f32(sb), z = f16_to_f32(zb);",
+                                   "const float s = range / 255.0f + (mx == mn), z = f16_to_f32(zb);")]),
+    ("append_slot_shifted", [("const int slot = pos % bs;", "const int slot = (pos + 1) % bs;")]),
+    ("append_scale_zp_swapped", [("sz[2 * srow + 0] = sb;", "sz[2 * srow + 0] = zb;"),
+                                 ("sz[2 * srow + 1] = zb;", "sz[2 * srow + 1] = sb;")]),
     ("tree_first_row_mask", [("return j == i || ((a->tree_mask[n] >> j) & 1u);",
                               "return j == i || ((a->tree_mask[n - i] >> j) & 1u);")]),
     ("v_read_in_k_layout", [("const size_t vidx = page + v_offset(slot, d, D, u8);",
@@ -52,7 +60,8 @@ MUTANTS = [
                           "page + k_offset(slot, D - 1 - d, D, u8), row);")]),
 ]
 
-PIN_ORDER = ["hand", "closed", "rows", "window", "gqa", "u8", "permutation", "ragged", "sdpa", "tree"]
+PIN_ORDER = ["hand", "closed", "rows", "window", "gqa", "u8", "permutation", "ragged", "sdpa", "tree",
+             "append"]
 
 
 def _source():
