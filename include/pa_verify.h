@@ -187,6 +187,33 @@ int pa_verify_forward_u8(const void* q, const uint8_t* k_cache, const uint8_t* v
                          const int32_t* subsequence_begins, int32_t max_context_len,
                          float scale, void* out, const pa_verify_params* p);
 
+/* Write the new tokens' K and V into their cache slots, the step before the
+ * forward call reads them (OpenVINO issue #38153, "Step-by-step reproduction":
+ * the op's cache holds the new tokens, u8 with f16 compute).  Token b_s + i
+ * of sequence s goes to position L_s + i: block
+ * block_tables[s][(L_s + i) / block_size], slot (L_s + i) % block_size, in
+ * the tiled page layout above.  k_new, v_new: device [num_tokens, Hkv, D] in
+ * p->q_dtype.  Uses p's sizes, dtypes, max_query_len, stream and the status
+ * word at the head of p->workspace (>= 4 bytes); not max_context_len.
+ * Device-side contract violations (as for the forward call, with positions
+ * bounded by max_blocks_per_seq * block_size) set the status word and write
+ * nothing for that token.  Enqueues one kernel; enqueue it before the forward
+ * call on the same stream. */
+int pa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                 const int32_t* block_tables, const int32_t* past_lens,
+                 const int32_t* subsequence_begins, const pa_verify_params* p);
+
+/* The same into a u8 cache: each (token, KV head) vector x of D values is
+ * quantised in IEEE fp32 steps, s = f16(range / 255), z = f16(-min / s),
+ * code = clamp(round_half_even(x / s + z), 0, 255) (a constant row, or one
+ * whose scale rounds to 0, takes s = 1, z = f16(-min)), and (s, z) is stored
+ * in k_scale_zp / v_scale_zp.  Inputs must be finite and within the f16
+ * range. */
+int pa_kv_append_u8(const void* k_new, const void* v_new, uint8_t* k_cache, uint8_t* v_cache,
+                    void* k_scale_zp, void* v_scale_zp, const int32_t* block_tables,
+                    const int32_t* past_lens, const int32_t* subsequence_begins,
+                    const pa_verify_params* p);
+
 /* Synchronise p->stream, read the sticky device status word from
  * p->workspace into *device_status (PA_OK or PA_ERR_DEVICE_CONTRACT) and clear
  * it.  For tests and debugging; it blocks the host. */

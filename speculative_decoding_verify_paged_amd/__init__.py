@@ -28,7 +28,8 @@ PA_F16, PA_BF16, PA_U8 = 0, 1, 2
 
 # every symbol include/pa_verify.h declares
 EXPORTS = ("pa_verify_make_plan", "pa_verify_workspace_bytes", "pa_verify_forward",
-           "pa_verify_forward_u8", "pa_verify_read_status", "pa_verify_status_string")
+           "pa_verify_forward_u8", "pa_kv_append", "pa_kv_append_u8", "pa_verify_read_status",
+           "pa_verify_status_string")
 
 
 class PaVerifyParams(ctypes.Structure):
@@ -92,6 +93,10 @@ def lib():
                 L.pa_verify_forward_u8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                                    ctypes.c_float, vp, P]
                 L.pa_verify_forward_u8.restype = ctypes.c_int
+                L.pa_kv_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, P]
+                L.pa_kv_append.restype = ctypes.c_int
+                L.pa_kv_append_u8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, P]
+                L.pa_kv_append_u8.restype = ctypes.c_int
                 L.pa_verify_read_status.argtypes = [P, ctypes.POINTER(i32)]
                 L.pa_verify_read_status.restype = ctypes.c_int
                 L.pa_verify_status_string.argtypes = [ctypes.c_int]
@@ -349,3 +354,69 @@ def prepare_forward_u8(q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables
                  subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
                  workspace, stream, None, prepare=True, max_query_len=max_query_len,
                  tree_mask=tree_mask)
+
+
+def _append(u8, k_new, v_new, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
+            subsequence_begins, max_query_len, stream):
+    torch = _torch()
+    dev = k_new.device
+    _check(k_new, "k_new", ndim=3, device=dev)
+    _check(v_new, "v_new", ndim=3, device=dev)
+    if v_new.shape != k_new.shape or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new and v_new must have the same shape and dtype")
+    _check(k_cache, "k_cache", ndim=4, device=dev)
+    _check(v_cache, "v_cache", ndim=4, device=dev)
+    for n, t in (("block_tables", block_tables), ("past_lens", past_lens),
+                 ("subsequence_begins", subsequence_begins)):
+        _check(t, n, dtype=torch.int32, device=dev)
+    num_tokens, Hkv, D = k_new.shape
+    nb, Hkv2, bs, D2 = k_cache.shape
+    if (Hkv2, D2) != (Hkv, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("caches must be [nb, Hkv, bs, D] matching k_new's Hkv and D")
+    if u8:
+        for n, t in (("k_scale_zp", k_scale_zp), ("v_scale_zp", v_scale_zp)):
+            _check(t, n, dtype=torch.float16, device=dev)
+            if tuple(t.shape) != (nb, Hkv, bs, 2):
+                raise ValueError(f"{n} must be [nb, Hkv, bs, 2] float16")
+    num_seqs = past_lens.shape[0]
+    if block_tables.shape[0] != num_seqs or subsequence_begins.shape[0] != num_seqs + 1:
+        raise ValueError("block_tables / subsequence_begins do not match past_lens")
+    params = make_params(num_seqs=num_seqs, num_tokens=num_tokens, num_q_heads=Hkv,
+                         num_kv_heads=Hkv, head_dim=D, block_size=bs, num_blocks=nb,
+                         max_blocks_per_seq=block_tables.shape[1], q_dtype=_dtype_code(k_new),
+                         kv_dtype=_dtype_code(k_cache), max_query_len=int(max_query_len))
+    params.stream = (torch.cuda.current_stream(dev).cuda_stream if stream is None else stream) or None
+    with torch.cuda.device(dev):
+        ws = workspace(256, dev)
+    params.workspace = ws.data_ptr()
+    params.workspace_bytes = ws.numel()
+    L = lib()
+    if u8:
+        rc = L.pa_kv_append_u8(k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+                               v_cache.data_ptr(), k_scale_zp.data_ptr(), v_scale_zp.data_ptr(),
+                               block_tables.data_ptr(), past_lens.data_ptr(),
+                               subsequence_begins.data_ptr(), ctypes.byref(params))
+    else:
+        rc = L.pa_kv_append(k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+                            v_cache.data_ptr(), block_tables.data_ptr(), past_lens.data_ptr(),
+                            subsequence_begins.data_ptr(), ctypes.byref(params))
+    if rc != PA_OK:
+        raise PaVerifyError(rc)
+
+
+def pa_kv_append(k_new, v_new, k_cache, v_cache, block_tables, past_lens, subsequence_begins, *,
+                 max_query_len: int = 0, stream: Optional[int] = None):
+    """Write the new tokens' K/V ([num_tokens, Hkv, D], f16 or bf16) into an
+    f16/bf16 cache of the same dtype at positions past_len + i (in place)."""
+    _append(False, k_new, v_new, k_cache, v_cache, None, None, block_tables, past_lens,
+            subsequence_begins, max_query_len, stream)
+
+
+def pa_kv_append_u8(k_new, v_new, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables,
+                    past_lens, subsequence_begins, *, max_query_len: int = 0,
+                    stream: Optional[int] = None):
+    """The same into a u8 cache: each (token, KV head) row is quantised and its
+    f16 (scale, zero point) written to k_scale_zp / v_scale_zp (in place)."""
+    _append(True, k_new, v_new, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
+            subsequence_begins, max_query_len, stream)
+

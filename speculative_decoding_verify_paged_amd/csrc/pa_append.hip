@@ -1,0 +1,158 @@
+// pa_append.hip — writing the T new tokens of each sequence into their paged
+// cache slots, the step just before the verify attention reads them.  Token
+// b_s + i of sequence s goes to position L_s + i: block
+// block_tables[s][(L_s + i) / block_size], slot (L_s + i) % block_size, in the
+// tiled page layout of the attention kernels.  For a u8 cache each (token,
+// KV head) vector is quantised on the way in: the cache holds u8 KV with f16
+// compute (OpenVINO issue #38153 "[GPU] PagedAttention with 2-4 query tokens
+// per sequence (speculative decoding verify) is ~8x slower than single-token
+// decode", section "Step-by-step reproduction"), per token per KV head,
+// asymmetric, f16 scale and zero point.  The steps are IEEE fp32 operations
+// in a fixed order, so codes are reproducible bit for bit:
+//   s = f16(range / 255), z = f16(-min / s), code = clamp(rne(x / s + z), 0, 255)
+// (a constant row, or one whose scale rounds to 0, takes s = 1, z = f16(-min)).
+#include "pa_kernels_impl.h"
+
+namespace pav {
+
+namespace {
+
+// Offsets of element (slot, d) inside one (block, KV head) page: the tiled
+// orders the segment kernel's loads assume (sub-tiles of 16 slots).
+__device__ __forceinline__ int k_off(int slot, int d, int D, bool u8) {
+  const int st = slot / 16, m = slot % 16;
+  if (u8) return (((st * (D / 64) + d / 64) * 4 + (d % 64) / 16) * 16 + m) * 16 + d % 16;
+  return (((st * (D / 32) + d / 32) * 4 + (d % 32) / 8) * 16 + m) * 8 + d % 8;
+}
+__device__ __forceinline__ int v_off(int slot, int d, int D, bool u8) {
+  const int st = slot / 16, qq = (slot % 16) / 4;
+  if (u8) return ((((st * (D / 64) + d / 64) * 4 + qq) * 16 + d % 16) * 4 + (d % 64) / 16) * 4 + slot % 4;
+  return ((((st * (D / 32) + d / 32) * 4 + qq) * 16 + d % 16) * 2 + (d % 32) / 16) * 4 + slot % 4;
+}
+
+template <int QT>
+__device__ __forceinline__ float in_value(const uint16_t* p) {
+  const uint16_t b = *p;
+  if constexpr (QT == kF16) return (float)__builtin_bit_cast(_Float16, b);
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+__device__ __forceinline__ float wave_min(float v) {
+  for (int m = 1; m < kWave; m <<= 1) v = fminf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  for (int m = 1; m < kWave; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+
+}  // namespace
+
+// One wavefront per (token, KV head, K or V).  Lane l handles d = l + 64*e.
+template <int QT, int KV, int D>
+__global__ __launch_bounds__(kWave) void pa_append(AppendArgs a) {
+  constexpr bool U8 = KV == kU8;
+  constexpr int E = D / kWave > 0 ? D / kWave : 1;      // elements per lane
+  const int lane = threadIdx.x;
+  const int n = blockIdx.x, g = blockIdx.y, kv = blockIdx.z;
+
+  // the token's sequence, and subsequence_begins checked on the way (as the
+  // combine kernel does): it starts at 0, never decreases, ends at num_tokens
+  bool ok = true;
+  int s = -1;
+  for (int b = 0; b < a.num_seqs; b += kWave) {
+    const int k = b + lane;
+    const int nx = k < a.num_seqs ? a.sb[k + 1] : 0;
+    const int th = k < a.num_seqs ? a.sb[k] : 0;
+    ok &= !__any(k < a.num_seqs && th > nx);
+    if (b == 0) ok &= __shfl(th, 0, kWave) == 0;
+    if (b + kWave >= a.num_seqs) ok &= __shfl(nx, a.num_seqs - 1 - b, kWave) == a.num_tokens;
+    const unsigned long long hit = __ballot(k < a.num_seqs && n < nx);
+    if (s < 0 && hit) s = b + __builtin_ctzll(hit);
+  }
+  ok &= s >= 0;
+  int blk = 0, slot = 0;
+  if (ok) {
+    const int b0 = a.sb[s], T = a.sb[s + 1] - b0, L = a.past_lens[s];
+    const int pos = L + (n - b0);
+    ok = T >= 1 && T <= a.max_q && L >= 0 && (int64_t)pos < (int64_t)a.mbps * a.bs;
+    if (ok) {
+      blk = a.bt[(size_t)s * a.mbps + pos / a.bs];
+      slot = pos % a.bs;
+      ok = blk >= 0 && blk < a.num_blocks;
+    }
+  }
+  if (!ok) {
+    if (lane == 0) atomicExch(a.status, kDeviceContract);
+    return;
+  }
+
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(kv ? a.v_new : a.k_new) +
+                        ((size_t)n * a.Hkv + g) * D;
+  const size_t page = ((size_t)blk * a.Hkv + g) * a.bs * D;
+  float x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int d = lane + e * kWave;
+    x[e] = d < D ? in_value<QT>(src + d) : 0.f;
+  }
+  if constexpr (!U8) {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(kv ? a.v_cache : a.k_cache) + page;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int d = lane + e * kWave;
+      if (d < D) dst[kv ? v_off(slot, d, D, false) : k_off(slot, d, D, false)] = src[d];
+    }
+  } else {
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int e = 1; e < E; ++e) {
+      mn = fminf(mn, x[e]);
+      mx = fmaxf(mx, x[e]);
+    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    const _Float16 s_try = (_Float16)__fdiv_rn(__fsub_rn(mx, mn), 255.0f);
+    _Float16 sh = (_Float16)1.0f, zh;
+    if (mx != mn && s_try != (_Float16)0.0f) {
+      sh = s_try;
+      zh = (_Float16)__fdiv_rn(-mn, (float)sh);
+    } else {
+      zh = (_Float16)(-mn);
+    }
+    const float sf = (float)sh, zf = (float)zh;
+    uint8_t* dst = reinterpret_cast<uint8_t*>(kv ? a.v_cache : a.k_cache) + page;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int d = lane + e * kWave;
+      const float r = fminf(fmaxf(rintf(__fadd_rn(__fdiv_rn(x[e], sf), zf)), 0.f), 255.f);
+      if (d < D) dst[kv ? v_off(slot, d, D, true) : k_off(slot, d, D, true)] = (uint8_t)r;
+    }
+    if (lane == 0) {
+      uint16_t* sz = reinterpret_cast<uint16_t*>(kv ? a.vsz : a.ksz) +
+                     (((size_t)blk * a.Hkv + g) * a.bs + slot) * 2;
+      sz[0] = __builtin_bit_cast(uint16_t, sh);
+      sz[1] = __builtin_bit_cast(uint16_t, zh);
+    }
+  }
+}
+
+template <int QT, int KV>
+static hipError_t launch_append_d(const AppendArgs& a, int D, hipStream_t st) {
+  const dim3 grid(a.num_tokens, a.Hkv, 2);
+  switch (D) {
+    case 64: hipLaunchKernelGGL((pa_append<QT, KV, 64>), grid, dim3(kWave), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((pa_append<QT, KV, 128>), grid, dim3(kWave), 0, st, a); break;
+    case 256: hipLaunchKernelGGL((pa_append<QT, KV, 256>), grid, dim3(kWave), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendArgs& a, int q_dtype, int kv_dtype, int D, hipStream_t st) {
+  if (kv_dtype == kU8)
+    return q_dtype == kF16 ? launch_append_d<kF16, kU8>(a, D, st) : launch_append_d<kBF16, kU8>(a, D, st);
+  return q_dtype == kF16 ? launch_append_d<kF16, kF16>(a, D, st) : launch_append_d<kBF16, kBF16>(a, D, st);
+}
+
+}  // namespace pav

@@ -37,6 +37,20 @@ struct SegmentArgs {
   float scale_log2;                  // scale * log2(e)
 };
 
+struct AppendArgs {
+  const void* k_new;                 // [num_tokens, Hkv, D] in the q dtype
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  void* ksz;                         // u8 only: f16 (scale, zero point) per token
+  void* vsz;
+  const int32_t* bt;
+  const int32_t* past_lens;
+  const int32_t* sb;
+  int32_t* status;                   // sticky device status word
+  int32_t num_seqs, num_tokens, Hkv, bs, mbps, num_blocks, max_q;
+};
+
 struct CombineArgs {
   SegmentArgs seg;
   void* out;
@@ -54,6 +68,7 @@ hipError_t launch_segment_u8(const SegmentArgs& a, int q_dtype, int D, int bs, i
                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_combine(const CombineArgs& a, int out_dtype, int D, int threads, dim3 grid,
                           hipStream_t st);
+hipError_t launch_append(const AppendArgs& a, int q_dtype, int kv_dtype, int D, hipStream_t st);
 // Combine workgroup size: enough threads that each loads at most 8 of the S
 // partials of its (token, q head) row (one batch of loads), 256..1024.
 constexpr int combine_threads(int S, int D) {

@@ -241,6 +241,41 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+int run_append(const void* k_new, const void* v_new, void* k, void* v, void* ksz, void* vsz,
+               const int32_t* bt, const int32_t* past_lens, const int32_t* sb,
+               const pa_verify_params* p, bool u8_entry) {
+  if (!p) return PA_ERR_INVALID_ARG;
+  // the positions written must have a block-table entry: plan for the whole row
+  const int64_t max_pos = (int64_t)p->max_blocks_per_seq * p->block_size;
+  int rc = validate(p, (int32_t)std::min<int64_t>(max_pos, INT32_MAX), u8_entry);
+  if (rc) return rc;
+  if (!k_new || !v_new || !k || !v || !bt || !past_lens || !sb) return PA_ERR_INVALID_ARG;
+  if (u8_entry && (!ksz || !vsz)) return PA_ERR_INVALID_ARG;
+  if (!p->workspace || p->workspace_bytes < sizeof(int32_t)) return PA_ERR_WORKSPACE;
+  if (p->num_tokens > 2147483647 / 2) return PA_ERR_UNSUPPORTED;
+  pav::AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k;
+  a.v_cache = v;
+  a.ksz = ksz;
+  a.vsz = vsz;
+  a.bt = bt;
+  a.past_lens = past_lens;
+  a.sb = sb;
+  a.status = static_cast<int32_t*>(p->workspace);
+  a.num_seqs = p->num_seqs;
+  a.num_tokens = p->num_tokens;
+  a.Hkv = p->num_kv_heads;
+  a.bs = p->block_size;
+  a.mbps = p->max_blocks_per_seq;
+  a.num_blocks = p->num_blocks;
+  a.max_q = (int32_t)query_bound(p);
+  const hipError_t e = pav::launch_append(a, p->q_dtype, p->kv_dtype, p->head_dim,
+                                          static_cast<hipStream_t>(p->stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -279,6 +314,21 @@ int pa_verify_forward_u8(const void* q, const uint8_t* k_cache, const uint8_t* v
                          void* out, const pa_verify_params* p) {
   return run(q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
              subsequence_begins, max_context_len, scale, out, p, true);
+}
+
+int pa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                 const int32_t* block_tables, const int32_t* past_lens,
+                 const int32_t* subsequence_begins, const pa_verify_params* p) {
+  return run_append(k_new, v_new, k_cache, v_cache, nullptr, nullptr, block_tables, past_lens,
+                    subsequence_begins, p, false);
+}
+
+int pa_kv_append_u8(const void* k_new, const void* v_new, uint8_t* k_cache, uint8_t* v_cache,
+                    void* k_scale_zp, void* v_scale_zp, const int32_t* block_tables,
+                    const int32_t* past_lens, const int32_t* subsequence_begins,
+                    const pa_verify_params* p) {
+  return run_append(k_new, v_new, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables,
+                    past_lens, subsequence_begins, p, true);
 }
 
 int pa_verify_read_status(const pa_verify_params* p, int32_t* device_status) {

@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "pa_verify.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(pa_verify_[a-z_0-9]+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(pa_(?:verify|kv)_[a-z_0-9]+)\s*\(",
                                  text, flags=re.M)))
 
 
@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
         assert hasattr(L, n), n
     nm = subprocess.run(["nm", "-D", "--defined-only", pav.LIB_PATH], capture_output=True,
                         text=True, check=True).stdout
-    exported = set(re.findall(r" T (pa_verify_\w+)", nm))
+    exported = set(re.findall(r" T (pa_(?:verify|kv)_\w+)", nm))
     assert set(names) <= exported
 
 
@@ -117,6 +117,26 @@ def test_null_pointers_and_entry_mismatch():
     assert call(params(kv_dtype=pav.PA_U8)) == pav.PA_ERR_UNSUPPORTED        # u8 cache, fp entry
     assert call(params(), u8=True) == pav.PA_ERR_UNSUPPORTED                 # fp cache, u8 entry
     assert call(params(), max_ctx=0) == pav.PA_ERR_INVALID_ARG
+
+
+def test_append_host_errors():
+    L = pav.lib()
+    ok = params(num_q_heads=8, workspace=FAKE, workspace_bytes=256)
+    args = [FAKE] * 7
+    # null pointers, missing workspace, wrong dtype pairing: all before any launch
+    for k in range(7):
+        a = list(args)
+        a[k] = None
+        assert L.pa_kv_append(*a, ctypes.byref(ok)) == pav.PA_ERR_INVALID_ARG
+    assert L.pa_kv_append(*args, ctypes.byref(params())) == pav.PA_ERR_WORKSPACE
+    assert L.pa_kv_append(*args, ctypes.byref(params(kv_dtype=pav.PA_U8, workspace=FAKE,
+                                                     workspace_bytes=256))) == pav.PA_ERR_UNSUPPORTED
+    u8 = params(kv_dtype=pav.PA_U8, workspace=FAKE, workspace_bytes=256)
+    assert L.pa_kv_append_u8(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                             ctypes.byref(u8)) == pav.PA_ERR_INVALID_ARG
+    assert L.pa_kv_append_u8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             ctypes.byref(params(workspace=FAKE, workspace_bytes=256))) == pav.PA_ERR_UNSUPPORTED
+    assert L.pa_kv_append(*args, None) == pav.PA_ERR_INVALID_ARG
 
 
 def test_missing_workspace_is_reported_before_any_launch():

@@ -349,3 +349,120 @@ def test_chain_tree_is_bitwise_causal():
         chain.tree_mask = pi.tree_masks([list(range(-1, T - 1)) for T in case.Ts])
         assert np.array_equal(to_f64(run_gpu(chain)), causal), case.name
 
+
+
+# ---------------------------------------------------------------------------
+# Writing the new tokens into the cache (and u8 quantisation on the way)
+# ---------------------------------------------------------------------------
+def _append_gpu(case, kn, vn, new_dtype, max_query_len=None, table=None):
+    """GPU append into device copies of the case's caches; returns host copies
+    of (k, v, ksz, vsz) after it."""
+    import torch
+    import speculative_decoding_verify_paged_amd as pav
+    from gpu_util import to_device
+    dev = to_device(case)
+    nt = torch.float16 if new_dtype == pi.F16 else torch.bfloat16
+    k_new = torch.from_numpy(np.ascontiguousarray(kn).view(np.int16)).cuda().view(nt)
+    v_new = torch.from_numpy(np.ascontiguousarray(vn).view(np.int16)).cuda().view(nt)
+    bt = dev["block_tables"] if table is None else torch.from_numpy(table).cuda()
+    mql = max(case.Ts) if max_query_len is None else max_query_len
+    if case.kv_dtype == pi.U8:
+        pav.pa_kv_append_u8(k_new, v_new, dev["k_cache"], dev["v_cache"], dev["k_scale_zp"],
+                            dev["v_scale_zp"], bt, dev["past_lens"], dev["subsequence_begins"],
+                            max_query_len=mql)
+    else:
+        pav.pa_kv_append(k_new, v_new, dev["k_cache"], dev["v_cache"], bt, dev["past_lens"],
+                         dev["subsequence_begins"], max_query_len=mql)
+    torch.cuda.synchronize()
+
+    def host(t):
+        if t is None:
+            return None
+        if t.element_size() == 2:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+    return (host(dev["k_cache"]).reshape(case.k_cache.shape), host(dev["v_cache"]).reshape(case.v_cache.shape),
+            host(dev.get("k_scale_zp")), host(dev.get("v_scale_zp")))
+
+
+def test_append_16bit_restores_the_cache_bit_for_bit():
+    from oracle_pins import _blank_new_tokens
+    rng = np.random.default_rng(41)
+    for k, (kv, D, bs, Ls, Ts) in enumerate([(pi.F16, 128, 16, [8190], [3]),
+                                             (pi.BF16, 256, 64, [5, 3000], [2, 4]),
+                                             (pi.F16, 64, 32, [0, 17, 400], [8, 1, 16])]):
+        case = pi.build_case([900, k], Ls, Ts, num_q_heads=8, num_kv_heads=2, head_dim=D,
+                             block_size=bs, q_dtype=kv, kv_dtype=kv, spare_blocks=2)
+        kn, vn, blank = _blank_new_tokens(case, rng)
+        k2, v2, _, _ = _append_gpu(blank, kn, vn, kv)
+        assert np.array_equal(k2, case.k_cache) and np.array_equal(v2, case.v_cache), k
+
+
+def test_append_u8_matches_the_oracle_bit_for_bit():
+    rng = np.random.default_rng(42)
+    for k, (qd, D, bs, Ls, Ts) in enumerate([(pi.F16, 256, 16, [32768], [3]),
+                                             (pi.BF16, 128, 32, [0, 700], [4, 2]),
+                                             (pi.F16, 64, 64, [63, 64, 65], [1, 9, 16])]):
+        case = pi.build_case([910, k], Ls, Ts, num_q_heads=8, num_kv_heads=2, head_dim=D,
+                             block_size=bs, q_dtype=qd, kv_dtype=pi.U8, spare_blocks=2)
+        T = case.num_tokens
+        scale = rng.choice([0.01, 1.0, 40.0], size=(T, 2, 1))
+        kf = rng.standard_normal((T, 2, D)) * scale
+        vf = rng.standard_normal((T, 2, D)) * scale
+        kf[0, 0, :] = 1.25                                     # a constant row
+        kn, vn = pi.f32_to_bits(kf, qd), pi.f32_to_bits(vf, qd)
+        st, k_o, v_o, ks_o, vs_o = oracle.get().kv_append(case, kn, vn, qd)
+        assert st == 0
+        k2, v2, ks2, vs2 = _append_gpu(case, kn, vn, qd)
+        assert np.array_equal(k2, k_o) and np.array_equal(v2, v_o), k
+        assert np.array_equal(ks2, ks_o) and np.array_equal(vs2, vs_o), k
+
+
+def test_append_then_verify():
+    """The serving order: append the drafts, then verify them, on one stream."""
+    import torch
+    import speculative_decoding_verify_paged_amd as pav
+    from gpu_util import to_device
+    rng = np.random.default_rng(43)
+    case = pi.build_case([920], [30000], [4], num_q_heads=16, num_kv_heads=4, head_dim=256,
+                         block_size=16, q_dtype=pi.F16, kv_dtype=pi.U8)
+    kf = rng.standard_normal((4, 4, 256))
+    vf = rng.standard_normal((4, 4, 256))
+    kn, vn = pi.f32_to_bits(kf, pi.F16), pi.f32_to_bits(vf, pi.F16)
+    st, k_o, v_o, ks_o, vs_o = oracle.get().kv_append(case, kn, vn, pi.F16)
+    done = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+    done.k_cache, done.v_cache, done.k_scale_zp, done.v_scale_zp = k_o, v_o, ks_o, vs_o
+    ref = oracle.forward(done)
+    dev = to_device(case)
+    k_new = torch.from_numpy(kn.view(np.int16)).cuda().view(torch.float16)
+    v_new = torch.from_numpy(vn.view(np.int16)).cuda().view(torch.float16)
+    pav.pa_kv_append_u8(k_new, v_new, dev["k_cache"], dev["v_cache"], dev["k_scale_zp"],
+                        dev["v_scale_zp"], dev["block_tables"], dev["past_lens"],
+                        dev["subsequence_begins"], max_query_len=4)
+    got = run_gpu(case, dev)
+    err = max_err(got, ref)
+    print(f"append+verify: max err {err:.3e}", flush=True)
+    assert err <= tol(case)
+    assert pav.pa_verify_read_status() == pav.PA_OK
+
+
+def test_append_contract_violation_writes_nothing():
+    import speculative_decoding_verify_paged_amd as pav
+    from oracle_pins import _blank_new_tokens
+    rng = np.random.default_rng(44)
+    case = pi.build_case([930], [40, 90], [2, 3], num_q_heads=4, num_kv_heads=2, head_dim=64,
+                         block_size=16, q_dtype=pi.F16, kv_dtype=pi.F16, spare_blocks=1)
+    kn, vn, blank = _blank_new_tokens(case, rng)
+    table = case.block_tables.copy()
+    table[1, 90 // 16] = case.num_blocks + 3               # sequence 1's first new position
+    k2, v2, _, _ = _append_gpu(blank, kn, vn, pi.F16, table=table)
+    assert pav.pa_verify_read_status() == pav.PA_ERR_DEVICE_CONTRACT
+    # sequence 0 written, sequence 1's token in the bad block untouched
+    kl2 = pi.untile_k(k2.reshape(case.num_blocks, 2, -1), 16, 64)
+    klb = pi.untile_k(blank.k_cache.reshape(case.num_blocks, 2, -1), 16, 64)
+    kl0 = pi.untile_k(case.k_cache.reshape(case.num_blocks, 2, -1), 16, 64)
+    for i in range(2):
+        blk = case.block_tables[0, (40 + i) // 16]
+        assert np.array_equal(kl2[blk, :, (40 + i) % 16], kl0[blk, :, (40 + i) % 16])
+    blk = case.block_tables[1, 90 // 16]
+    assert np.array_equal(kl2[blk, :, 90 % 16], klb[blk, :, 90 % 16])
