@@ -176,6 +176,56 @@ class Runner:
         return statistics.median(per_call), statistics.median(per_kernel), per_call
 
 
+def time_append(case, steps, warmup, repeats):
+    """µs per pa_kv_append(_u8) call writing the case's T new tokens (values
+    drawn once, stored in the q dtype), graph-replayed like the forward."""
+    import numpy as np
+    import torch
+    import speculative_decoding_verify_paged_amd as pav
+    from gpu_util import to_device
+    dev = to_device(case)
+    rng = np.random.default_rng(1)
+    qt = dev["q"].dtype
+    shape = (case.num_tokens, case.num_kv_heads, case.head_dim)
+    k_new = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).cuda().to(qt)
+    v_new = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).cuda().to(qt)
+
+    def one(stream):
+        if case.kv_dtype == 2:
+            pav.pa_kv_append_u8(k_new, v_new, dev["k_cache"], dev["v_cache"], dev["k_scale_zp"],
+                                dev["v_scale_zp"], dev["block_tables"], dev["past_lens"],
+                                dev["subsequence_begins"], max_query_len=max(case.Ts), stream=stream)
+        else:
+            pav.pa_kv_append(k_new, v_new, dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                             dev["past_lens"], dev["subsequence_begins"], max_query_len=max(case.Ts),
+                             stream=stream)
+
+    for _ in range(warmup):
+        one(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream().cuda_stream
+        for _ in range(steps):
+            one(cs)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per = []
+    for _ in range(repeats):
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1000.0 / steps)
+    e = 1 if case.kv_dtype == 2 else 2
+    written = case.num_tokens * case.num_kv_heads * (2 * case.head_dim * e + (8 if e == 1 else 0))
+    return {"us_per_call": round(statistics.median(per), 3), "bytes_written": written,
+            "what": f"{case.num_tokens} new tokens x {case.num_kv_heads} KV heads into the "
+                    f"{'u8 (quantised)' if e == 1 else 'f16/bf16'} cache"}
+
+
 def read_ceiling():
     """Best HBM streaming-read rate of a plain 16-byte-load kernel over 4 GiB
     (beyond the 256 MB Infinity Cache), GB/s.  Also runs one 1 GiB copy, the
@@ -270,6 +320,7 @@ def main():
         t1 = {"us_per_call": round(us1, 3), "us_segment_kernel": round(us1_kernel, 3),
               "kv_gbs": round(case1.kv_bytes() / us1 / 1e3, 1)}
         del run1
+    append = time_append(case, args.steps, args.warmup, args.repeats)
     ceiling = None if args.no_ceiling else read_ceiling()
 
     value = kv / us / 1e3                                  # bytes/µs -> GB/s
@@ -306,6 +357,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "kernel_us": round(us_kernel, 3), "traffic": traffic},
     }
+    line["kv_append"] = append
     if t1 is not None:
         line["T1"] = t1
         line["t_over_t1"] = round(us / t1["us_per_call"], 4)
