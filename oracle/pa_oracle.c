@@ -34,9 +34,10 @@
  *
  * Layouts (the library's C ABI defines them; restated here on purpose):
  *   q [num_tokens][Hq][D]; k and v [nb][Hkv][page], each page holding the
- *   block_size x D elements of one (block, KV head) in the tiled order of
- *   k_offset / v_offset below; scale/zero point [nb][Hkv][bs][2] (f16);
- *   block_tables [num_seqs][mbps].  Requires block_size % 16 == 0 and
+ *   block_size x D elements of one (block, KV head) in the order of
+ *   k_offset / v_offset below (tiled for block_size % 16 == 0; K row-major
+ *   and V d-major for pages of 1, 2, 4 or 8 slots); scale/zero point
+ *   [nb][Hkv][bs][2] (f16); block_tables [num_seqs][mbps].  Requires
  *   D % 32 == 0 (D % 64 == 0 for u8).
  * Element codes: 0 = f16 bits, 1 = bf16 bits, 2 = u8 code with f16
  * (scale, zero point), 3 = fp64 value (test-only input form).
@@ -83,17 +84,20 @@ static double dec_elem(const void* base, size_t idx, int code) {
   }
 }
 
-/* Offsets of element (slot, d) inside one page.  Sub-tiles of 16 slots; in
+/* Offsets of element (slot, d) inside one page.  Pages of 1-8 slots: K is
+ * [slot][d], V is [d][slot].  Otherwise sub-tiles of 16 slots; in
  * each, K is ordered [d/32][(d%32)/8][slot%16][d%8] (u8: [d/64][(d%64)/16]
  * [slot%16][d%16]) and V [d/32][(slot%16)/4][d%16][(d%32)/16][slot%4] (u8:
  * [d/64][(slot%16)/4][d%16][(d%64)/16][slot%4]). */
-static size_t k_offset(int slot, int d, int D, int u8) {
+static size_t k_offset(int slot, int d, int D, int u8, int bs) {
+  if (bs < 16) return (size_t)slot * D + d;        /* small pages: [slot][d] */
   const size_t st = (size_t)(slot / 16), m = (size_t)(slot % 16);
   if (u8) return (((st * (D / 64) + d / 64) * 4 + (d % 64) / 16) * 16 + m) * 16 + d % 16;
   return (((st * (D / 32) + d / 32) * 4 + (d % 32) / 8) * 16 + m) * 8 + d % 8;
 }
 
-static size_t v_offset(int slot, int d, int D, int u8) {
+static size_t v_offset(int slot, int d, int D, int u8, int bs) {
+  if (bs < 16) return (size_t)d * bs + slot;       /* small pages: [d][slot] */
   const size_t st = (size_t)(slot / 16), qq = (size_t)((slot % 16) / 4);
   if (u8) return ((((st * (D / 64) + d / 64) * 4 + qq) * 16 + d % 16) * 4 + (d % 64) / 16) * 4 + slot % 4;
   return ((((st * (D / 32) + d / 32) * 4 + qq) * 16 + d % 16) * 2 + (d % 32) / 16) * 4 + slot % 4;
@@ -119,8 +123,10 @@ static int check_args(const pa_oracle_args* a) {
   if (a->num_seqs < 1 || a->num_q_heads < 1 || a->num_kv_heads < 1 || a->head_dim < 1 ||
       a->block_size < 1 || a->num_q_heads % a->num_kv_heads != 0)
     return PA_ORACLE_ERR_ARG;
-  if (a->block_size % 16 != 0 || a->head_dim % (a->kv_dtype == PA_ORACLE_U8 ? 64 : 32) != 0)
-    return PA_ORACLE_ERR_ARG;                       /* the tiled page layout needs these */
+  if ((a->block_size % 16 != 0 && a->block_size != 1 && a->block_size != 2 && a->block_size != 4 &&
+       a->block_size != 8) ||
+      a->head_dim % (a->kv_dtype == PA_ORACLE_U8 ? 64 : 32) != 0)
+    return PA_ORACLE_ERR_ARG;                       /* the page layouts need these */
   if (!a->q || !a->k_cache || !a->v_cache || !a->block_tables || !a->past_lens ||
       !a->subsequence_begins)
     return PA_ORACLE_ERR_ARG;
@@ -188,7 +194,7 @@ static void attend_one(const pa_oracle_args* a, int n, int h, double* z, double*
     double dot = 0.0;
     for (int d = 0; d < D; ++d)
       dot += dec_elem(a->q, q_off + d, a->q_dtype) *
-             kv_value(a, a->k_cache, a->k_scale_zp, page + k_offset(slot, d, D, u8), row);
+             kv_value(a, a->k_cache, a->k_scale_zp, page + k_offset(slot, d, D, u8, bs), row);
     z[t - lo] = a->scale * dot;
     if (z[t - lo] > m) m = z[t - lo];
   }
@@ -204,7 +210,7 @@ static void attend_one(const pa_oracle_args* a, int n, int h, double* z, double*
     const size_t row = (blk * Hkv + g) * bs + slot;
     const size_t page = (blk * Hkv + g) * (size_t)bs * D;
     for (int d = 0; d < D; ++d) {
-      const size_t vidx = page + v_offset(slot, d, D, u8);
+      const size_t vidx = page + v_offset(slot, d, D, u8, bs);
       out_row[d] += w * kv_value(a, a->v_cache, a->v_scale_zp, vidx, row);
     }
   }
@@ -355,7 +361,8 @@ int pa_oracle_kv_append(const pa_oracle_append_args* a) {
   if (!u8 && a->kv_dtype != a->new_dtype) return PA_ORACLE_ERR_ARG;
   if (u8 && (!a->k_scale_zp || !a->v_scale_zp)) return PA_ORACLE_ERR_ARG;
   const int D = a->head_dim, bs = a->block_size, Hkv = a->num_kv_heads;
-  if (bs % 16 != 0 || D % (u8 ? 64 : 32) != 0) return PA_ORACLE_ERR_ARG;
+  if ((bs % 16 != 0 && bs != 1 && bs != 2 && bs != 4 && bs != 8) || D % (u8 ? 64 : 32) != 0)
+    return PA_ORACLE_ERR_ARG;
   if (a->subsequence_begins[0] != 0 || a->subsequence_begins[a->num_seqs] != a->num_tokens)
     return PA_ORACLE_ERR_META;
   float* row = (float*)malloc(sizeof(float) * (size_t)D);
@@ -394,7 +401,7 @@ int pa_oracle_kv_append(const pa_oracle_append_args* a) {
           void* cache = kv ? a->v_cache : a->k_cache;
           if (!u8) {
             for (int d = 0; d < D; ++d) {
-              const size_t off = page + (kv ? v_offset(slot, d, D, 0) : k_offset(slot, d, D, 0));
+              const size_t off = page + (kv ? v_offset(slot, d, D, 0, bs) : k_offset(slot, d, D, 0, bs));
               ((uint16_t*)cache)[off] = in[src + d];
             }
             continue;
@@ -403,7 +410,7 @@ int pa_oracle_kv_append(const pa_oracle_append_args* a) {
           uint16_t sb, zb;
           pa_oracle_quantize_row(row, D, codes, &sb, &zb);
           for (int d = 0; d < D; ++d) {
-            const size_t off = page + (kv ? v_offset(slot, d, D, 1) : k_offset(slot, d, D, 1));
+            const size_t off = page + (kv ? v_offset(slot, d, D, 1, bs) : k_offset(slot, d, D, 1, bs));
             ((uint8_t*)cache)[off] = codes[d];
           }
           uint16_t* sz = kv ? a->v_scale_zp : a->k_scale_zp;

@@ -27,7 +27,8 @@ Recipe (also the basis of every parity case and of the benchmark):
 
 Layouts match the C ABI header: every (block, KV head) page of K and V holds
 its block_size x D elements in the tiled order of ``k_page_offset`` /
-``v_page_offset`` (16-slot sub-tiles in MFMA operand order); scale/zp
+``v_page_offset`` (16-slot sub-tiles in MFMA operand order; pages of 1-8
+slots: K row-major, V d-major); scale/zp
 [nb, Hkv, bs, 2] f16; q [num_tokens, Hq, D].  ``tile_k`` / ``tile_v`` turn
 [..., bs, D] pages into that order and ``untile_k`` / ``untile_v`` back.
 """
@@ -115,15 +116,21 @@ def quantize_u8(x: np.ndarray):
 # ----------------------------------------------------------------------------
 # page layouts (data movement only)
 # ----------------------------------------------------------------------------
-def k_page_offset(slot, d, D, u8=False):
-    """Element offset of K[slot, d] inside one (block, KV head) page."""
+def k_page_offset(slot, d, D, u8=False, bs=16):
+    """Element offset of K[slot, d] inside one (block, KV head) page.  Pages
+    of fewer than 16 slots are row-major [slot][d]."""
+    if bs < 16:
+        return slot * D + d
     if u8:
         return ((((slot // 16) * (D // 64) + d // 64) * 4 + (d % 64) // 16) * 16 + slot % 16) * 16 + d % 16
     return ((((slot // 16) * (D // 32) + d // 32) * 4 + (d % 32) // 8) * 16 + slot % 16) * 8 + d % 8
 
 
-def v_page_offset(slot, d, D, u8=False):
-    """Element offset of V[slot, d] inside one (block, KV head) page."""
+def v_page_offset(slot, d, D, u8=False, bs=16):
+    """Element offset of V[slot, d] inside one (block, KV head) page.  Pages
+    of fewer than 16 slots are d-major [d][slot]."""
+    if bs < 16:
+        return d * bs + slot
     if u8:
         return (((((slot // 16) * (D // 64) + d // 64) * 4 + (slot % 16) // 4) * 16 + d % 16) * 4
                 + (d % 64) // 16) * 4 + slot % 4
@@ -134,7 +141,7 @@ def v_page_offset(slot, d, D, u8=False):
 def _perm(bs, D, fn, u8):
     slot = np.arange(bs)[:, None]
     d = np.arange(D)[None, :]
-    return fn(slot, d, D, u8).reshape(-1)          # offset of logical (slot, d), row-major
+    return fn(slot, d, D, u8, bs).reshape(-1)      # offset of logical (slot, d), row-major
 
 
 def tile_k(pages, u8=False):

@@ -137,7 +137,7 @@ def tiny_random_cases(n=48, seed=7):
         Hkv = int(rng.choice([1, 2]))
         kv = int(rng.choice([pi.F16, pi.BF16, pi.U8]))
         D = 64 if kv == pi.U8 else int(rng.choice([32, 64]))
-        bs = int(rng.choice([16, 32]))
+        bs = int(rng.choice([1, 2, 4, 8, 16, 16, 32, 32]))
         W = int(rng.choice([0, 0, 1, 5, 64]))
         qd = pi.BF16 if kv == pi.BF16 else pi.F16
         num_seqs = int(rng.choice([1, 1, 2, 3]))

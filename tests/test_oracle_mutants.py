@@ -24,6 +24,10 @@ MUTANTS = [
     ("tree_self_not_implied", [("return j == i || ((a->tree_mask[n] >> j) & 1u);",
                                 "return ((a->tree_mask[n] >> j) & 1u);")]),
     ("tree_hides_the_past", [("if (t < L) return 1;", "if (t < L) return 0;")]),
+    ("small_page_v_slot_major", [("if (bs < 16) return (size_t)d * bs + slot;",
+                                  "if (bs < 16) return (size_t)slot * D + d;")]),
+    ("small_page_k_d_major", [("if (bs < 16) return (size_t)slot * D + d;        /* small pages: [slot][d] */",
+                               "if (bs < 16) return (size_t)d * bs + slot;")]),
     ("quantise_floor", [("float r = rintf(y);", "float r = floorf(y);")]),
     ("quantise_no_clamp", [("if (r > 255.0f) r = 255.0f;", "if (r > 255.0f) r = r - 256.0f;")]),
     ("quantise_zp_sign", [("zb = f32_to_f16(-mn / f16_to_f32(sb));", "zb = f32_to_f16(mn / f16_to_f32(sb));")]),
@@ -34,9 +38,9 @@ MUTANTS = [
                                  ("sz[2 * srow + 1] = zb;", "sz[2 * srow + 1] = sb;")]),
     ("tree_first_row_mask", [("return j == i || ((a->tree_mask[n] >> j) & 1u);",
                               "return j == i || ((a->tree_mask[n - i] >> j) & 1u);")]),
-    ("v_read_in_k_layout", [("const size_t vidx = page + v_offset(slot, d, D, u8);",
-                             "const size_t vidx = page + k_offset(slot, d, D, u8);")]),
-    ("k_page_row_major", [("page + k_offset(slot, d, D, u8), row);",
+    ("v_read_in_k_layout", [("const size_t vidx = page + v_offset(slot, d, D, u8, bs);",
+                             "const size_t vidx = page + k_offset(slot, d, D, u8, bs);")]),
+    ("k_page_row_major", [("page + k_offset(slot, d, D, u8, bs), row);",
                            "page + (size_t)slot * D + d, row);")]),
     ("v_slot_quads_swapped", [("return ((((st * (D / 32) + d / 32) * 4 + qq) * 16 + d % 16) * 2 + (d % 32) / 16) * 4 + slot % 4;",
                                "return ((((st * (D / 32) + d / 32) * 4 + slot % 4) * 16 + d % 16) * 2 + (d % 32) / 16) * 4 + qq;")]),
@@ -56,8 +60,8 @@ MUTANTS = [
     ("bf16_shift", [("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;")]),
     ("q_head_major_layout", [("const size_t q_off = ((size_t)n * Hq + h) * D;",
                               "const size_t q_off = ((size_t)h * a->num_tokens + n) * D;")]),
-    ("k_dims_reversed", [("page + k_offset(slot, d, D, u8), row);",
-                          "page + k_offset(slot, D - 1 - d, D, u8), row);")]),
+    ("k_dims_reversed", [("page + k_offset(slot, d, D, u8, bs), row);",
+                          "page + k_offset(slot, D - 1 - d, D, u8, bs), row);")]),
 ]
 
 PIN_ORDER = ["hand", "closed", "rows", "window", "gqa", "u8", "permutation", "ragged", "sdpa", "tree",
