@@ -42,6 +42,9 @@ def workloads():
         "gqa4_d128_f16_L32768": lambda T: pi.config2(32768, T),
         "gqa4_d128_f16_L8192": lambda T: pi.config2(8192, T),
         "gqa4_d128_f16_L32768_tree": lambda T: pi.config2(32768, T, tree=True),
+        "gqa4_d128_f16_L32768_bs1": lambda T: pi.config2(32768, T, block_size=1),
+        "gqa4_d128_f16_L32768_bs4": lambda T: pi.config2(32768, T, block_size=4),
+        "gqa4_d128_f16_L32768_bs8": lambda T: pi.config2(32768, T, block_size=8),
         "u8kv_d256_L32768": lambda T: pi.config3(32768, T),
         "swa_pair_global_L32768": lambda T: pi.config4(32768, window=0, T=T),
         "swa_pair_global_L51200": lambda T: pi.config4(51200, window=0, T=T),
@@ -313,7 +316,7 @@ def main():
 
     t1 = None
     if not args.no_t1 and args.T != 1 and args.workload.startswith("gqa4"):
-        case1 = workloads()[args.workload.replace("_tree", "")](1)
+        case1 = workloads()[args.workload.replace("_tree", "")](1)   # causal T = 1, same pages
         run1 = Runner(case1)
         us1, _ = run1.time_graph(args.steps, args.warmup, args.repeats)
         _, us1_kernel, _ = run1.time(args.steps, args.warmup, args.repeats)

@@ -405,13 +405,15 @@ def config1(rep: int = 0, poison: bool = False) -> Case:
                       scale=1.0 / 8.0, poison=poison, name="tiny_L512_T3")
 
 
-def config2(L: int, T: int, rep: int = 0, poison: bool = False, tree: bool = False) -> Case:
+def config2(L: int, T: int, rep: int = 0, poison: bool = False, tree: bool = False,
+            block_size: int = 16) -> Case:
     """1 seq, Hq 32 / Hkv 8 (GQA 4), D 128, bs 16, fp16 Q/KV/out (tree: a random
-    draft tree over the T new tokens)."""
+    draft tree over the T new tokens; block_size: other page sizes)."""
     return build_case([2, L, T, rep], [L], [T], num_q_heads=32, num_kv_heads=8,
-                      head_dim=128, block_size=16, q_dtype=F16, kv_dtype=F16,
+                      head_dim=128, block_size=block_size, q_dtype=F16, kv_dtype=F16,
                       poison=poison, tree=tree,
-                      name=f"gqa4_d128_f16_L{L}_T{T}" + ("_tree" if tree else ""))
+                      name=f"gqa4_d128_f16_L{L}_T{T}" + ("_tree" if tree else "")
+                      + ("" if block_size == 16 else f"_bs{block_size}"))
 
 
 def config3(L: int = 32768, T: int = 3, rep: int = 0, poison: bool = False) -> Case:

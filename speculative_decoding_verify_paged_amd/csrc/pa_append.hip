@@ -17,14 +17,17 @@ namespace pav {
 
 namespace {
 
-// Offsets of element (slot, d) inside one (block, KV head) page: the tiled
-// orders the segment kernel's loads assume (sub-tiles of 16 slots).
-__device__ __forceinline__ int k_off(int slot, int d, int D, bool u8) {
+// Offsets of element (slot, d) inside one (block, KV head) page of bs slots:
+// the orders the segment kernel's loads assume (sub-tiles of 16 slots; pages
+// of fewer slots: K [slot][d], V [d][slot]).
+__device__ __forceinline__ int k_off(int slot, int d, int D, bool u8, int bs) {
+  if (bs < 16) return slot * D + d;
   const int st = slot / 16, m = slot % 16;
   if (u8) return (((st * (D / 64) + d / 64) * 4 + (d % 64) / 16) * 16 + m) * 16 + d % 16;
   return (((st * (D / 32) + d / 32) * 4 + (d % 32) / 8) * 16 + m) * 8 + d % 8;
 }
-__device__ __forceinline__ int v_off(int slot, int d, int D, bool u8) {
+__device__ __forceinline__ int v_off(int slot, int d, int D, bool u8, int bs) {
+  if (bs < 16) return d * bs + slot;
   const int st = slot / 16, qq = (slot % 16) / 4;
   if (u8) return ((((st * (D / 64) + d / 64) * 4 + qq) * 16 + d % 16) * 4 + (d % 64) / 16) * 4 + slot % 4;
   return ((((st * (D / 32) + d / 32) * 4 + qq) * 16 + d % 16) * 2 + (d % 32) / 16) * 4 + slot % 4;
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(kWave) void pa_append(AppendArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int d = lane + e * kWave;
-      if (d < D) dst[kv ? v_off(slot, d, D, false) : k_off(slot, d, D, false)] = src[d];
+      if (d < D) dst[kv ? v_off(slot, d, D, false, a.bs) : k_off(slot, d, D, false, a.bs)] = src[d];
     }
   } else {
     float mn = x[0], mx = x[0];
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(kWave) void pa_append(AppendArgs a) {
     for (int e = 0; e < E; ++e) {
       const int d = lane + e * kWave;
       const float r = fminf(fmaxf(rintf(__fadd_rn(__fdiv_rn(x[e], sf), zf)), 0.f), 255.f);
-      if (d < D) dst[kv ? v_off(slot, d, D, true) : k_off(slot, d, D, true)] = (uint8_t)r;
+      if (d < D) dst[kv ? v_off(slot, d, D, true, a.bs) : k_off(slot, d, D, true, a.bs)] = (uint8_t)r;
     }
     if (lane == 0) {
       uint16_t* sz = reinterpret_cast<uint16_t*>(kv ? a.vsz : a.ksz) +

@@ -90,19 +90,27 @@ struct SegConfig {
   int prefetch;
   int groups_per_cu;
 };
-constexpr SegConfig seg_config(int kv_dtype, int D, int rb) {
+constexpr SegConfig seg_config(int kv_dtype, int D, int rb, int bs = 16) {
+  // pages of fewer than 16 slots gather per lane (more address registers)
+  if (bs < 16) return D >= 256 ? SegConfig{1, 1, 1} : SegConfig{2, 1, 2};
   if (rb > 1) return SegConfig{1, 1, 1};
   if (kv_dtype == kU8)
     return D >= 256 ? SegConfig{2, 1, 1} : D >= 128 ? SegConfig{1, 2, 1} : SegConfig{4, 1, 4};
   return D >= 256 ? SegConfig{1, 1, 1} : D >= 128 ? SegConfig{1, 2, 1} : SegConfig{4, 1, 4};
 }
-constexpr int groups_per_cu(int kv_dtype, int D, int rb) { return seg_config(kv_dtype, D, rb).groups_per_cu; }
+constexpr int groups_per_cu(int kv_dtype, int D, int rb, int bs) {
+  return seg_config(kv_dtype, D, rb, bs).groups_per_cu;
+}
 static_assert(kWavesPerGroup == 4, "the table above assumes 4-wavefront workgroups");
 // Row blocks built per (cache dtype, head_dim): each adds D/4 accumulator
 // and D/8 query registers per lane and 16 * (D + 4) * 16 B of LDS; these are
 // the largest counts that compile without register spills.
 constexpr int max_row_blocks(int kv_dtype, int D) {
   return D <= 64 ? 4 : D <= 128 ? 3 : kv_dtype == kU8 ? 2 : 1;
+}
+// Pages of fewer than 16 slots are built for one row block only.
+constexpr int max_row_blocks(int kv_dtype, int D, int bs) {
+  return bs < 16 ? 1 : max_row_blocks(kv_dtype, D);
 }
 static_assert(kWavesPerGroup == 4, "the table above assumes 4-wavefront workgroups");
 

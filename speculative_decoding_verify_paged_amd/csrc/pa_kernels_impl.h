@@ -75,6 +75,20 @@ __device__ __forceinline__ u32x4 ld16_stream(const char* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// Narrower streaming loads for pages of fewer than 16 slots.
+__device__ __forceinline__ u32x2 ld8_stream(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+__device__ __forceinline__ uint32_t ld4_stream(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+__device__ __forceinline__ uint32_t ld2_stream(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+}
+__device__ __forceinline__ uint32_t ld1_stream(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint8_t*>(p));
+}
+
 // 16x16x32: A and B hold 8 consecutive k values per lane.
 template <int QT>
 __device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
@@ -185,7 +199,8 @@ void pa_segment(SegmentArgs a) {
   constexpr int DT = D / 16;                      // 16-wide d tiles of O^T
   constexpr int OSTRIDE = D + 4;                  // padded LDS row of the merge buffer
   constexpr int ROWS = kRows * RB;                // stacked rows this instance holds
-  static_assert(BS % 16 == 0 && kKeysPerStep == 32, "two 16-slot sub-tiles per step");
+  static_assert((BS % 16 == 0 || BS == 1 || BS == 2 || BS == 4 || BS == 8) && kKeysPerStep == 32,
+                "two 16-slot sub-tiles per step, within one page or across 16 / BS pages");
   __shared__ int s_bt[kMaxSegBlocks];
   __shared__ float s_m[NW][ROWS];
   __shared__ float s_l[NW][ROWS];
@@ -368,7 +383,107 @@ void pa_segment(SegmentArgs a) {
   // address) and is masked out in compute_step.  Branch-free loads keep the
   // outstanding-load count static, so the wait before a step's math covers
   // that step's loads only, not the prefetch of the next one.
+  // Pages of 1, 2, 4 or 8 slots: K pages are row-major [slot][d] and V pages
+  // d-major [d][slot], so each lane gathers its own operand pieces: the K row
+  // of its slot (the same 16 B chunks a tiled sub-tile load delivers), and
+  // for V the 4 consecutive slots of its lane group at each of its d, which
+  // lie in one page when BS >= 4 (one 8 B load), else in 16 / BS ... pages.
+  // Keys outside [lo0, ctx) read the segment's first page, as below.
+  auto load_step_small = [&](int st, Step& r) {
+    const int key0 = si.base + st * kKeysPerStep;
+    // keys [t, t + n) of one page: its id and t's slot, or the segment's
+    // first page when none of them lies in [lo0, ctx) (a piece that is only
+    // partly inside reads its real page; its outside keys are masked later)
+    auto page_row = [&](int t, int n, int& pg, int& row) {
+      const bool present = t < si.ctx && t + n > si.lo0;
+      pg = s_bt[present ? t / BS - blk_lo : 0];
+      row = present ? t % BS : 0;
+    };
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const int t0 = key0 + tau * 16;
+      {
+        int pg, row;
+        page_row(t0 + n16, 1, pg, row);
+        const char* kp = kb + ((((size_t)pg * Hkv + h) * BS + row) * D) * EB;
+#pragma unroll
+        for (int c = 0; c < LK; ++c) {
+          const int d0 = U8 ? c * 64 + q4 * 16 : c * 32 + q4 * 8;
+          r.k[tau][c] = ld16_stream(kp + d0 * EB);
+        }
+      }
+      constexpr int NP = BS >= 4 ? 1 : 4 / BS;                // pages holding the 4 slots
+      constexpr int SP = 4 / NP;                              // slots per piece
+      int pg[NP], row[NP];
+#pragma unroll
+      for (int pc = 0; pc < NP; ++pc) page_row(t0 + q4 * 4 + pc * SP, SP, pg[pc], row[pc]);
+      // element (slot row[pc] .. + SP, d) of piece pc
+      auto vaddr = [&](int pc, int d) {
+        return vb + ((((size_t)pg[pc] * Hkv + h) * BS * D) + (size_t)d * BS + row[pc]) * EB;
+      };
+      if constexpr (U8) {
+#pragma unroll
+        for (int c = 0; c < LV; ++c) {
+#pragma unroll
+          for (int jd = 0; jd < 4; ++jd) {
+            const int d = c * 64 + jd * 16 + n16;
+            uint32_t w;
+            if constexpr (NP == 1) w = ld4_stream(vaddr(0, d));
+            else if constexpr (NP == 2) w = ld2_stream(vaddr(0, d)) | (ld2_stream(vaddr(1, d)) << 16);
+            else
+              w = ld1_stream(vaddr(0, d)) | (ld1_stream(vaddr(1, d)) << 8) |
+                  (ld1_stream(vaddr(2, d)) << 16) | (ld1_stream(vaddr(3, d)) << 24);
+            r.v[tau][c][jd] = w;
+          }
+        }
+        size_t so[NP];                                        // (scale, zero point) offsets
+#pragma unroll
+        for (int pc = 0; pc < NP; ++pc) so[pc] = (((size_t)pg[pc] * Hkv + h) * BS + row[pc]) * 4;
+        u32x4 ks, vs;
+        if constexpr (NP == 1) {
+          ks = ld16_stream(kszb + so[0]);
+          vs = ld16_stream(vszb + so[0]);
+        } else if constexpr (NP == 2) {
+          const u32x2 k0 = ld8_stream(kszb + so[0]), k1 = ld8_stream(kszb + so[1]);
+          const u32x2 v0 = ld8_stream(vszb + so[0]), v1 = ld8_stream(vszb + so[1]);
+          ks = u32x4{k0[0], k0[1], k1[0], k1[1]};
+          vs = u32x4{v0[0], v0[1], v1[0], v1[1]};
+        } else {
+#pragma unroll
+          for (int pc = 0; pc < 4; ++pc) {
+            ks[pc] = ld4_stream(kszb + so[pc]);
+            vs[pc] = ld4_stream(vszb + so[pc]);
+          }
+        }
+        r.ks[tau] = ks;
+        r.vs[tau] = vs;
+      } else {
+#pragma unroll
+        for (int dp = 0; dp < LV; ++dp) {
+          u32x2 half[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int d = dp * 32 + hh * 16 + n16;
+            if constexpr (NP == 1) {
+              half[hh] = ld8_stream(vaddr(0, d));
+            } else if constexpr (NP == 2) {
+              half[hh] = u32x2{ld4_stream(vaddr(0, d)), ld4_stream(vaddr(1, d))};
+            } else {
+              half[hh] = u32x2{ld2_stream(vaddr(0, d)) | (ld2_stream(vaddr(1, d)) << 16),
+                               ld2_stream(vaddr(2, d)) | (ld2_stream(vaddr(3, d)) << 16)};
+            }
+          }
+          r.v[tau][dp] = u32x4{half[0][0], half[0][1], half[1][0], half[1][1]};
+        }
+      }
+    }
+  };
+
   auto load_step = [&](int st, Step& r) {
+    if constexpr (BS < 16) {
+      load_step_small(st, r);
+      return;
+    }
     const int key0 = si.base + st * kKeysPerStep;
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
@@ -686,7 +801,7 @@ void pa_segment(SegmentArgs a) {
 // ---------------------------------------------------------------------------
 template <int QT, int KV, int D, int BS, int RB>
 hipError_t launch_seg(const SegmentArgs& a, dim3 grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  constexpr SegConfig c = seg_config(KV, D, RB);
+  constexpr SegConfig c = seg_config(KV, D, RB, BS);
   constexpr auto kern = pa_segment<QT, KV, D, BS, kWavesPerGroup, c.waves_per_simd, c.prefetch, RB>;
   // with events, the dispatch itself timestamps the kernel's start and end
   if (ev0 || ev1)
@@ -702,13 +817,13 @@ hipError_t dispatch_rb(const SegmentArgs& a, int rb, dim3 grid, hipStream_t st, 
   switch (rb) {
     case 1: return launch_seg<QT, KV, D, BS, 1>(a, grid, st, e0, e1);
     case 2:
-      if constexpr (max_row_blocks(KV, D) >= 2) return launch_seg<QT, KV, D, BS, 2>(a, grid, st, e0, e1);
+      if constexpr (BS >= 16 && max_row_blocks(KV, D) >= 2) return launch_seg<QT, KV, D, BS, 2>(a, grid, st, e0, e1);
       break;
     case 3:
-      if constexpr (max_row_blocks(KV, D) >= 3) return launch_seg<QT, KV, D, BS, 3>(a, grid, st, e0, e1);
+      if constexpr (BS >= 16 && max_row_blocks(KV, D) >= 3) return launch_seg<QT, KV, D, BS, 3>(a, grid, st, e0, e1);
       break;
     case 4:
-      if constexpr (max_row_blocks(KV, D) >= 4) return launch_seg<QT, KV, D, BS, 4>(a, grid, st, e0, e1);
+      if constexpr (BS >= 16 && max_row_blocks(KV, D) >= 4) return launch_seg<QT, KV, D, BS, 4>(a, grid, st, e0, e1);
       break;
   }
   return hipErrorInvalidValue;
@@ -718,6 +833,10 @@ template <int QT, int KV, int D>
 hipError_t dispatch_bs(const SegmentArgs& a, int bs, int rb, dim3 grid, hipStream_t st,
                        hipEvent_t e0, hipEvent_t e1) {
   switch (bs) {
+    case 1: return dispatch_rb<QT, KV, D, 1>(a, rb, grid, st, e0, e1);
+    case 2: return dispatch_rb<QT, KV, D, 2>(a, rb, grid, st, e0, e1);
+    case 4: return dispatch_rb<QT, KV, D, 4>(a, rb, grid, st, e0, e1);
+    case 8: return dispatch_rb<QT, KV, D, 8>(a, rb, grid, st, e0, e1);
     case 16: return dispatch_rb<QT, KV, D, 16>(a, rb, grid, st, e0, e1);
     case 32: return dispatch_rb<QT, KV, D, 32>(a, rb, grid, st, e0, e1);
     case 64: return dispatch_rb<QT, KV, D, 64>(a, rb, grid, st, e0, e1);

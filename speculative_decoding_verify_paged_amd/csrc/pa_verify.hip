@@ -54,7 +54,9 @@ int validate(const pa_verify_params* p, int32_t max_ctx, bool u8_entry) {
   const int G = p->num_q_heads / p->num_kv_heads;
   if (!is_pow2_in(G, 1, 8)) return PA_ERR_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256) return PA_ERR_UNSUPPORTED;
-  if (p->block_size != 16 && p->block_size != 32 && p->block_size != 64) return PA_ERR_UNSUPPORTED;
+  if (p->block_size != 1 && p->block_size != 2 && p->block_size != 4 && p->block_size != 8 &&
+      p->block_size != 16 && p->block_size != 32 && p->block_size != 64)
+    return PA_ERR_UNSUPPORTED;
   if (p->q_dtype != PA_F16 && p->q_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   if (u8_entry) {
     if (p->kv_dtype != PA_U8) return PA_ERR_UNSUPPORTED;
@@ -67,7 +69,8 @@ int validate(const pa_verify_params* p, int32_t max_ctx, bool u8_entry) {
   if (p->num_seqs > 65535 || p->num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;   // grid y, x limits
   if (p->max_query_len < 0) return PA_ERR_INVALID_ARG;
   if (p->max_query_len > pav::kMaxT) return PA_ERR_UNSUPPORTED;
-  if ((int64_t)G * query_bound(p) > (int64_t)pav::kRows * pav::max_row_blocks(p->kv_dtype, p->head_dim))
+  if ((int64_t)G * query_bound(p) >
+      (int64_t)pav::kRows * pav::max_row_blocks(p->kv_dtype, p->head_dim, p->block_size))
     return PA_ERR_UNSUPPORTED;
   if (p->tree_mask && p->sliding_window > 0) return PA_ERR_UNSUPPORTED;
   return PA_OK;
@@ -100,7 +103,7 @@ int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_ve
     // batch 1, and in a ragged batch the longest sequence is not left to a
     // few CUs), but at most kMaxRounds rounds of workgroups in all.
     const int64_t groups =
-        (int64_t)num_cus * pav::groups_per_cu(p->kv_dtype, p->head_dim, row_blocks(p));
+        (int64_t)num_cus * pav::groups_per_cu(p->kv_dtype, p->head_dim, row_blocks(p), p->block_size);
     const int64_t pairs = (int64_t)p->num_kv_heads * p->num_seqs;
     S = cdiv(groups, p->num_kv_heads);
     S = std::min(S, std::max<int64_t>(cdiv(groups, pairs), kMaxRounds * groups / pairs));

@@ -94,7 +94,8 @@ def call(p, max_ctx=32771, u8=False, null=None):
     (dict(sliding_window=-1), pav.PA_ERR_INVALID_ARG),
     (dict(num_segments=-2), pav.PA_ERR_INVALID_ARG),
     (dict(head_dim=96), pav.PA_ERR_UNSUPPORTED),
-    (dict(block_size=8, max_blocks_per_seq=5000), pav.PA_ERR_UNSUPPORTED),
+    (dict(block_size=12, max_blocks_per_seq=5000), pav.PA_ERR_UNSUPPORTED),
+    (dict(block_size=8, max_blocks_per_seq=5000, num_tokens=8, max_query_len=8), pav.PA_ERR_UNSUPPORTED),  # 32 rows, small pages
     (dict(num_q_heads=24, num_kv_heads=8), pav.PA_ERR_UNSUPPORTED),  # G = 3
     (dict(num_q_heads=128, num_kv_heads=8), pav.PA_ERR_UNSUPPORTED),  # G = 16
     (dict(kv_dtype=pav.PA_BF16), pav.PA_ERR_UNSUPPORTED),      # (f16, bf16) pair

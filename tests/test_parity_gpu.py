@@ -466,3 +466,59 @@ def test_append_contract_violation_writes_nothing():
         assert np.array_equal(kl2[blk, :, (40 + i) % 16], kl0[blk, :, (40 + i) % 16])
     blk = case.block_tables[1, 90 // 16]
     assert np.array_equal(kl2[blk, :, 90 % 16], klb[blk, :, 90 % 16])
+
+
+# ---------------------------------------------------------------------------
+# Pages of 1, 2, 4 or 8 slots (K row-major, V d-major per page)
+# ---------------------------------------------------------------------------
+def test_small_pages_all_instances():
+    rng = np.random.default_rng(141)
+    k = 0
+    for bs in (1, 2, 4, 8):
+        for D in (64, 128, 256):
+            for kv in (pi.F16, pi.BF16, pi.U8):
+                qd = pi.BF16 if kv == pi.BF16 else pi.F16 if k % 2 == 0 or kv == pi.F16 else pi.BF16
+                G = int(rng.choice([1, 2, 4]))
+                T = int(rng.integers(1, max(1, min(4, 16 // G)) + 1))
+                L = int(rng.choice([0, 3, 31, 70, int(rng.integers(0, 1500))]))
+                W = int(rng.choice([0, 0, 5, 100]))
+                case = pi.build_case([150, k], [L], [T], num_q_heads=2 * G, num_kv_heads=2,
+                                     head_dim=D, block_size=bs, q_dtype=qd, kv_dtype=kv,
+                                     sliding_window=W, spare_blocks=3, poison=True,
+                                     name=f"page{bs}_D{D}_kv{kv}_G{G}_T{T}_L{L}_W{W}")
+                _full(case, rounding_aware=True)
+                k += 1
+
+
+@pytest.mark.parametrize("bs", [1, 4, 8])
+def test_small_pages_32k(bs):
+    _sampled(pi.config2(32768, 3, block_size=bs), n=64)
+
+
+def test_small_pages_ragged_tree_u8():
+    case = pi.build_case([160], [900, 40, 2500], [4, 1, 3], num_q_heads=8, num_kv_heads=2,
+                         head_dim=128, block_size=2, q_dtype=pi.F16, kv_dtype=pi.U8,
+                         spare_blocks=4, poison=True, tree=True, name="page2_ragged_tree_u8")
+    _full(case, rounding_aware=True)
+
+
+def test_small_pages_append():
+    from oracle_pins import _blank_new_tokens
+    rng = np.random.default_rng(161)
+    for k, bs in enumerate((1, 2, 4, 8)):
+        case = pi.build_case([170, k], [33, 100], [3, 2], num_q_heads=4, num_kv_heads=2,
+                             head_dim=128, block_size=bs, q_dtype=pi.BF16, kv_dtype=pi.BF16,
+                             spare_blocks=2)
+        kn, vn, blank = _blank_new_tokens(case, rng)
+        k2, v2, _, _ = _append_gpu(blank, kn, vn, pi.BF16)
+        assert np.array_equal(k2, case.k_cache) and np.array_equal(v2, case.v_cache), bs
+        cu = pi.build_case([180, k], [60], [4], num_q_heads=4, num_kv_heads=2, head_dim=64,
+                           block_size=bs, q_dtype=pi.F16, kv_dtype=pi.U8, spare_blocks=2)
+        kf = pi.f32_to_bits(rng.standard_normal((4, 2, 64)), pi.F16)
+        vf = pi.f32_to_bits(rng.standard_normal((4, 2, 64)), pi.F16)
+        st, k_o, v_o, ks_o, vs_o = oracle.get().kv_append(cu, kf, vf, pi.F16)
+        assert st == 0
+        k3, v3, ks3, vs3 = _append_gpu(cu, kf, vf, pi.F16)
+        assert np.array_equal(k3, k_o) and np.array_equal(v3, v_o), bs
+        assert np.array_equal(ks3, ks_o) and np.array_equal(vs3, vs_o), bs
+
