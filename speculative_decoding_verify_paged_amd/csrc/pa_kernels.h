@@ -12,7 +12,7 @@ enum : int { kF16 = 0, kBF16 = 1, kU8 = 2 };
 constexpr int kKeysPerStep = 32;     // keys one wavefront consumes per iteration
 constexpr int kRows = 16;            // stacked query rows per MFMA tile (one row block)
 constexpr int kMaxT = 16;            // verify rows per sequence (tree-mask words are 16 bits used)
-constexpr int kWavesPerGroup = 4;    // wavefronts per segment workgroup
+constexpr int kWavesPerGroup = 4;    // wavefronts per segment workgroup (default of the table below)
 constexpr int kMaxSegBlocks = 1040;  // LDS slots for a segment's block ids
 constexpr int kDeviceContract = 5;   // value of PA_ERR_DEVICE_CONTRACT
 constexpr float kRescaleLog2 = 8.f;  // softmax reference max moves only past this margin
@@ -75,33 +75,36 @@ constexpr int combine_threads(int S, int D) {
   return S * (D / 4) <= 256 * 8 ? 256 : S * (D / 4) <= 512 * 8 ? 512 : 1024;
 }
 
-// Per (cache dtype, head_dim, row blocks): wavefronts per SIMD the segment
-// kernel is compiled for (its register budget, no spills), the steps each
-// wavefront keeps loaded (1: load then compute; 2: the next step's loads in
-// flight during this step's math), and the segment workgroups the planner
-// puts on each CU (at most the resident count, 4 SIMDs per CU).  u8 with
-// D = 256 runs two wavefronts per SIMD for latency hiding but one workgroup
-// per CU in the plan: twice the segments only doubles the partials the
-// combine reads (measured on MI355X: no faster segment kernel, slower call).
-// More than one row block needs the whole register file of one wavefront
-// per SIMD (and its LDS merge buffer allows one workgroup per CU).
+// Per (cache dtype, head_dim, row blocks, block size): wavefronts per SIMD
+// the segment kernel is compiled for (its register budget, no spills), the
+// steps each wavefront keeps loaded (1: load then compute; 2: the next
+// step's loads in flight during this step's math), the segment workgroups
+// the planner puts on each CU (at most the resident count, 4 SIMDs per CU)
+// and the wavefronts per workgroup.  Measured on MI355X at 32k context:
+// head_dim 128 (16-bit) and u8 head_dim 256 run best as one 8-wavefront
+// workgroup per CU, two wavefronts per SIMD with one step each (C2 shape
+// 27.6 vs 28.2 µs per call for 4 wavefronts with two steps each; u8 21.4 vs
+// 22.5 µs) — two workgroups of 4 instead would double the partials the
+// combine reads.  More than one row block needs the whole register file of
+// one wavefront per SIMD (and its LDS merge buffer allows one workgroup per
+// CU).
 struct SegConfig {
   int waves_per_simd;
   int prefetch;
   int groups_per_cu;
+  int waves_per_group = kWavesPerGroup;
 };
 constexpr SegConfig seg_config(int kv_dtype, int D, int rb, int bs = 16) {
   // pages of fewer than 16 slots gather per lane (more address registers)
   if (bs < 16) return D >= 256 ? SegConfig{1, 1, 1} : SegConfig{2, 1, 2};
   if (rb > 1) return SegConfig{1, 1, 1};
   if (kv_dtype == kU8)
-    return D >= 256 ? SegConfig{2, 1, 1} : D >= 128 ? SegConfig{1, 2, 1} : SegConfig{4, 1, 4};
-  return D >= 256 ? SegConfig{1, 1, 1} : D >= 128 ? SegConfig{1, 2, 1} : SegConfig{4, 1, 4};
+    return D >= 256 ? SegConfig{2, 1, 1, 8} : D >= 128 ? SegConfig{1, 2, 1} : SegConfig{4, 1, 4};
+  return D >= 256 ? SegConfig{1, 1, 1} : D >= 128 ? SegConfig{2, 1, 1, 8} : SegConfig{4, 1, 4};
 }
 constexpr int groups_per_cu(int kv_dtype, int D, int rb, int bs) {
   return seg_config(kv_dtype, D, rb, bs).groups_per_cu;
 }
-static_assert(kWavesPerGroup == 4, "the table above assumes 4-wavefront workgroups");
 // Row blocks built per (cache dtype, head_dim): each adds D/4 accumulator
 // and D/8 query registers per lane and 16 * (D + 4) * 16 B of LDS; these are
 // the largest counts that compile without register spills.

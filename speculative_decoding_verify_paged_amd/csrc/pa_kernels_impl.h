@@ -802,12 +802,13 @@ void pa_segment(SegmentArgs a) {
 template <int QT, int KV, int D, int BS, int RB>
 hipError_t launch_seg(const SegmentArgs& a, dim3 grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   constexpr SegConfig c = seg_config(KV, D, RB, BS);
-  constexpr auto kern = pa_segment<QT, KV, D, BS, kWavesPerGroup, c.waves_per_simd, c.prefetch, RB>;
+  static_assert(c.waves_per_group <= 4 * c.waves_per_simd, "a workgroup must fit on one CU");
+  constexpr auto kern = pa_segment<QT, KV, D, BS, c.waves_per_group, c.waves_per_simd, c.prefetch, RB>;
   // with events, the dispatch itself timestamps the kernel's start and end
   if (ev0 || ev1)
-    hipExtLaunchKernelGGL(kern, grid, dim3(kWavesPerGroup * kWave), 0, st, ev0, ev1, 0, a);
+    hipExtLaunchKernelGGL(kern, grid, dim3(c.waves_per_group * kWave), 0, st, ev0, ev1, 0, a);
   else
-    hipLaunchKernelGGL(kern, grid, dim3(kWavesPerGroup * kWave), 0, st, a);
+    hipLaunchKernelGGL(kern, grid, dim3(c.waves_per_group * kWave), 0, st, a);
   return hipGetLastError();
 }
 

@@ -19,7 +19,6 @@
 namespace {
 
 using pav::kKeysPerStep;
-using pav::kWavesPerGroup;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -117,11 +116,12 @@ int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_ve
   pl->row_blocks = row_blocks(p);
   pl->keys_per_step = kKeysPerStep;
   pl->span = (int32_t)span;
-  pl->waves_per_group = kWavesPerGroup;
+  const int nw = pav::seg_config(p->kv_dtype, p->head_dim, pl->row_blocks, p->block_size).waves_per_group;
+  pl->waves_per_group = nw;
   pl->grid[0] = p->num_kv_heads;
   pl->grid[1] = p->num_seqs;
   pl->grid[2] = (int32_t)S;
-  pl->block_threads = kWavesPerGroup * 64;
+  pl->block_threads = nw * 64;
   const int64_t rows = (int64_t)p->num_tokens * p->num_q_heads;
   pl->combine_grid[0] = (int32_t)rows;
   pl->combine_grid[1] = 1;
