@@ -12,8 +12,8 @@ value = algorithmic KV bytes of one call / device time per call (GB/s), the
 calls replayed from a HIP graph so host launch overhead is excluded (the
 eager per-call time is reported beside it).
 roofline = the segment kernel's algorithmic KV bytes / its own average
-duration from HIP events recorded around it in the timed region, against
-MI355X's 8 TB/s HBM peak.  cpu_baseline = the fp64 oracle timed on the host
+duration from HIP events its dispatch stamps (every 4th call of an eager
+timed loop that keeps the GPU busy), against MI355X's 8 TB/s HBM peak.  cpu_baseline = the fp64 oracle timed on the host
 cores over a bounded sample of the same call.
 """
 from __future__ import annotations
@@ -151,17 +151,21 @@ class Runner:
         del g
         return statistics.median(per_call), per_call
 
-    def time(self, steps, warmup, repeats):
+    def time(self, steps, warmup, repeats, stamp_every=4):
         """Eager launches: median µs per call and the segment kernel's mean
-        duration from events its own dispatch stamps, over `repeats` regions."""
+        duration from events its own dispatch stamps, over `repeats` regions.
+        Every `stamp_every`-th call carries the events: a dispatch with events
+        costs the host ~25 µs, so stamping every call would leave the GPU
+        idle between calls instead of running them back to back."""
         import torch
         for i in range(warmup):
             self.call(i)
         torch.cuda.synchronize()
         per_call, per_kernel = [], []
-        evb = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        eve = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        for e in evb + eve:
+        stamped = list(range(stamp_every - 1, steps, stamp_every))
+        evb = {i: torch.cuda.Event(enable_timing=True) for i in stamped}
+        eve = {i: torch.cuda.Event(enable_timing=True) for i in stamped}
+        for e in list(evb.values()) + list(eve.values()):
             e.record(self.stream)           # create the underlying hipEvent
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
@@ -170,12 +174,11 @@ class Runner:
             torch.cuda.synchronize()
             t0.record(self.stream)
             for i in range(steps):
-                self.call(i, prof=(evb[i].cuda_event, eve[i].cuda_event))
+                self.call(i, prof=(evb[i].cuda_event, eve[i].cuda_event) if i in evb else None)
             t1.record(self.stream)
             torch.cuda.synchronize()
             per_call.append(t0.elapsed_time(t1) * 1000.0 / steps)
-            per_kernel.append(statistics.mean(evb[i].elapsed_time(eve[i]) * 1000.0
-                                              for i in range(steps)))
+            per_kernel.append(statistics.mean(evb[i].elapsed_time(eve[i]) * 1000.0 for i in stamped))
         return statistics.median(per_call), statistics.median(per_kernel), per_call
 
 
