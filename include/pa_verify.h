@@ -144,10 +144,17 @@ typedef struct pa_verify_plan {
                                   covers steps [j*N/S, (j+1)*N/S) of num_steps = N */
   int32_t num_steps;           /* N: steps covering span */
   int32_t row_blocks;          /* 16-row blocks of stacked query rows the kernel is built with */
+  int32_t worklist;            /* 1 for a batch of several sequences: the grid is
+                                  (Hkv, 1, chunks) and each workgroup takes one chunk of a
+                                  work list the device builds from the sequence lengths
+                                  (chunk size chosen so the chunks fill one round of
+                                  target_items workgroups per KV head); 0: fixed segments */
+  int32_t target_items;        /* work-list chunks per KV head the chunk size aims at */
   int32_t keys_per_step;       /* keys one wavefront consumes per loop iteration */
   int32_t span;                /* bound on keys any one sequence's rows touch */
   int32_t waves_per_group;     /* wavefronts per segment workgroup */
-  int32_t grid[3];             /* segment kernel grid: (Hkv, num_seqs, S); z = S-1-j */
+  int32_t grid[3];             /* segment kernel grid: (Hkv, num_seqs, S), z = S-1-j; work
+                                  list: (Hkv, 1, chunks) */
   int32_t block_threads;       /* segment kernel workgroup size */
   int32_t combine_grid[3];     /* combine kernel grid */
   int32_t combine_threads;     /* combine kernel workgroup size */

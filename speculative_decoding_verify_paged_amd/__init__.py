@@ -52,6 +52,7 @@ class PaVerifyPlan(ctypes.Structure):
     _fields_ = [
         ("num_segments", ctypes.c_int32), ("steps_per_segment", ctypes.c_int32),
         ("num_steps", ctypes.c_int32), ("row_blocks", ctypes.c_int32),
+        ("worklist", ctypes.c_int32), ("target_items", ctypes.c_int32),
         ("keys_per_step", ctypes.c_int32), ("span", ctypes.c_int32),
         ("waves_per_group", ctypes.c_int32), ("grid", ctypes.c_int32 * 3),
         ("block_threads", ctypes.c_int32), ("combine_grid", ctypes.c_int32 * 3),

@@ -34,6 +34,9 @@ struct SegmentArgs {
   int32_t num_blocks, mbps, window, max_ctx;
   int32_t max_q;                     // bound on T_s the host planned for (<= kMaxT)
   int32_t S, steps_per_seg, n_steps;   // segments; max steps of one segment; steps the host plans for
+  int32_t worklist;                  // ragged batch: chunks of device-chosen size, see below
+  int32_t target_items;              // work-list chunks per KV head the chunk size aims at
+  int32_t max_sps;                   // most steps whose block ids fit the LDS table
   float scale_log2;                  // scale * log2(e)
 };
 

@@ -183,6 +183,97 @@ __device__ __forceinline__ SeqInfo seq_info(const SegmentArgs& a, int s, int row
 }
 
 // ---------------------------------------------------------------------------
+// Work list of a ragged batch.  Every sequence's steps are cut into chunks
+// of C steps; C is the smallest size (not below the host's steps per
+// segment, nor above what the LDS block-id table holds) whose chunks of all
+// sequences fit the target count of workgroups per KV head, so one round of
+// equal workgroups covers the batch however its lengths are spread.  A sequence that breaks the contract gets one chunk
+// (it writes NaN partials).  Computed redundantly and identically by every
+// wavefront of every workgroup from the sequence metadata.  Wave-wide.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int wl_steps(const SegmentArgs& a, int seq, int rows, bool& ok) {
+  const SeqInfo q = seq_info(a, seq, rows);
+  ok = q.ok;
+  return q.n_steps;
+}
+
+// chunks of all sequences for chunk size C
+__device__ __forceinline__ int wl_count(const SegmentArgs& a, int rows, int C) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int n = 0;
+  for (int b = 0; b < a.num_seqs; b += kWave) {
+    const int k = b + lane;
+    if (k < a.num_seqs) {
+      bool ok;
+      const int st = wl_steps(a, k, rows, ok);
+      n += ok ? (st + C - 1) / C : 1;
+    }
+  }
+  for (int m = 1; m < kWave; m <<= 1) n += __shfl_xor(n, m, kWave);
+  return n;
+}
+
+__device__ __forceinline__ int wl_chunk(const SegmentArgs& a, int rows) {
+  const int lane = threadIdx.x & (kWave - 1);
+  long long total = 0;
+  int longest = 1;
+  for (int b = 0; b < a.num_seqs; b += kWave) {
+    const int k = b + lane;
+    if (k < a.num_seqs) {
+      bool ok;
+      const int st = wl_steps(a, k, rows, ok);
+      total += st;
+      longest = max(longest, st);
+    }
+  }
+  for (int m = 1; m < kWave; m <<= 1) {
+    total += __shfl_xor(total, m, kWave);
+    longest = max(longest, __shfl_xor(longest, m, kWave));
+  }
+  const long long want = (total + a.target_items - 1) / a.target_items;
+  int hi = max(1, min(longest, a.max_sps));               // a chunk's block ids fit LDS
+  int lo = (int)min<long long>(max<long long>(a.steps_per_seg, want), hi);
+  lo = max(lo, 1);
+  if (wl_count(a, rows, hi) > a.target_items) return hi;   // the fewest chunks possible
+  while (lo < hi) {                                         // smallest C that fits
+    const int mid = lo + (hi - lo) / 2;
+    if (wl_count(a, rows, mid) <= a.target_items) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
+
+// the sequence holding chunk number `item` (in sequence order), and the
+// chunk's index inside it; -1 when item is past the last chunk
+__device__ __forceinline__ int wl_find(const SegmentArgs& a, int rows, int C, int item, int& chunk) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int base = 0;
+  for (int b = 0; b < a.num_seqs; b += kWave) {
+    const int k = b + lane;
+    int items = 0;
+    if (k < a.num_seqs) {
+      bool ok;
+      const int st = wl_steps(a, k, rows, ok);
+      items = ok ? (st + C - 1) / C : 1;
+    }
+    int inc = items;
+    for (int m = 1; m < kWave; m <<= 1) {
+      const int v = __shfl_up(inc, m, kWave);
+      if (lane >= m) inc += v;
+    }
+    const int excl = inc - items;
+    const unsigned long long hit = __ballot(k < a.num_seqs && item >= base + excl && item < base + inc);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      chunk = item - base - __shfl(excl, l, kWave);
+      return b + l;
+    }
+    base += __shfl(inc, kWave - 1, kWave);
+  }
+  chunk = 0;
+  return -1;
+}
+
+// ---------------------------------------------------------------------------
 // Segment kernel.  QT: dtype of q (and of the MFMA operands); KV: cache dtype
 // (QT, or kU8 for codes with per-token f16 scale and zero point); RB: 16-row
 // blocks of stacked query rows (G * T <= 16 * RB): each K/V operand a step
@@ -214,22 +305,39 @@ void pa_segment(SegmentArgs a) {
   // Grid (Hkv, num_seqs, S), segments last and in reverse: the launch
   // starts with the highest segments, which only the longest sequences of a
   // ragged batch have, so their work is not left for the final round.
-  const int h = blockIdx.x, s = blockIdx.y, j = a.S - 1 - (int)blockIdx.z;
+  // A ragged batch (work-list mode) instead has grid (Hkv, 1, chunks) and
+  // takes its sequence and steps from the work list.
+  const int h = blockIdx.x;
+  int s, j, st_begin, st_cap, wl_items = 0;
+  if (!a.worklist) {
+    s = blockIdx.y;
+    j = a.S - 1 - (int)blockIdx.z;
+    // Segment j owns steps [j*N/S, (j+1)*N/S) of the N steps planned on the
+    // host: segment lengths differ by at most one step.
+    st_begin = (int)(((int64_t)j * a.n_steps) / a.S);
+    st_cap = (int)(((int64_t)(j + 1) * a.n_steps) / a.S);
+  } else {
+    const int C = wl_chunk(a, ROWS);
+    s = wl_find(a, ROWS, C, (int)blockIdx.z, j);
+    if (s < 0) return;                                        // past the last chunk (uniform)
+    bool ok;
+    const int st = wl_steps(a, s, ROWS, ok);
+    wl_items = ok ? (st + C - 1) / C : 1;
+    st_begin = j * C;
+    st_cap = st_begin + C;
+  }
   const int32_t* bt_row = a.bt + (size_t)s * a.mbps;
 
-  // Full-causal layers: segment j's block range does not depend on the
-  // sequence's length, so its block ids are requested together with the
-  // sequence metadata — one memory round trip before the first KV load
-  // instead of two.  The loads stay inside the block-table row; ids of
-  // blocks past the sequence are never used.
+  // Full-causal layers with a fixed segment grid: segment j's block range
+  // does not depend on the sequence's length, so its block ids are
+  // requested together with the sequence metadata — one memory round trip
+  // before the first KV load instead of two.  The loads stay inside the
+  // block-table row; ids of blocks past the sequence are never used.
   constexpr int kSlots = (kMaxSegBlocks + NW * kWave - 1) / (NW * kWave);
-  // Segment j owns steps [j*N/S, (j+1)*N/S) of the N steps planned on the
-  // host: segment lengths differ by at most one step.
-  const int st_begin = (int)(((int64_t)j * a.n_steps) / a.S);
-  const int st_cap = (int)(((int64_t)(j + 1) * a.n_steps) / a.S);
   int spec_id[kSlots];
   const int spec_lo = (st_begin * kKeysPerStep) / BS;
-  const int spec_n = a.window == 0 ? min(a.mbps - spec_lo, (a.steps_per_seg * kKeysPerStep) / BS + 1) : 0;
+  const bool spec = a.window == 0 && !a.worklist;
+  const int spec_n = spec ? min(a.mbps - spec_lo, (a.steps_per_seg * kKeysPerStep) / BS + 1) : 0;
 #pragma unroll
   for (int k = 0; k < kSlots; ++k) {
     const int x = threadIdx.x + k * NW * kWave;
@@ -244,12 +352,26 @@ void pa_segment(SegmentArgs a) {
     if (j == 0 && h == 0 && threadIdx.x == 0) atomicExch(a.status, kDeviceContract);
     const int t0 = min(max(si.b0, 0), a.num_tokens);
     const int t1 = min(max(si.b0 + si.T, t0), a.num_tokens);
-    for (int x = threadIdx.x; x < (t1 - t0) * a.G; x += NW * kWave) {
-      const size_t row = ((size_t)(t0 + x / a.G) * a.Hq + h * a.G + x % a.G) * a.S + j;
+    // work-list mode: the sequence's only chunk marks all its slots
+    const int nj = a.worklist ? a.S : 1;
+    for (int x = threadIdx.x; x < (t1 - t0) * a.G * nj; x += NW * kWave) {
+      const int jj = a.worklist ? x % nj : j, y = x / nj;
+      const size_t row = ((size_t)(t0 + y / a.G) * a.Hq + h * a.G + y % a.G) * a.S + jj;
       a.ws_ml[row * 2 + 0] = NAN;
       a.ws_ml[row * 2 + 1] = 0.f;
     }
     return;
+  }
+  if (a.worklist && j == 0) {
+    // slots past the sequence's chunks hold no partial: mark them empty so
+    // the combine reads all S slots without knowing the chunk size
+    const int R0 = a.G * si.T, nj = a.S - wl_items;
+    for (int x = threadIdx.x; x < R0 * nj; x += NW * kWave) {
+      const int r = x / nj, jj = wl_items + x % nj;
+      const size_t row = ((size_t)(si.b0 + r % si.T) * a.Hq + h * a.G + r / si.T) * a.S + jj;
+      a.ws_ml[row * 2 + 0] = -INFINITY;
+      a.ws_ml[row * 2 + 1] = 0.f;
+    }
   }
   const int T = si.T;
   const int R = a.G * T;
@@ -280,7 +402,7 @@ void pa_segment(SegmentArgs a) {
       const int b = blk_lo + x;
       int id = 0;
       if ((b + 1) * BS > si.lo0) {
-        id = a.window == 0 ? spec_id[k] : bt_row[b];
+        id = spec ? spec_id[k] : bt_row[b];
         if ((unsigned)id >= (unsigned)a.num_blocks) {
           s_bad = 1;
           id = 0;

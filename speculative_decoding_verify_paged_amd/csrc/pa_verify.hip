@@ -121,6 +121,18 @@ int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_ve
   pl->grid[0] = p->num_kv_heads;
   pl->grid[1] = p->num_seqs;
   pl->grid[2] = (int32_t)S;
+  pl->worklist = p->num_seqs > 1 ? 1 : 0;
+  pl->target_items = (int32_t)std::max<int64_t>(
+      1, cdiv((int64_t)num_cus * pav::groups_per_cu(p->kv_dtype, p->head_dim, pl->row_blocks,
+                                                    p->block_size), p->num_kv_heads));
+  if (pl->worklist) {
+    // a ragged batch: one workgroup per work-list chunk, at most
+    // max(target, every sequence at its fewest chunks)
+    const int64_t most = std::max<int64_t>(pl->target_items, (int64_t)p->num_seqs * cdiv(n_steps, max_sps));
+    if (most > 65535) return PA_ERR_UNSUPPORTED;
+    pl->grid[1] = 1;
+    pl->grid[2] = (int32_t)most;
+  }
   pl->block_threads = nw * 64;
   const int64_t rows = (int64_t)p->num_tokens * p->num_q_heads;
   pl->combine_grid[0] = (int32_t)rows;
@@ -219,6 +231,9 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
   a.S = pl.num_segments;
   a.steps_per_seg = pl.steps_per_segment;
   a.n_steps = pl.num_steps;
+  a.worklist = pl.worklist;
+  a.target_items = pl.target_items;
+  a.max_sps = (int32_t)(((int64_t)(pav::kMaxSegBlocks - 2) * p->block_size) / pav::kKeysPerStep);
   a.scale_log2 = scale * 1.4426950408889634f;
 
   hipStream_t st = static_cast<hipStream_t>(p->stream);

@@ -171,7 +171,11 @@ def check_plan_covers(pl, max_ctx, window=0, nseq=1, hkv=8, bs=16, tq=4):
     lens = [(j + 1) * steps // S - j * steps // S for j in range(S)]
     assert sum(lens) == steps and min(lens) >= 1 and max(lens) - min(lens) <= 1
     assert pl["steps_per_segment"] == max(lens)
-    assert pl["grid"] == [hkv, nseq, S]
+    if nseq == 1:
+        assert pl["grid"] == [hkv, 1, S] and pl["worklist"] == 0
+    else:   # work list: one workgroup per chunk, at least one round of them
+        assert pl["worklist"] == 1 and pl["grid"][:2] == [hkv, 1]
+        assert pl["grid"][2] >= pl["target_items"]
     assert pl["steps_per_segment"] * pl["keys_per_step"] // bs + 2 <= 1040
 
 
