@@ -129,6 +129,27 @@ def test_small_ragged_batches():
         _full(pi.config5(rep=rep, lo=1, hi=3000, poison=True), rounding_aware=True)
 
 
+def test_work_list_shapes():
+    """Batches of several sequences take their steps from the device-side
+    work list: more than one 64-lane pass over the sequences, chunk sizes
+    capped by the block-id table (1-slot pages), more sequences than
+    workgroup slots, equal lengths, and one long sequence among many short."""
+    rng = np.random.default_rng(191)
+    shapes = [
+        ("many150_bs16", [int(x) for x in rng.integers(0, 2000, 150)], 16, 64, pi.F16),
+        ("bs1_long", [int(x) for x in rng.integers(2000, 5000, 5)] + [0, 7, 40], 1, 128, pi.BF16),
+        ("tiny600", [int(x) for x in rng.integers(0, 40, 600)], 16, 64, pi.BF16),
+        ("equal8", [4096] * 8, 16, 128, pi.F16),
+        ("one_long", [30000] + [int(x) for x in rng.integers(0, 300, 40)], 32, 128, pi.BF16),
+    ]
+    for k, (nm, Ls, bs, D, dt) in enumerate(shapes):
+        Ts = [int(t) for t in rng.integers(1, 5, len(Ls))]
+        case = pi.build_case([190, k], Ls, Ts, num_q_heads=8, num_kv_heads=2, head_dim=D,
+                             block_size=bs, q_dtype=dt, kv_dtype=dt, spare_blocks=3,
+                             poison=True, name=f"worklist_{nm}")
+        _full(case, rounding_aware=True)
+
+
 @pytest.mark.parametrize("S", [1, 2, 7, 0, 10 ** 6])
 def test_segment_count_invariance(S):
     case = pi.config2(8192, 3)
