@@ -198,7 +198,8 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
   rc = device_cus(&cus);
   if (rc) return rc;
   pa_verify_plan pl;
-  make_plan(p, max_ctx, cus, &pl);
+  rc = make_plan(p, max_ctx, cus, &pl);                      // grid limits
+  if (rc) return rc;
   if (!p->workspace || p->workspace_bytes < pl.workspace_bytes) return PA_ERR_WORKSPACE;
   maybe_log(p, pl, max_ctx);
 
@@ -313,7 +314,7 @@ size_t pa_verify_workspace_bytes(const pa_verify_params* p, int32_t max_context_
   int cus = 0;
   if (device_cus(&cus)) return 0;
   pa_verify_plan pl;
-  make_plan(p, max_context_len, cus, &pl);
+  if (make_plan(p, max_context_len, cus, &pl)) return 0;
   return pl.workspace_bytes;
 }
 

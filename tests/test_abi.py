@@ -243,3 +243,22 @@ def test_plan_long_context_respects_lds_block_limit():
 def test_plan_ragged_batch():
     pl = plan(131072, num_seqs=8, num_tokens=20, max_blocks_per_seq=8192, num_blocks=60000)
     check_plan_covers(pl, 131072, nseq=8)
+
+
+def test_plan_grid_limits_are_reported():
+    # 1-slot pages hold 32 steps per segment in the block-id table: 100M keys
+    # need more than 65535 segments (the grid's z limit)
+    big = 100_000_000
+    with pytest.raises(pav.PaVerifyError) as e:
+        plan(big, block_size=1, max_blocks_per_seq=big, num_blocks=1 << 20)
+    assert e.value.code == pav.PA_ERR_UNSUPPORTED
+    # a batch whose worst case needs more than 65535 work-list chunks
+    n = 3000
+    with pytest.raises(pav.PaVerifyError) as e:
+        plan(100_000, block_size=1, max_blocks_per_seq=100_000, num_blocks=1 << 20,
+             num_seqs=n, num_tokens=n)
+    assert e.value.code == pav.PA_ERR_UNSUPPORTED
+    # just inside the limits
+    pl = plan(100_000, block_size=1, max_blocks_per_seq=100_000, num_blocks=1 << 20,
+              num_seqs=600, num_tokens=600)
+    assert pl["grid"][2] == 600 * -(-3125 // 32) and pl["grid"][2] <= 65535
