@@ -2,7 +2,10 @@
 // shared by the per-dtype translation units pa_segment_*.hip and pa_combine.hip).
 //
 // Two kernels per call:
-//   1. pa_segment: one workgroup per (KV segment j, KV head, sequence).  Its
+//   1. pa_segment: one workgroup per (KV segment j, KV head, sequence) — for
+//      a batch of several sequences, per (work-list chunk, KV head), a chunk
+//      being a run of one sequence's steps whose size the device picks from
+//      the lengths so the chunks fill one round of workgroups.  Its
 //      wavefronts stream the segment's K/V page tiles straight from HBM into
 //      MFMA operand registers, each tile read once for all G*T stacked query
 //      rows of the GQA group, and keep an online softmax.  The workgroup
@@ -28,6 +31,8 @@
 //   K: [d/32][(d%32)/8][slot%16][d%8]          (u8: [d/64][(d%64)/16][slot%16][d%16])
 //   V: [d/32][(slot%16)/4][d%16][(d%32)/16][slot%4]
 //                                               (u8: [d/64][(slot%16)/4][d%16][(d%64)/16][slot%4])
+// Pages of 1, 2, 4 or 8 slots hold K row-major [slot][d] and V d-major
+// [d][slot]; each lane gathers its own operand pieces from them.
 //
 // Data path of one wavefront step (32 keys = two sub-tiles, stacked rows
 // r = g*T + i padded to 16):
