@@ -300,8 +300,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU: this build measures the single-GPU kernel and has no "
-              f"multi-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)
+        print(f"bench.py measures one GPU: the library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
 
     import torch

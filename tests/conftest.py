@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped only when no GPU is visible at all; on a GPU machine a
+    # GPU tests are skipped only when no GPU is visible at all; with a GPU a
     # missing or broken library makes them fail, never fall back.
     try:
         import torch

@@ -141,7 +141,7 @@ def test_append_host_errors():
 
 
 def test_missing_workspace_is_reported_before_any_launch():
-    # valid arguments, no workspace: PA_ERR_WORKSPACE on a GPU machine, PA_ERR_HIP
+    # valid arguments, no workspace: PA_ERR_WORKSPACE with a GPU, PA_ERR_HIP
     # (no device to size the plan for) here; nothing is enqueued either way
     assert call(params()) in (pav.PA_ERR_WORKSPACE, pav.PA_ERR_HIP)
 
