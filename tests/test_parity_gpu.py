@@ -543,3 +543,38 @@ def test_small_pages_append():
         assert np.array_equal(k3, k_o) and np.array_equal(v3, v_o), bs
         assert np.array_equal(ks3, ks_o) and np.array_equal(vs3, vs_o), bs
 
+
+
+# ---------------------------------------------------------------------------
+# Feature combinations drawn at random (fixed seed): every cache dtype, head
+# dim, page size, group size, window, tree masks, ragged batches and forced
+# segment counts, mixed in ways the targeted tests above do not list.
+# ---------------------------------------------------------------------------
+def _max_rows(kv, D, bs):
+    if bs < 16:
+        return 16
+    return 16 * (4 if D <= 64 else 3 if D <= 128 else 2 if kv == pi.U8 else 1)
+
+
+def test_random_feature_combinations():
+    rng = np.random.default_rng(2024)
+    for k in range(40):
+        D = int(rng.choice([64, 128, 256]))
+        kv = int(rng.choice([pi.F16, pi.BF16, pi.U8]))
+        qd = kv if kv != pi.U8 else int(rng.choice([pi.F16, pi.BF16]))
+        bs = int(rng.choice([1, 2, 4, 8, 16, 16, 32, 64]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        Hkv = int(rng.choice([1, 2, 3]))
+        tmax = max(1, min(16, _max_rows(kv, D, bs) // G))
+        nseq = int(rng.integers(1, 7))
+        Ts = [int(t) for t in rng.integers(1, tmax + 1, nseq)]
+        Ls = [int(np.exp(rng.uniform(0, np.log(3000)))) - 1 for _ in range(nseq)]
+        tree = bool(rng.random() < 0.3)
+        W = 0 if tree else int(rng.choice([0, 0, 1, 17, 300]))
+        S = int(rng.choice([0, 0, 0, 1, 3, 50]))
+        case = pi.build_case([800, k], Ls, Ts, num_q_heads=G * Hkv, num_kv_heads=Hkv,
+                             head_dim=D, block_size=bs, q_dtype=qd, kv_dtype=kv,
+                             sliding_window=W, spare_blocks=2, poison=True, tree=tree,
+                             name=f"combo{k}_D{D}_kv{kv}_q{qd}_bs{bs}_G{G}_H{Hkv}_T{Ts}_W{W}"
+                                  f"_S{S}" + ("_tree" if tree else ""))
+        _full(case, rounding_aware=True, num_segments=S)
