@@ -51,6 +51,8 @@
  *     V f16/bf16: (((((s/16)*(D/32) + d/32)*4 + (s%16)/4)*16 + d%16)*2 + (d%32)/16)*4 + s%4
  *     K u8:       ((((s/16)*(D/64) + d/64)*4 + (d%64)/16)*16 + s%16)*16 + d%16
  *     V u8:       (((((s/16)*(D/64) + d/64)*4 + (s%16)/4)*16 + d%16)*4 + (d%64)/16)*4 + s%4
+ *                Pages of 1, 2, 4 or 8 slots hold K row-major (s*D + d) and V
+ *                d-major (d*block_size + s), for every cache dtype.
  *  k_scale_zp,   [num_blocks, Hkv, block_size, 2]     f16 (scale, zero_point) per
  *  v_scale_zp    token per KV head, u8 variant only; dequant = (u - zp) * scale
  *  block_tables  [num_seqs, max_blocks_per_seq] int32 physical block ids
@@ -98,11 +100,12 @@ typedef enum pa_dtype {
 } pa_dtype;
 
 /* Sizes and options of one call.  Supported: head_dim in {64, 128, 256},
- * block_size in {16, 32, 64}, group size G = Hq/Hkv in {1, 2, 4, 8}, dtype
- * pairs (q, kv) = (f16, f16), (bf16, bf16), (f16, u8), (bf16, u8), and up to
- * 16 new tokens per sequence with G * max_query_len <= 64 stacked rows
- * (<= 32 for head_dim 256); T_s <= max_query_len is checked per sequence on
- * the device. */
+ * block_size in {1, 2, 4, 8, 16, 32, 64}, group size G = Hq/Hkv in
+ * {1, 2, 4, 8}, dtype pairs (q, kv) = (f16, f16), (bf16, bf16), (f16, u8),
+ * (bf16, u8), and up to 16 new tokens per sequence with G * max_query_len
+ * stacked rows of at most 64 for head_dim 64, 48 for 128, 32 for u8 at 256
+ * and 16 for f16/bf16 at 256 (16 for every head_dim when block_size < 16);
+ * T_s <= max_query_len is checked per sequence on the device. */
 typedef struct pa_verify_params {
   int32_t num_seqs;            /* sequences in the batch, 1 ..= 65535 */
   int32_t num_tokens;          /* == subsequence_begins[num_seqs], >= num_seqs */
