@@ -43,6 +43,7 @@ def workloads():
         "gqa4_d128_f16_L8192": lambda T: pi.config2(8192, T),
         "gqa4_d128_f16_L32768_tree": lambda T: pi.config2(32768, T, tree=True),
         "gqa4_d128_f16_L32768_bs1": lambda T: pi.config2(32768, T, block_size=1),
+        "gqa4_d128_f16_L32768_bs2": lambda T: pi.config2(32768, T, block_size=2),
         "gqa4_d128_f16_L32768_bs4": lambda T: pi.config2(32768, T, block_size=4),
         "gqa4_d128_f16_L32768_bs8": lambda T: pi.config2(32768, T, block_size=8),
         "u8kv_d256_L32768": lambda T: pi.config3(32768, T),
