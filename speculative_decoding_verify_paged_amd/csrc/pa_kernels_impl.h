@@ -152,6 +152,10 @@ __device__ __forceinline__ u32x2 u8x4_to_16(uint32_t w) {
   }
 }
 
+// Wait for this wavefront's LDS operations; the memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ float xor_max(float v, int m) {
   return fmaxf(v, __shfl_xor(v, m, kWave));
 }
@@ -302,6 +306,15 @@ void pa_segment(SegmentArgs a) {
   __shared__ float s_l[NW][ROWS];
   __shared__ __attribute__((aligned(16))) float s_o[NW][ROWS][OSTRIDE];
   __shared__ int s_bad;
+  // Pages of 1 or 2 slots: V is loaded as whole page rows (1 KB per
+  // instruction) and turned into the PV operand layout through this
+  // per-wavefront LDS area: each sub-tile's 16/BS pages, page-major, each
+  // padded by 16 B against bank conflicts.
+  constexpr bool WIDE_V = BS <= 2;
+  constexpr int kPageBytes = BS * D * EB;                 // one page of one KV head
+  constexpr int kPagePad = kPageBytes + 16;
+  constexpr int kVtTau = (16 / BS) * kPagePad;           // one sub-tile
+  __shared__ __attribute__((aligned(16))) char s_vt[WIDE_V ? NW * 2 * kVtTau : 16];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -548,9 +561,21 @@ void pa_segment(SegmentArgs a) {
       auto vaddr = [&](int pc, int d) {
         return vb + ((((size_t)pg[pc] * Hkv + h) * BS * D) + (size_t)d * BS + row[pc]) * EB;
       };
-      if constexpr (U8) {
+      if constexpr (WIDE_V) {
+        // load c covers bytes [1024 c, 1024 c + 1024) of the sub-tile's pages
+        // laid end to end: lane i reads 16 B of page (1024 c + 16 i) / page size
+        static_assert(16 * D * EB == LV * 1024, "one 1 KB load per register of the step");
 #pragma unroll
         for (int c = 0; c < LV; ++c) {
+          const int L = c * 1024 + lane * 16;
+          int wpg, wrow;                                      // wrow is 0: pages start at 16-slot bounds
+          page_row(t0 + (L / kPageBytes) * BS, BS, wpg, wrow);
+          r.v[tau][c] = ld16_stream(vb + ((size_t)wpg * Hkv + h) * kPageBytes + L % kPageBytes);
+        }
+      }
+      if constexpr (U8) {
+#pragma unroll
+        for (int c = 0; c < (WIDE_V ? 0 : LV); ++c) {
 #pragma unroll
           for (int jd = 0; jd < 4; ++jd) {
             const int d = c * 64 + jd * 16 + n16;
@@ -586,7 +611,7 @@ void pa_segment(SegmentArgs a) {
         r.vs[tau] = vs;
       } else {
 #pragma unroll
-        for (int dp = 0; dp < LV; ++dp) {
+        for (int dp = 0; dp < (WIDE_V ? 0 : LV); ++dp) {
           u32x2 half[2];
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
@@ -646,7 +671,72 @@ void pa_segment(SegmentArgs a) {
     c_run[rb] = 0.f;
   }
 
+  // Pages of 1 or 2 slots: the step's V, loaded as page rows, through LDS
+  // into the operand order the other page sizes load directly (for each d,
+  // the 4 keys 4*q4 .. 4*q4+3 of the lane group).  The area is this
+  // wavefront's own; the waits keep the reads after the writes and the
+  // compiler from moving LDS accesses across them.
+  auto v_to_operands = [&](Step& r) {
+    char* vt = s_vt + wave * 2 * kVtTau;
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+#pragma unroll
+      for (int c = 0; c < LV; ++c) {
+        const int L = c * 1024 + lane * 16;
+        *reinterpret_cast<u32x4*>(vt + tau * kVtTau + (L / kPageBytes) * kPagePad + L % kPageBytes) =
+            r.v[tau][c];
+      }
+    }
+    wait_lgkmcnt0();
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const char* base = vt + tau * kVtTau;
+      // byte of (slot s of the sub-tile, dim d): page s / BS, element d * BS + s % BS
+      auto at = [&](int s, int d) { return base + (s / BS) * kPagePad + (d * BS + s % BS) * EB; };
+      const int s0 = 4 * q4;
+      if constexpr (U8) {
+#pragma unroll
+        for (int c = 0; c < LV; ++c) {
+#pragma unroll
+          for (int jd = 0; jd < 4; ++jd) {
+            const int d = c * 64 + jd * 16 + n16;
+            uint32_t w;
+            if constexpr (BS == 2)
+              w = *reinterpret_cast<const uint16_t*>(at(s0, d)) |
+                  ((uint32_t)*reinterpret_cast<const uint16_t*>(at(s0 + 2, d)) << 16);
+            else
+              w = (uint32_t)*reinterpret_cast<const uint8_t*>(at(s0, d)) |
+                  ((uint32_t)*reinterpret_cast<const uint8_t*>(at(s0 + 1, d)) << 8) |
+                  ((uint32_t)*reinterpret_cast<const uint8_t*>(at(s0 + 2, d)) << 16) |
+                  ((uint32_t)*reinterpret_cast<const uint8_t*>(at(s0 + 3, d)) << 24);
+            r.v[tau][c][jd] = w;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int dp = 0; dp < LV; ++dp) {
+          uint32_t w[4];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int d = dp * 32 + hh * 16 + n16;
+            if constexpr (BS == 2) {
+              w[2 * hh] = *reinterpret_cast<const uint32_t*>(at(s0, d));
+              w[2 * hh + 1] = *reinterpret_cast<const uint32_t*>(at(s0 + 2, d));
+            } else {
+              w[2 * hh] = (uint32_t)*reinterpret_cast<const uint16_t*>(at(s0, d)) |
+                          ((uint32_t)*reinterpret_cast<const uint16_t*>(at(s0 + 1, d)) << 16);
+              w[2 * hh + 1] = (uint32_t)*reinterpret_cast<const uint16_t*>(at(s0 + 2, d)) |
+                              ((uint32_t)*reinterpret_cast<const uint16_t*>(at(s0 + 3, d)) << 16);
+            }
+          }
+          r.v[tau][dp] = u32x4{w[0], w[1], w[2], w[3]};
+        }
+      }
+    }
+  };
+
   auto compute_step = [&](int st, Step& r) {
+    if constexpr (WIDE_V) v_to_operands(r);
     const int key0 = si.base + st * kKeysPerStep;
     // S^T for both sub-tiles: lane (row, q4) gets keys key0 + 16*tau + 4*q4 + 0..3
     float sv[RB][8];
