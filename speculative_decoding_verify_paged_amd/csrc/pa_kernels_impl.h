@@ -306,15 +306,17 @@ void pa_segment(SegmentArgs a) {
   __shared__ float s_l[NW][ROWS];
   __shared__ __attribute__((aligned(16))) float s_o[NW][ROWS][OSTRIDE];
   __shared__ int s_bad;
-  // Pages of 1 or 2 slots: V is loaded as whole page rows (1 KB per
-  // instruction) and turned into the PV operand layout through this
-  // per-wavefront LDS area: each sub-tile's 16/BS pages, page-major, each
-  // padded by 16 B against bank conflicts.
+  // Pages of fewer than 16 slots: K (and for 1 or 2 slots, V) is loaded as
+  // whole page rows (1 KB per instruction) and turned into the MFMA operand
+  // layout through this per-wavefront LDS area, K first, then V: each
+  // sub-tile's 16/BS pages, page-major, each padded by 16 B against bank
+  // conflicts.
+  constexpr bool WIDE_K = BS < 16;
   constexpr bool WIDE_V = BS <= 2;
-  constexpr int kPageBytes = BS * D * EB;                 // one page of one KV head
+  constexpr int kPageBytes = BS * D * EB;                 // one page of one KV head (K or V)
   constexpr int kPagePad = kPageBytes + 16;
   constexpr int kVtTau = (16 / BS) * kPagePad;           // one sub-tile
-  __shared__ __attribute__((aligned(16))) char s_vt[WIDE_V ? NW * 2 * kVtTau : 16];
+  __shared__ __attribute__((aligned(16))) char s_vt[WIDE_K ? NW * 2 * kVtTau : 16];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -543,13 +545,15 @@ void pa_segment(SegmentArgs a) {
     for (int tau = 0; tau < 2; ++tau) {
       const int t0 = key0 + tau * 16;
       {
-        int pg, row;
-        page_row(t0 + n16, 1, pg, row);
-        const char* kp = kb + ((((size_t)pg * Hkv + h) * BS + row) * D) * EB;
+        // K as whole page rows: load c covers bytes [1024 c, 1024 c + 1024)
+        // of the sub-tile's pages laid end to end
+        static_assert(16 * D * EB == LK * 1024, "one 1 KB load per register of the step");
 #pragma unroll
         for (int c = 0; c < LK; ++c) {
-          const int d0 = U8 ? c * 64 + q4 * 16 : c * 32 + q4 * 8;
-          r.k[tau][c] = ld16_stream(kp + d0 * EB);
+          const int L = c * 1024 + lane * 16;
+          int wpg, wrow;                                      // wrow is 0: pages start at 16-slot bounds
+          page_row(t0 + (L / kPageBytes) * BS, BS, wpg, wrow);
+          r.k[tau][c] = ld16_stream(kb + ((size_t)wpg * Hkv + h) * kPageBytes + L % kPageBytes);
         }
       }
       constexpr int NP = BS >= 4 ? 1 : 4 / BS;                // pages holding the 4 slots
@@ -671,13 +675,37 @@ void pa_segment(SegmentArgs a) {
     c_run[rb] = 0.f;
   }
 
-  // Pages of 1 or 2 slots: the step's V, loaded as page rows, through LDS
-  // into the operand order the other page sizes load directly (for each d,
-  // the 4 keys 4*q4 .. 4*q4+3 of the lane group).  The area is this
-  // wavefront's own; the waits keep the reads after the writes and the
-  // compiler from moving LDS accesses across them.
-  auto v_to_operands = [&](Step& r) {
+  // Pages of fewer than 16 slots: the step's K (and for 1 or 2 slots its V),
+  // loaded as page rows, through LDS into the operand order of a tiled
+  // sub-tile (K: 8 or 16 d of the lane's slot; V: for each d, the 4 keys
+  // 4*q4 .. 4*q4+3 of the lane group).  The area is this wavefront's own;
+  // the waits keep the reads after the writes and the compiler from moving
+  // LDS accesses across them.
+  auto to_operands = [&](Step& r) {
     char* vt = s_vt + wave * 2 * kVtTau;
+    // K: lane (slot n16, group q4) takes the 16 B of its slot's row that a
+    // tiled sub-tile load would give it
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+#pragma unroll
+      for (int c = 0; c < LK; ++c) {
+        const int L = c * 1024 + lane * 16;
+        *reinterpret_cast<u32x4*>(vt + tau * kVtTau + (L / kPageBytes) * kPagePad + L % kPageBytes) =
+            r.k[tau][c];
+      }
+    }
+    wait_lgkmcnt0();
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+#pragma unroll
+      for (int c = 0; c < LK; ++c) {
+        const int d0 = U8 ? c * 64 + q4 * 16 : c * 32 + q4 * 8;
+        r.k[tau][c] = *reinterpret_cast<const u32x4*>(vt + tau * kVtTau + (n16 / BS) * kPagePad +
+                                                       ((n16 % BS) * D + d0) * EB);
+      }
+    }
+    if constexpr (!WIDE_V) return;
+    wait_lgkmcnt0();                                          // K read back before V overwrites it
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
 #pragma unroll
@@ -736,7 +764,7 @@ void pa_segment(SegmentArgs a) {
   };
 
   auto compute_step = [&](int st, Step& r) {
-    if constexpr (WIDE_V) v_to_operands(r);
+    if constexpr (WIDE_K) to_operands(r);
     const int key0 = si.base + st * kKeysPerStep;
     // S^T for both sub-tiles: lane (row, q4) gets keys key0 + 16*tau + 4*q4 + 0..3
     float sv[RB][8];
