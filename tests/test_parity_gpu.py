@@ -150,6 +150,19 @@ def test_work_list_shapes():
         _full(case, rounding_aware=True)
 
 
+def test_very_large_batches():
+    """Thousands of short sequences: the work list's scans over the batch
+    (many 64-lane passes) and grids of thousands of workgroups."""
+    rng = np.random.default_rng(197)
+    for k, (n, Hkv, G) in enumerate([(3000, 16, 1), (20000, 2, 2)]):
+        Ls = [int(x) for x in rng.integers(0, 40, n)]
+        Ts = [int(x) for x in rng.integers(1, 3, n)]
+        case = pi.build_case([196, k], Ls, Ts, num_q_heads=G * Hkv, num_kv_heads=Hkv,
+                             head_dim=64, block_size=16, q_dtype=pi.F16, kv_dtype=pi.F16,
+                             spare_blocks=2, poison=True, name=f"batch{n}_H{Hkv}_G{G}")
+        _full(case, rounding_aware=True)
+
+
 @pytest.mark.parametrize("S", [1, 2, 7, 0, 10 ** 6])
 def test_segment_count_invariance(S):
     case = pi.config2(8192, 3)
