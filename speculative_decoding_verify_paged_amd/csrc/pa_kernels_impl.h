@@ -206,35 +206,55 @@ __device__ __forceinline__ int wl_steps(const SegmentArgs& a, int seq, int rows,
   return q.n_steps;
 }
 
+// A sequence for the work list: its step count, -1 if it breaks the
+// contract (one chunk), -2 past the end of the batch (no chunk).
+__device__ __forceinline__ int wl_code(const SegmentArgs& a, int seq, int rows) {
+  if (seq >= a.num_seqs) return -2;
+  bool ok;
+  const int st = wl_steps(a, seq, rows, ok);
+  return ok ? st : -1;
+}
+__device__ __forceinline__ int wl_items(int code, int C) {
+  return code >= 0 ? (code + C - 1) / C : code == -1 ? 1 : 0;
+}
+
+// The codes of the batch's first kWlCached * 64 sequences, lane-strided,
+// kept in registers: the chunk-size search scans them once per candidate.
+constexpr int kWlCached = 4;
+struct WorkList {
+  int code[kWlCached];
+};
+__device__ __forceinline__ WorkList wl_load(const SegmentArgs& a, int rows) {
+  const int lane = threadIdx.x & (kWave - 1);
+  WorkList w;
+#pragma unroll
+  for (int p = 0; p < kWlCached; ++p) w.code[p] = wl_code(a, p * kWave + lane, rows);
+  return w;
+}
+
 // chunks of all sequences for chunk size C
-__device__ __forceinline__ int wl_count(const SegmentArgs& a, int rows, int C) {
+__device__ __forceinline__ int wl_count(const SegmentArgs& a, int rows, int C, const WorkList& w) {
   const int lane = threadIdx.x & (kWave - 1);
   int n = 0;
-  for (int b = 0; b < a.num_seqs; b += kWave) {
-    const int k = b + lane;
-    if (k < a.num_seqs) {
-      bool ok;
-      const int st = wl_steps(a, k, rows, ok);
-      n += ok ? (st + C - 1) / C : 1;
-    }
-  }
+#pragma unroll
+  for (int p = 0; p < kWlCached; ++p) n += wl_items(w.code[p], C);
+  for (int b = kWlCached * kWave; b < a.num_seqs; b += kWave) n += wl_items(wl_code(a, b + lane, rows), C);
   for (int m = 1; m < kWave; m <<= 1) n += __shfl_xor(n, m, kWave);
   return n;
 }
 
-__device__ __forceinline__ int wl_chunk(const SegmentArgs& a, int rows) {
+__device__ __forceinline__ int wl_chunk(const SegmentArgs& a, int rows, const WorkList& w) {
   const int lane = threadIdx.x & (kWave - 1);
   long long total = 0;
   int longest = 1;
-  for (int b = 0; b < a.num_seqs; b += kWave) {
-    const int k = b + lane;
-    if (k < a.num_seqs) {
-      bool ok;
-      const int st = wl_steps(a, k, rows, ok);
-      total += st;
-      longest = max(longest, st);
-    }
-  }
+  auto add = [&](int code) {
+    const int st = max(code, 0);
+    total += st;
+    longest = max(longest, st);
+  };
+#pragma unroll
+  for (int p = 0; p < kWlCached; ++p) add(w.code[p]);
+  for (int b = kWlCached * kWave; b < a.num_seqs; b += kWave) add(wl_code(a, b + lane, rows));
   for (int m = 1; m < kWave; m <<= 1) {
     total += __shfl_xor(total, m, kWave);
     longest = max(longest, __shfl_xor(longest, m, kWave));
@@ -243,41 +263,45 @@ __device__ __forceinline__ int wl_chunk(const SegmentArgs& a, int rows) {
   int hi = max(1, min(longest, a.max_sps));               // a chunk's block ids fit LDS
   int lo = (int)min<long long>(max<long long>(a.steps_per_seg, want), hi);
   lo = max(lo, 1);
-  if (wl_count(a, rows, hi) > a.target_items) return hi;   // the fewest chunks possible
+  if (wl_count(a, rows, hi, w) > a.target_items) return hi;   // the fewest chunks possible
   while (lo < hi) {                                         // smallest C that fits
     const int mid = lo + (hi - lo) / 2;
-    if (wl_count(a, rows, mid) <= a.target_items) hi = mid; else lo = mid + 1;
+    if (wl_count(a, rows, mid, w) <= a.target_items) hi = mid; else lo = mid + 1;
   }
   return lo;
 }
 
 // the sequence holding chunk number `item` (in sequence order), and the
 // chunk's index inside it; -1 when item is past the last chunk
-__device__ __forceinline__ int wl_find(const SegmentArgs& a, int rows, int C, int item, int& chunk) {
+__device__ __forceinline__ int wl_find(const SegmentArgs& a, int rows, int C, int item, int& chunk,
+                                       const WorkList& w) {
   const int lane = threadIdx.x & (kWave - 1);
   int base = 0;
-  for (int b = 0; b < a.num_seqs; b += kWave) {
-    const int k = b + lane;
-    int items = 0;
-    if (k < a.num_seqs) {
-      bool ok;
-      const int st = wl_steps(a, k, rows, ok);
-      items = ok ? (st + C - 1) / C : 1;
-    }
+  // one pass over sequences b .. b + 63: true when the chunk lies in it
+  auto pass = [&](int b, int code, int& seq) {
+    const int items = wl_items(code, C);
     int inc = items;
     for (int m = 1; m < kWave; m <<= 1) {
       const int v = __shfl_up(inc, m, kWave);
       if (lane >= m) inc += v;
     }
     const int excl = inc - items;
-    const unsigned long long hit = __ballot(k < a.num_seqs && item >= base + excl && item < base + inc);
+    const unsigned long long hit = __ballot(item >= base + excl && item < base + inc);
     if (hit) {
       const int l = __builtin_ctzll(hit);
       chunk = item - base - __shfl(excl, l, kWave);
-      return b + l;
+      seq = b + l;
+      return true;
     }
     base += __shfl(inc, kWave - 1, kWave);
-  }
+    return false;
+  };
+  int seq = -1;
+#pragma unroll
+  for (int p = 0; p < kWlCached; ++p)
+    if (pass(p * kWave, w.code[p], seq)) return seq;
+  for (int b = kWlCached * kWave; b < a.num_seqs; b += kWave)
+    if (pass(b, wl_code(a, b + lane, rows), seq)) return seq;
   chunk = 0;
   return -1;
 }
@@ -337,8 +361,9 @@ void pa_segment(SegmentArgs a) {
     st_begin = (int)(((int64_t)j * a.n_steps) / a.S);
     st_cap = (int)(((int64_t)(j + 1) * a.n_steps) / a.S);
   } else {
-    const int C = wl_chunk(a, ROWS);
-    s = wl_find(a, ROWS, C, (int)blockIdx.z, j);
+    const WorkList wl = wl_load(a, ROWS);
+    const int C = wl_chunk(a, ROWS, wl);
+    s = wl_find(a, ROWS, C, (int)blockIdx.z, j, wl);
     if (s < 0) return;                                        // past the last chunk (uniform)
     bool ok;
     const int st = wl_steps(a, s, ROWS, ok);
