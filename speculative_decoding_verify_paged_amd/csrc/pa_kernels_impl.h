@@ -192,13 +192,14 @@ __device__ __forceinline__ SeqInfo seq_info(const SegmentArgs& a, int s, int row
 }
 
 // ---------------------------------------------------------------------------
-// Work list of a ragged batch.  Every sequence's steps are cut into chunks
-// of C steps; C is the smallest size (not below the host's steps per
-// segment, nor above what the LDS block-id table holds) whose chunks of all
-// sequences fit the target count of workgroups per KV head, so one round of
-// equal workgroups covers the batch however its lengths are spread.  A sequence that breaks the contract gets one chunk
-// (it writes NaN partials).  Computed redundantly and identically by every
-// wavefront of every workgroup from the sequence metadata.  Wave-wide.
+// Work list of a batch of several sequences.  Every sequence's steps are cut
+// into chunks of C steps; C is the smallest size (not below the host's steps
+// per segment, nor above what the LDS block-id table holds) whose chunks of
+// all sequences fit the target count of workgroups per KV head, so one round
+// of equal workgroups covers the batch however its lengths are spread.  A
+// sequence that breaks the contract gets one chunk (it writes NaN partials).
+// Computed redundantly and identically by every wavefront of every workgroup
+// from the sequence metadata.  Wave-wide.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int wl_steps(const SegmentArgs& a, int seq, int rows, bool& ok) {
   const SeqInfo q = seq_info(a, seq, rows);
@@ -346,11 +347,10 @@ void pa_segment(SegmentArgs a) {
   const int wave = threadIdx.x / kWave;
   const int n16 = lane & 15;          // stacked query row owned by this lane (in each row block)
   const int q4 = lane >> 4;           // lane group
-  // Grid (Hkv, num_seqs, S), segments last and in reverse: the launch
-  // starts with the highest segments, which only the longest sequences of a
-  // ragged batch have, so their work is not left for the final round.
-  // A ragged batch (work-list mode) instead has grid (Hkv, 1, chunks) and
-  // takes its sequence and steps from the work list.
+  // Fixed segments (one sequence): grid (Hkv, num_seqs, S) with segment
+  // j = S - 1 - blockIdx.z.  Work-list mode (a batch of several sequences):
+  // grid (Hkv, 1, chunks), the sequence and steps of chunk blockIdx.z taken
+  // from the work list.
   const int h = blockIdx.x;
   int s, j, st_begin, st_cap, wl_items = 0;
   if (!a.worklist) {
