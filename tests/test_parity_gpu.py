@@ -264,15 +264,17 @@ def test_graph_capture_replays_match_eager():
     import torch
     from gpu_util import to_device
     import speculative_decoding_verify_paged_amd as pav
-    cases = [pi.config2(8192, 3, rep=7), pi.config4(4096, window=1024, rep=7)]
+    # fixed segments, a sliding window, a work-list batch, 1-slot pages
+    # (LDS reordering), a tree and the u8 entry point
+    cases = [pi.config2(8192, 3, rep=7), pi.config4(4096, window=1024, rep=7),
+             pi.config5(rep=7, lo=1, hi=3000), pi.config2(2048, 3, rep=7, block_size=1),
+             pi.config2(2048, 4, rep=7, tree=True), pi.config3(2048, 3, rep=7)]
     devs = [to_device(c) for c in cases]
     outs = [torch.empty_like(d["q"]) for d in devs]
 
     def call_all(stream):
         for c, d, o in zip(cases, devs, outs):
-            pav.pa_verify_forward(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
-                                  d["past_lens"], d["subsequence_begins"], c.max_context_len,
-                                  c.scale, o, sliding_window=c.sliding_window, stream=stream)
+            run_gpu(c, dev=d, out=o, sync=False, stream=stream)
 
     call_all(torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
