@@ -72,6 +72,11 @@ hipError_t launch_segment_u8(const SegmentArgs& a, int q_dtype, int D, int bs, i
 hipError_t launch_combine(const CombineArgs& a, int out_dtype, int D, int threads, dim3 grid,
                           hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, int q_dtype, int kv_dtype, int D, hipStream_t st);
+// Most steps a segment or work-list chunk may span: its block ids (one more
+// for a step that starts inside a page, one more for the last page) must fit
+// the kMaxSegBlocks-entry LDS table.
+constexpr int max_steps_per_segment(int bs) { return (kMaxSegBlocks - 2) * bs / kKeysPerStep; }
+
 // Combine workgroup size: enough threads that each loads at most 8 of the S
 // partials of its (token, q head) row (one batch of loads), 256..1024.
 constexpr int combine_threads(int S, int D) {

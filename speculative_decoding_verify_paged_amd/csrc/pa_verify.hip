@@ -92,7 +92,7 @@ int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_ve
   }
   const int64_t n_steps = cdiv(span, kKeysPerStep);
   // a segment's block ids must fit the kernel's LDS staging buffer
-  const int64_t max_sps = ((int64_t)(pav::kMaxSegBlocks - 2) * bs) / kKeysPerStep;
+  const int64_t max_sps = pav::max_steps_per_segment(bs);
   int64_t S;
   if (p->num_segments > 0) {
     S = p->num_segments;
@@ -234,7 +234,7 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
   a.n_steps = pl.num_steps;
   a.worklist = pl.worklist;
   a.target_items = pl.target_items;
-  a.max_sps = (int32_t)(((int64_t)(pav::kMaxSegBlocks - 2) * p->block_size) / pav::kKeysPerStep);
+  a.max_sps = pav::max_steps_per_segment(p->block_size);
   a.scale_log2 = scale * 1.4426950408889634f;
 
   hipStream_t st = static_cast<hipStream_t>(p->stream);
