@@ -93,9 +93,11 @@ constexpr int combine_threads(int S, int D) {
 // workgroup per CU, two wavefronts per SIMD with one step each (C2 shape
 // 27.6 vs 28.2 µs per call for 4 wavefronts with two steps each; u8 21.4 vs
 // 22.5 µs) — two workgroups of 4 instead would double the partials the
-// combine reads.  More than one row block needs the whole register file of
-// one wavefront per SIMD (and its LDS merge buffer allows one workgroup per
-// CU).
+// combine reads.  Two row blocks at head_dim <= 128 still fit two
+// wavefronts per SIMD (T = 5 and 8 at 32k: 30.0 and 30.7 us per call against
+// 30.35 and 31.3 at one); more row blocks, or head_dim 256, need the whole
+// register file of one wavefront per SIMD (and the LDS merge buffer allows
+// one workgroup per CU).
 struct SegConfig {
   int waves_per_simd;
   int prefetch;
@@ -105,7 +107,7 @@ struct SegConfig {
 constexpr SegConfig seg_config(int kv_dtype, int D, int rb, int bs = 16) {
   // pages of fewer than 16 slots gather per lane (more address registers)
   if (bs < 16) return D >= 256 ? SegConfig{1, 1, 1} : SegConfig{2, 1, 2};
-  if (rb > 1) return SegConfig{1, 1, 1};
+  if (rb > 1) return rb == 2 && D <= 128 ? SegConfig{2, 1, 1, 8} : SegConfig{1, 1, 1};
   if (kv_dtype == kU8)
     return D >= 256 ? SegConfig{2, 1, 1, 8} : D >= 128 ? SegConfig{1, 2, 1} : SegConfig{4, 1, 4};
   return D >= 256 ? SegConfig{1, 1, 1} : D >= 128 ? SegConfig{2, 1, 1, 8} : SegConfig{4, 1, 4};
