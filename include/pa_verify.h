@@ -60,6 +60,16 @@
  *  subsequence_begins [num_seqs + 1] int32, cumulative, [0] == 0,
  *                [num_seqs] == num_tokens
  *
+ * Alignment (the kernels use 16-byte vector accesses).  Forward calls: q,
+ * k_cache, v_cache, k_scale_zp, v_scale_zp and the workspace 16-byte
+ * aligned; out 2 bytes; block_tables, past_lens, subsequence_begins and
+ * tree_mask 4 bytes.  Append calls: the new K/V rows, the caches and the
+ * scale/zero-point arrays 2 bytes (the u8 caches 1), the int32 arrays and the
+ * workspace 4 bytes.  A misaligned pointer is PA_ERR_INVALID_ARG (a
+ * misaligned workspace PA_ERR_WORKSPACE), returned before anything is
+ * enqueued.  hipMalloc and torch's allocator give 256-byte aligned storage;
+ * a view that starts inside a storage may not be.
+ *
  * Ownership and behaviour.  The library never allocates, frees or retains a
  * pointer past the call and never synchronises (except pa_verify_read_status).
  * A forward call enqueues exactly two kernels (segment kernel, then combine
@@ -86,9 +96,9 @@ extern "C" {
 
 typedef enum pa_status {
   PA_OK = 0,
-  PA_ERR_INVALID_ARG = 1,      /* null pointer, non-positive size, inconsistent sizes */
+  PA_ERR_INVALID_ARG = 1,      /* null or misaligned pointer, non-positive size, inconsistent sizes */
   PA_ERR_UNSUPPORTED = 2,      /* valid but not built: D, block_size, group size, dtype combo */
-  PA_ERR_WORKSPACE = 3,        /* workspace missing or smaller than pa_verify_workspace_bytes */
+  PA_ERR_WORKSPACE = 3,        /* workspace missing, misaligned or smaller than pa_verify_workspace_bytes */
   PA_ERR_HIP = 4,              /* a HIP runtime call or kernel launch failed */
   PA_ERR_DEVICE_CONTRACT = 5   /* device-side metadata violated the contract (see above) */
 } pa_status;

@@ -27,6 +27,8 @@ constexpr int64_t kMaxRounds = 8;
 // T_s bound when the caller gives none (max_query_len == 0).
 constexpr int64_t kDefaultQueryLen = 4;
 
+bool aligned(const void* x, uintptr_t a) { return (reinterpret_cast<uintptr_t>(x) & (a - 1)) == 0; }
+
 bool is_pow2_in(int v, int lo, int hi) {
   if (v < lo || v > hi) return false;
   return (v & (v - 1)) == 0;
@@ -193,6 +195,12 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
   if (rc) return rc;
   if (!q || !k || !v || !bt || !past_lens || !sb || !out) return PA_ERR_INVALID_ARG;
   if (u8_entry && (!ksz || !vsz)) return PA_ERR_INVALID_ARG;
+  // the widths the kernels access these with
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 2) ||
+      !aligned(bt, 4) || !aligned(past_lens, 4) || !aligned(sb, 4) || !aligned(p->tree_mask, 4))
+    return PA_ERR_INVALID_ARG;
+  if (u8_entry && (!aligned(ksz, 16) || !aligned(vsz, 16))) return PA_ERR_INVALID_ARG;
+  if (!aligned(p->workspace, 16)) return PA_ERR_WORKSPACE;
   if (!(scale == scale)) return PA_ERR_INVALID_ARG;
   int cus = 0;
   rc = device_cus(&cus);
@@ -270,7 +278,13 @@ int run_append(const void* k_new, const void* v_new, void* k, void* v, void* ksz
   if (rc) return rc;
   if (!k_new || !v_new || !k || !v || !bt || !past_lens || !sb) return PA_ERR_INVALID_ARG;
   if (u8_entry && (!ksz || !vsz)) return PA_ERR_INVALID_ARG;
-  if (!p->workspace || p->workspace_bytes < sizeof(int32_t)) return PA_ERR_WORKSPACE;
+  const uintptr_t ce = u8_entry ? 1 : 2;                      // bytes per cache element
+  if (!aligned(k_new, 2) || !aligned(v_new, 2) || !aligned(k, ce) || !aligned(v, ce) ||
+      !aligned(ksz, 2) || !aligned(vsz, 2) || !aligned(bt, 4) || !aligned(past_lens, 4) ||
+      !aligned(sb, 4))
+    return PA_ERR_INVALID_ARG;
+  if (!p->workspace || !aligned(p->workspace, 4) || p->workspace_bytes < sizeof(int32_t))
+    return PA_ERR_WORKSPACE;
   if (p->num_tokens > 2147483647 / 2) return PA_ERR_UNSUPPORTED;
   pav::AppendArgs a;
   a.k_new = k_new;
@@ -365,9 +379,9 @@ int pa_verify_read_status(const pa_verify_params* p, int32_t* device_status) {
 const char* pa_verify_status_string(int status) {
   switch (status) {
     case PA_OK: return "PA_OK";
-    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG: null pointer or inconsistent sizes";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG: null or misaligned pointer, or inconsistent sizes";
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: head_dim, block_size, group size or dtype combination not built";
-    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or smaller than pa_verify_workspace_bytes";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing, misaligned or smaller than pa_verify_workspace_bytes";
     case PA_ERR_HIP: return "PA_ERR_HIP: HIP runtime call or kernel launch failed";
     case PA_ERR_DEVICE_CONTRACT: return "PA_ERR_DEVICE_CONTRACT: device metadata violated the contract";
   }

@@ -140,6 +140,36 @@ def test_append_host_errors():
     assert L.pa_kv_append(*args, None) == pav.PA_ERR_INVALID_ARG
 
 
+def test_misaligned_pointers_are_rejected_before_any_launch():
+    # every case below fails the alignment check, so nothing reaches a device
+    L = pav.lib()
+    for k, off in [(0, 8), (1, 8), (2, 4), (3, 2), (4, 2), (5, 1)]:   # q, k, v: 16 B; ints: 4 B
+        args = [FAKE] * 6
+        args[k] = FAKE + off
+        assert L.pa_verify_forward(*args, 32771, 0.1, FAKE, ctypes.byref(params())) \
+            == pav.PA_ERR_INVALID_ARG, k
+    assert L.pa_verify_forward(*[FAKE] * 6, 32771, 0.1, FAKE + 1, ctypes.byref(params())) \
+        == pav.PA_ERR_INVALID_ARG                                          # out: 2 B
+    assert call(params(tree_mask=FAKE + 2)) == pav.PA_ERR_INVALID_ARG
+    assert call(params(workspace=FAKE + 8, workspace_bytes=1 << 30)) == pav.PA_ERR_WORKSPACE
+    u8 = ctypes.byref(params(kv_dtype=pav.PA_U8, head_dim=256, num_q_heads=16, num_kv_heads=4))
+    for k in range(2):                                                 # scale / zero point: 16 B
+        sz = [FAKE, FAKE]
+        sz[k] = FAKE + 4
+        assert L.pa_verify_forward_u8(FAKE, FAKE, FAKE, *sz, FAKE, FAKE, FAKE, 32771, 0.1, FAKE,
+                                      u8) == pav.PA_ERR_INVALID_ARG
+    ok = ctypes.byref(params(num_q_heads=8, workspace=FAKE, workspace_bytes=256))
+    for k in range(7):                  # new rows and 16-bit caches: 2 B; ints: 4 B
+        a = [FAKE] * 7
+        a[k] = FAKE + (1 if k < 4 else 2)
+        assert L.pa_kv_append(*a, ok) == pav.PA_ERR_INVALID_ARG, k
+    bad_ws = ctypes.byref(params(num_q_heads=8, workspace=FAKE + 2, workspace_bytes=256))
+    assert L.pa_kv_append(*[FAKE] * 7, bad_ws) == pav.PA_ERR_WORKSPACE
+    u8a = ctypes.byref(params(kv_dtype=pav.PA_U8, workspace=FAKE, workspace_bytes=256))
+    assert L.pa_kv_append_u8(FAKE, FAKE, FAKE, FAKE, FAKE + 1, FAKE, FAKE, FAKE, FAKE,
+                             u8a) == pav.PA_ERR_INVALID_ARG                # scale / zero point: 2 B
+
+
 def test_missing_workspace_is_reported_before_any_launch():
     # valid arguments, no workspace: PA_ERR_WORKSPACE with a GPU, PA_ERR_HIP
     # (no device to size the plan for) here; nothing is enqueued either way
