@@ -157,14 +157,30 @@ def _dtype_code(t) -> int:
 
 
 def workspace(nbytes: int, device):
-    """A zero-initialised device workspace of at least nbytes, cached per device."""
+    """A zero-initialised device workspace of at least nbytes, cached per device.
+
+    Every call on the device that is given no ``workspace=`` uses this one
+    buffer, so such calls must be ordered (one stream, or streams that wait
+    on each other); calls that may run concurrently need their own
+    workspaces.  Allocating or growing it synchronises the device (no call
+    still uses the old buffer, and the zeroed status word is in place before
+    any stream runs on the new one), so it cannot happen during graph capture:
+    make one eager call with the largest shape first."""
     torch = _torch()
     key = (str(device),)
-    buf = _ws_cache.get(key)
-    if buf is None or buf.numel() < nbytes:
+    old = _ws_cache.get(key)
+    if old is None or old.numel() < nbytes:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("the cached workspace must be sized before graph capture: make one "
+                               "eager call with the largest shape first, or pass workspace=")
+        torch.cuda.synchronize(device)
         buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        if old is not None:
+            buf[:4].copy_(old[:4])                  # a pending sticky status survives the growth
+        torch.cuda.synchronize(device)
         _ws_cache[key] = buf
-    return buf
+        return buf
+    return old
 
 
 def _check(t, name, dtype=None, ndim=None, device=None):
@@ -299,7 +315,10 @@ def pa_verify_forward(q, k_cache, v_cache, block_tables, past_lens, subsequence_
     optional pair of raw hipEvent_t recorded around the segment kernel.
     ``max_query_len`` bounds the new tokens per sequence (0: derived from
     num_tokens and num_seqs); ``tree_mask`` is an optional int32/uint32
-    device tensor [num_tokens] of draft-tree visibility words."""
+    device tensor [num_tokens] of draft-tree visibility words.
+    ``workspace``: a device uint8 tensor of at least pa_verify_workspace_bytes,
+    its first 4 bytes zeroed once; default the per-device cached one (see
+    ``workspace()``: calls that share it must be ordered)."""
     return _call(False, q, k_cache, v_cache, None, None, block_tables, past_lens,
                  subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
                  workspace, stream, prof_events, max_query_len=max_query_len, tree_mask=tree_mask)

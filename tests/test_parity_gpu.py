@@ -258,6 +258,27 @@ def test_device_contract_violations_give_nan_and_status():
     assert np.max(np.abs(got[:2] - ref[:2])) <= 2e-3
 
 
+def test_cached_workspace_growth_keeps_a_pending_status():
+    """Growing the binding's cached workspace keeps an unread contract
+    violation, and calls after the growth run on the new buffer."""
+    import torch
+    import speculative_decoding_verify_paged_amd as pav
+    base = pi.build_case([31], [300, 200], [2, 3], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                         block_size=16, name="growth")
+    ref = oracle.forward(base)
+    assert pav.pa_verify_read_status() in (pav.PA_OK, pav.PA_ERR_DEVICE_CONTRACT)
+    got = to_f64(run_gpu(base, max_query_len=2))            # T = 3 > 2: a violation
+    assert np.all(np.isnan(got[2:]))
+    dev = torch.device("cuda", torch.cuda.current_device())
+    old = pav.workspace(0, dev)
+    new = pav.workspace(old.numel() + (1 << 20), dev)
+    assert new.numel() > old.numel() and new.data_ptr() != old.data_ptr()
+    assert pav.pa_verify_read_status() == pav.PA_ERR_DEVICE_CONTRACT
+    got = to_f64(run_gpu(base))
+    assert pav.pa_verify_read_status() == pav.PA_OK
+    assert np.max(np.abs(got - ref)) <= 2e-3
+
+
 def test_graph_capture_replays_match_eager():
     """A call captured in a HIP graph replays to the eager result, replay after
     replay, with other eager work and synchronisations in between."""
