@@ -97,6 +97,31 @@ def test_max_context():
     _sampled(case, n=48)
 
 
+def test_contexts_where_the_block_id_table_sets_the_segment_count():
+    """Contexts long enough that a segment's block ids, not the CU count, set
+    the number of segments: 140k keys on 2-slot and 131k on 1-slot pages (one
+    block id per key), 8 KV heads each.  (16-slot pages reach the limit only
+    past 530k keys at 8 KV heads; the planner test covers that on the CPU.)"""
+    import speculative_decoding_verify_paged_amd as pav
+    cases = [pi.build_case([9, 140000, 3], [140000], [3], num_q_heads=16, num_kv_heads=8,
+                           head_dim=64, block_size=2, q_dtype=pi.BF16, kv_dtype=pi.BF16,
+                           name="ctx140k_bs2_T3"),
+             pi.build_case([9, 131069, 3], [131069], [3], num_q_heads=32, num_kv_heads=8,
+                           head_dim=64, block_size=1, name="ctx131072_bs1_T3")]
+    for case in cases:
+        p = pav.make_params(num_seqs=1, num_tokens=case.num_tokens,
+                            num_q_heads=case.num_q_heads, num_kv_heads=case.num_kv_heads,
+                            head_dim=case.head_dim, block_size=case.block_size,
+                            num_blocks=case.num_blocks, max_blocks_per_seq=case.max_blocks_per_seq,
+                            q_dtype=case.q_dtype, kv_dtype=case.kv_dtype)
+        plan = pav.pa_verify_make_plan(p, case.max_context_len, 256)
+        table_steps = (1040 - 2) * case.block_size // 32          # steps whose ids fit the table
+        need = -(-plan["num_steps"] // table_steps)
+        print(case.name, plan["num_segments"], need, flush=True)
+        assert plan["num_segments"] == need and plan["steps_per_segment"] <= table_steps, plan
+        _sampled(case, n=24)
+
+
 def _small_cases():
     rng = np.random.default_rng(77)
     out = []
@@ -339,6 +364,29 @@ def test_prepared_call_matches_the_plain_call():
             pc(stream=st)
             torch.cuda.synchronize()
             assert np.array_equal(to_f64(out), want), case.name
+
+
+def test_misaligned_views_are_refused_and_out_is_untouched():
+    """Tensor views that start inside their storage at an offset the kernels
+    cannot read with 16-byte vectors are refused before anything runs."""
+    import torch
+    import speculative_decoding_verify_paged_amd as pav
+    from gpu_util import to_device
+    case = pi.config2(2048, 3)
+    dev = to_device(case)
+    q = dev["q"]
+    shifted = torch.empty(q.numel() + 1, dtype=q.dtype, device=q.device)[1:].view(q.shape)
+    shifted.copy_(q)                                         # 2 bytes past a 16-byte boundary
+    out = torch.full_like(q, 7.0)
+    with pytest.raises(pav.PaVerifyError) as e:
+        pav.pa_verify_forward(shifted, dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                              dev["past_lens"], dev["subsequence_begins"], case.max_context_len,
+                              case.scale, out)
+    assert e.value.code == pav.PA_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert bool(torch.all(out == 7.0))
+    got = to_f64(run_gpu(case, dev))                        # the aligned call still runs
+    assert max_err(got, oracle.forward(case)) <= tol(case)
 
 
 # ---------------------------------------------------------------------------
