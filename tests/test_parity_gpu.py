@@ -99,11 +99,13 @@ def test_max_context():
 
 def test_contexts_where_the_block_id_table_sets_the_segment_count():
     """Contexts long enough that a segment's block ids, not the CU count, set
-    the number of segments: 140k keys on 2-slot and 131k on 1-slot pages (one
-    block id per key), 8 KV heads each.  (16-slot pages reach the limit only
-    past 530k keys at 8 KV heads; the planner test covers that on the CPU.)"""
+    the number of segments, so segments fill the LDS block-id table almost to
+    its end: 600k keys on 16-slot pages, 140k on 2-slot and 131k on 1-slot
+    pages (one block id per key), 8 KV heads each."""
     import speculative_decoding_verify_paged_amd as pav
-    cases = [pi.build_case([9, 140000, 3], [140000], [3], num_q_heads=16, num_kv_heads=8,
+    cases = [pi.build_case([9, 600000, 2], [600000], [2], num_q_heads=8, num_kv_heads=8,
+                           head_dim=128, block_size=16, name="ctx600k_bs16_T2"),
+             pi.build_case([9, 140000, 3], [140000], [3], num_q_heads=16, num_kv_heads=8,
                            head_dim=64, block_size=2, q_dtype=pi.BF16, kv_dtype=pi.BF16,
                            name="ctx140k_bs2_T3"),
              pi.build_case([9, 131069, 3], [131069], [3], num_q_heads=32, num_kv_heads=8,
