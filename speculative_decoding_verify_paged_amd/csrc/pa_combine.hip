@@ -5,7 +5,8 @@
 namespace pav {
 
 // ---------------------------------------------------------------------------
-// Combine kernel: one workgroup per (token, q head), NT threads with NT sized
+// Combine kernel: one workgroup per (token, q head) (placed by CombineArgs::xcds
+// on the XCD that wrote the pair's partials), NT threads with NT sized
 // by the host so all S partials are loaded in one batch of K per thread.  Thread t owns d columns
 // [c4, c4 + 4) of the segments sub, sub + NSUB, ...; it merges them with the
 // same online rescaling as the segment kernel (every load independent of the
@@ -21,7 +22,14 @@ __global__ __launch_bounds__(NT) void pa_combine(CombineArgs a) {
   __shared__ float s_den[NSUB];
   __shared__ __attribute__((aligned(16))) f32x4 s_acc[NSUB][LPS];
 
-  const int pair = blockIdx.x;                                // token * Hq + q head
+  int pair = blockIdx.x;                                      // token * Hq + q head
+  if (a.xcds > 0) {
+    // the pairs of KV heads x, x + xcds, ... in (token, KV head, group) order
+    const int X = a.xcds, x = (int)blockIdx.x % X, k = (int)blockIdx.x / X;
+    const int G = a.seg.G, HX = a.seg.Hkv / X;
+    const int g = k % G, t = k / G;
+    pair = (t / HX) * a.Hq + ((t % HX) * X + x) * G + g;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int sub = tid / LPS;

@@ -58,6 +58,11 @@ struct CombineArgs {
   SegmentArgs seg;
   void* out;
   int32_t num_tokens, Hq;
+  // > 0 (the device's XCD count, which divides Hkv): workgroup i takes a
+  // (token, q head) pair whose KV head is congruent to i modulo xcds.
+  // Workgroups go to the XCDs round-robin by linear id, so it runs on the XCD
+  // whose L2 still holds that KV head's partials from the segment kernel.
+  int32_t xcds;
 };
 
 // ev0/ev1: optional events timestamped by the segment kernel's own dispatch

@@ -167,6 +167,20 @@ int device_cus(int* cus) {
   return PA_OK;
 }
 
+// XCDs of the current device (0 when the runtime cannot say), queried once
+// per device.
+int device_xccs() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  const int c = cache[dev].load(std::memory_order_relaxed);
+  if (c != 0) return c < 0 ? 0 : c;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || n <= 0) n = -1;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n < 0 ? 0 : n;
+}
+
 void maybe_log(const pa_verify_params* p, const pa_verify_plan& pl, int32_t max_ctx) {
   static const bool on = [] {
     const char* e = std::getenv("PA_VERIFY_LOG");
@@ -264,6 +278,11 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
   c.out = out;
   c.num_tokens = p->num_tokens;
   c.Hq = p->num_q_heads;
+  // The segment grid's x dimension is the KV head, so every workgroup of KV
+  // head h ran on XCD h mod X when X divides Hkv: put the pair's combine
+  // workgroup there too.
+  const int X = device_xccs();
+  c.xcds = X > 1 && p->num_kv_heads % X == 0 ? X : 0;
   e = pav::launch_combine(c, p->q_dtype, p->head_dim, pl.combine_threads, dim3(pl.combine_grid[0]), st);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
