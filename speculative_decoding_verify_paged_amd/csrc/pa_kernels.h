@@ -58,10 +58,11 @@ struct CombineArgs {
   SegmentArgs seg;
   void* out;
   int32_t num_tokens, Hq;
-  // > 0 (the device's XCD count, which divides Hkv): workgroup i takes a
+  // > 1 (gcd of the device's XCD count and Hkv): workgroup i takes a
   // (token, q head) pair whose KV head is congruent to i modulo xcds.
-  // Workgroups go to the XCDs round-robin by linear id, so it runs on the XCD
-  // whose L2 still holds that KV head's partials from the segment kernel.
+  // Workgroups go to the XCDs round-robin by linear id, so it runs on an XCD
+  // whose L2 may still hold that KV head's partials from the segment kernel
+  // (all of them when the XCD count divides Hkv).
   int32_t xcds;
 };
 

@@ -278,11 +278,17 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
   c.out = out;
   c.num_tokens = p->num_tokens;
   c.Hq = p->num_q_heads;
-  // The segment grid's x dimension is the KV head, so every workgroup of KV
-  // head h ran on XCD h mod X when X divides Hkv: put the pair's combine
-  // workgroup there too.
-  const int X = device_xccs();
-  c.xcds = X > 1 && p->num_kv_heads % X == 0 ? X : 0;
+  // The segment grid's x dimension is the KV head and workgroups reach the X
+  // XCDs round-robin by linear id, so the workgroups of KV head h ran on the
+  // XCDs congruent to h modulo gcd(X, Hkv) (all on XCD h mod X when X
+  // divides Hkv): put the pair's combine workgroup on one of those.
+  int g = device_xccs();
+  for (int b = p->num_kv_heads; b != 0;) {
+    const int t = g % b;
+    g = b;
+    b = t;
+  }
+  c.xcds = g > 1 ? g : 0;
   e = pav::launch_combine(c, p->q_dtype, p->head_dim, pl.combine_threads, dim3(pl.combine_grid[0]), st);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
