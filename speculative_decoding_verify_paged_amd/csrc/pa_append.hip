@@ -144,12 +144,11 @@ template <int QT, int KV>
 static hipError_t launch_append_d(const AppendArgs& a, int D, hipStream_t st) {
   const dim3 grid(a.num_tokens, a.Hkv, 2);
   switch (D) {
-    case 64: hipLaunchKernelGGL((pa_append<QT, KV, 64>), grid, dim3(kWave), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((pa_append<QT, KV, 128>), grid, dim3(kWave), 0, st, a); break;
-    case 256: hipLaunchKernelGGL((pa_append<QT, KV, 256>), grid, dim3(kWave), 0, st, a); break;
-    default: return hipErrorInvalidValue;
+    case 64: return launch_kernel(reinterpret_cast<const void*>(pa_append<QT, KV, 64>), grid, dim3(kWave), st, a);
+    case 128: return launch_kernel(reinterpret_cast<const void*>(pa_append<QT, KV, 128>), grid, dim3(kWave), st, a);
+    case 256: return launch_kernel(reinterpret_cast<const void*>(pa_append<QT, KV, 256>), grid, dim3(kWave), st, a);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_append(const AppendArgs& a, int q_dtype, int kv_dtype, int D, hipStream_t st) {

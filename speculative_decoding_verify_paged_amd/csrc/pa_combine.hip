@@ -136,11 +136,9 @@ __global__ __launch_bounds__(NT) void pa_combine(CombineArgs a) {
 
 template <int D, int NT>
 static hipError_t launch_combine_nt(const CombineArgs& a, int out_dtype, dim3 grid, hipStream_t st) {
-  if (out_dtype == kF16)
-    hipLaunchKernelGGL((pa_combine<D, kF16, NT>), grid, dim3(NT), 0, st, a);
-  else
-    hipLaunchKernelGGL((pa_combine<D, kBF16, NT>), grid, dim3(NT), 0, st, a);
-  return hipGetLastError();
+  const void* fn = out_dtype == kF16 ? reinterpret_cast<const void*>(pa_combine<D, kF16, NT>)
+                                     : reinterpret_cast<const void*>(pa_combine<D, kBF16, NT>);
+  return launch_kernel(fn, grid, dim3(NT), st, a);
 }
 
 template <int D>

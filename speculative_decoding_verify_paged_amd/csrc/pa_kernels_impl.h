@@ -69,6 +69,18 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// Launch a kernel that takes one argument struct; returns this launch's own
+// error (not an earlier call's, as a later hipGetLastError would).  With
+// events, the dispatch itself timestamps the kernel's start and end.
+template <typename Args>
+inline hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, hipStream_t st,
+                                const Args& a, hipEvent_t ev0 = nullptr,
+                                hipEvent_t ev1 = nullptr) {
+  void* args[] = {const_cast<Args*>(&a)};
+  if (ev0 || ev1) return hipExtLaunchKernel(fn, grid, block, args, 0, st, ev0, ev1, 0);
+  return hipLaunchKernel(fn, grid, block, args, 0, st);
+}
+
 __device__ __forceinline__ u32x4 ld16(const char* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
@@ -1075,12 +1087,8 @@ hipError_t launch_seg(const SegmentArgs& a, dim3 grid, hipStream_t st, hipEvent_
   constexpr SegConfig c = seg_config(KV, D, RB, BS);
   static_assert(c.waves_per_group <= 4 * c.waves_per_simd, "a workgroup must fit on one CU");
   constexpr auto kern = pa_segment<QT, KV, D, BS, c.waves_per_group, c.waves_per_simd, c.prefetch, RB>;
-  // with events, the dispatch itself timestamps the kernel's start and end
-  if (ev0 || ev1)
-    hipExtLaunchKernelGGL(kern, grid, dim3(c.waves_per_group * kWave), 0, st, ev0, ev1, 0, a);
-  else
-    hipLaunchKernelGGL(kern, grid, dim3(c.waves_per_group * kWave), 0, st, a);
-  return hipGetLastError();
+  return launch_kernel(reinterpret_cast<const void*>(kern), grid, dim3(c.waves_per_group * kWave),
+                       st, a, ev0, ev1);
 }
 
 template <int QT, int KV, int D, int BS>

@@ -38,16 +38,22 @@ extern "C" {
 // bytes must be a multiple of 16; grid workgroups of 256 threads.
 int pa_membench_read(const void* buf, size_t bytes, void* sink, int grid, void* stream) {
   if (!buf || !sink || bytes % 16 || grid < 1) return 1;
-  hipLaunchKernelGGL(membench_read, dim3(grid), dim3(256), 0, (hipStream_t)stream,
-                     (const u32x4*)buf, bytes / 16, (uint32_t*)sink);
-  return hipGetLastError() == hipSuccess ? 0 : 4;
+  const u32x4* b = (const u32x4*)buf;
+  size_t n = bytes / 16;
+  uint32_t* k = (uint32_t*)sink;
+  void* args[] = {&b, &n, &k};
+  return hipLaunchKernel(reinterpret_cast<const void*>(membench_read), dim3(grid), dim3(256), args,
+                         0, (hipStream_t)stream) == hipSuccess ? 0 : 4;
 }
 
 int pa_membench_copy(void* dst, const void* src, size_t bytes, int grid, void* stream) {
   if (!dst || !src || bytes % 16 || grid < 1) return 1;
-  hipLaunchKernelGGL(membench_copy, dim3(grid), dim3(256), 0, (hipStream_t)stream, (u32x4*)dst,
-                     (const u32x4*)src, bytes / 16);
-  return hipGetLastError() == hipSuccess ? 0 : 4;
+  u32x4* d = (u32x4*)dst;
+  const u32x4* s = (const u32x4*)src;
+  size_t n = bytes / 16;
+  void* args[] = {&d, &s, &n};
+  return hipLaunchKernel(reinterpret_cast<const void*>(membench_copy), dim3(grid), dim3(256), args,
+                         0, (hipStream_t)stream) == hipSuccess ? 0 : 4;
 }
 
 }  // extern "C"
