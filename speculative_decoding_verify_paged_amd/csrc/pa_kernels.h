@@ -111,8 +111,12 @@ struct SegConfig {
   int waves_per_group = kWavesPerGroup;
 };
 constexpr SegConfig seg_config(int kv_dtype, int D, int rb, int bs = 16) {
-  // pages of fewer than 16 slots gather per lane (more address registers)
-  if (bs < 16) return D >= 256 ? SegConfig{1, 1, 1} : SegConfig{2, 1, 2};
+  // Pages of fewer than 16 slots: one 8-wavefront workgroup per CU as for
+  // 16-slot pages (C2 shape at 32k, us per call: 2 slots 29.8 vs 29.9 for two
+  // 4-wavefront groups, 4 slots 27.6 vs 28.1, 8 slots 27.8 vs 28.0), except
+  // 1-slot pages: their 32-step segment cap (one block id per key) then needs
+  // more segments than one round of workgroups holds.
+  if (bs < 16) return D >= 256 ? SegConfig{1, 1, 1} : bs >= 2 ? SegConfig{2, 1, 1, 8} : SegConfig{2, 1, 2};
   if (rb > 1) return rb == 2 && D <= 128 ? SegConfig{2, 1, 1, 8} : SegConfig{1, 1, 1};
   if (kv_dtype == kU8)
     return D >= 256 ? SegConfig{2, 1, 1, 8} : D >= 128 ? SegConfig{1, 2, 1} : SegConfig{4, 1, 4};
