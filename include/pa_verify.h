@@ -166,6 +166,10 @@ typedef struct pa_verify_plan {
   int32_t keys_per_step;       /* keys one wavefront consumes per loop iteration */
   int32_t span;                /* bound on keys any one sequence's rows touch */
   int32_t waves_per_group;     /* wavefronts per segment workgroup */
+  int32_t max_steps_per_segment; /* most steps one segment or work-list chunk may span: its
+                                  block ids (one per page, plus one for a step that starts
+                                  inside a page and one for the last page) fit the kernel's
+                                  LDS table of 1040 ids (2080 for block_size 1) */
   int32_t grid[3];             /* segment kernel grid: (Hkv, num_seqs, S), z = S-1-j; work
                                   list: (Hkv, 1, chunks) */
   int32_t block_threads;       /* segment kernel workgroup size */

@@ -54,7 +54,8 @@ class PaVerifyPlan(ctypes.Structure):
         ("num_steps", ctypes.c_int32), ("row_blocks", ctypes.c_int32),
         ("worklist", ctypes.c_int32), ("target_items", ctypes.c_int32),
         ("keys_per_step", ctypes.c_int32), ("span", ctypes.c_int32),
-        ("waves_per_group", ctypes.c_int32), ("grid", ctypes.c_int32 * 3),
+        ("waves_per_group", ctypes.c_int32), ("max_steps_per_segment", ctypes.c_int32),
+        ("grid", ctypes.c_int32 * 3),
         ("block_threads", ctypes.c_int32), ("combine_grid", ctypes.c_int32 * 3),
         ("combine_threads", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
     ]

@@ -13,7 +13,9 @@ constexpr int kKeysPerStep = 32;     // keys one wavefront consumes per iteratio
 constexpr int kRows = 16;            // stacked query rows per MFMA tile (one row block)
 constexpr int kMaxT = 16;            // verify rows per sequence (tree-mask words are 16 bits used)
 constexpr int kWavesPerGroup = 4;    // wavefronts per segment workgroup (default of the table below)
-constexpr int kMaxSegBlocks = 1040;  // LDS slots for a segment's block ids
+// LDS slots for a segment's block ids: 1040, or 2080 for 1-slot pages (one id
+// per key), whose segments would otherwise span at most 32 steps.
+constexpr int seg_block_slots(int bs) { return bs == 1 ? 2080 : 1040; }
 constexpr int kDeviceContract = 5;   // value of PA_ERR_DEVICE_CONTRACT
 constexpr float kRescaleLog2 = 8.f;  // softmax reference max moves only past this margin
 
@@ -80,8 +82,8 @@ hipError_t launch_combine(const CombineArgs& a, int out_dtype, int D, int thread
 hipError_t launch_append(const AppendArgs& a, int q_dtype, int kv_dtype, int D, hipStream_t st);
 // Most steps a segment or work-list chunk may span: its block ids (one more
 // for a step that starts inside a page, one more for the last page) must fit
-// the kMaxSegBlocks-entry LDS table.
-constexpr int max_steps_per_segment(int bs) { return (kMaxSegBlocks - 2) * bs / kKeysPerStep; }
+// the seg_block_slots(bs)-entry LDS table.
+constexpr int max_steps_per_segment(int bs) { return (seg_block_slots(bs) - 2) * bs / kKeysPerStep; }
 
 // Combine workgroup size: enough threads that each loads at most 8 of the S
 // partials of its (token, q head) row (one batch of loads), 256..1024.
@@ -113,10 +115,8 @@ struct SegConfig {
 constexpr SegConfig seg_config(int kv_dtype, int D, int rb, int bs = 16) {
   // Pages of fewer than 16 slots: one 8-wavefront workgroup per CU as for
   // 16-slot pages (C2 shape at 32k, us per call: 2 slots 29.8 vs 29.9 for two
-  // 4-wavefront groups, 4 slots 27.6 vs 28.1, 8 slots 27.8 vs 28.0), except
-  // 1-slot pages: their 32-step segment cap (one block id per key) then needs
-  // more segments than one round of workgroups holds.
-  if (bs < 16) return D >= 256 ? SegConfig{1, 1, 1} : bs >= 2 ? SegConfig{2, 1, 1, 8} : SegConfig{2, 1, 2};
+  // 4-wavefront groups, 4 slots 27.6 vs 28.1, 8 slots 27.8 vs 28.0).
+  if (bs < 16) return D >= 256 ? SegConfig{1, 1, 1} : SegConfig{2, 1, 1, 8};
   if (rb > 1) return rb == 2 && D <= 128 ? SegConfig{2, 1, 1, 8} : SegConfig{1, 1, 1};
   if (kv_dtype == kU8)
     return D >= 256 ? SegConfig{2, 1, 1, 8} : D >= 128 ? SegConfig{1, 2, 1} : SegConfig{4, 1, 4};

@@ -338,7 +338,8 @@ void pa_segment(SegmentArgs a) {
   constexpr int ROWS = kRows * RB;                // stacked rows this instance holds
   static_assert((BS % 16 == 0 || BS == 1 || BS == 2 || BS == 4 || BS == 8) && kKeysPerStep == 32,
                 "two 16-slot sub-tiles per step, within one page or across 16 / BS pages");
-  __shared__ int s_bt[kMaxSegBlocks];
+  constexpr int kSegSlots = seg_block_slots(BS);
+  __shared__ int s_bt[kSegSlots];
   __shared__ float s_m[NW][ROWS];
   __shared__ float s_l[NW][ROWS];
   __shared__ __attribute__((aligned(16))) float s_o[NW][ROWS][OSTRIDE];
@@ -390,7 +391,7 @@ void pa_segment(SegmentArgs a) {
   // requested together with the sequence metadata — one memory round trip
   // before the first KV load instead of two.  The loads stay inside the
   // block-table row; ids of blocks past the sequence are never used.
-  constexpr int kSlots = (kMaxSegBlocks + NW * kWave - 1) / (NW * kWave);
+  constexpr int kSlots = (kSegSlots + NW * kWave - 1) / (NW * kWave);
   int spec_id[kSlots];
   const int spec_lo = (st_begin * kKeysPerStep) / BS;
   const bool spec = a.window == 0 && !a.worklist;

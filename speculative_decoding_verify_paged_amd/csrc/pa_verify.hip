@@ -120,6 +120,7 @@ int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_ve
   pl->span = (int32_t)span;
   const int nw = pav::seg_config(p->kv_dtype, p->head_dim, pl->row_blocks, p->block_size).waves_per_group;
   pl->waves_per_group = nw;
+  pl->max_steps_per_segment = (int32_t)max_sps;
   pl->grid[0] = p->num_kv_heads;
   pl->grid[1] = p->num_seqs;
   pl->grid[2] = (int32_t)S;

@@ -41,11 +41,11 @@ def test_struct_layout_matches_header():
 #include <stdio.h>
 #include "{HEADER}"
 int main(void) {{
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(pa_verify_params),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(pa_verify_params),
          offsetof(pa_verify_params, workspace), offsetof(pa_verify_params, stream),
          offsetof(pa_verify_params, max_query_len), offsetof(pa_verify_params, tree_mask),
          sizeof(pa_verify_plan), offsetof(pa_verify_plan, row_blocks),
-         offsetof(pa_verify_plan, workspace_bytes));
+         offsetof(pa_verify_plan, max_steps_per_segment), offsetof(pa_verify_plan, workspace_bytes));
   return 0;
 }}
 """
@@ -59,7 +59,8 @@ int main(void) {{
     want = [ctypes.sizeof(pav.PaVerifyParams), pav.PaVerifyParams.workspace.offset,
             pav.PaVerifyParams.stream.offset, pav.PaVerifyParams.max_query_len.offset,
             pav.PaVerifyParams.tree_mask.offset, ctypes.sizeof(pav.PaVerifyPlan),
-            pav.PaVerifyPlan.row_blocks.offset, pav.PaVerifyPlan.workspace_bytes.offset]
+            pav.PaVerifyPlan.row_blocks.offset, pav.PaVerifyPlan.max_steps_per_segment.offset,
+            pav.PaVerifyPlan.workspace_bytes.offset]
     assert got == want
 
 
@@ -206,7 +207,8 @@ def check_plan_covers(pl, max_ctx, window=0, nseq=1, hkv=8, bs=16, tq=4):
     else:   # work list: one workgroup per chunk, at least one round of them
         assert pl["worklist"] == 1 and pl["grid"][:2] == [hkv, 1]
         assert pl["grid"][2] >= pl["target_items"]
-    assert pl["steps_per_segment"] * pl["keys_per_step"] // bs + 2 <= 1040
+    assert pl["steps_per_segment"] <= pl["max_steps_per_segment"]
+    assert pl["max_steps_per_segment"] * pl["keys_per_step"] // bs + 2 <= (2080 if bs == 1 else 1040)
 
 
 @pytest.mark.parametrize("L,T", [(8192, 1), (8192, 4), (32768, 1), (32768, 3), (32768, 4)])
@@ -255,7 +257,7 @@ def test_plan_window_and_forced_segments():
               num_blocks=801, max_blocks_per_seq=801, sliding_window=1024, num_tokens=2,
               q_dtype=pav.PA_BF16, kv_dtype=pav.PA_BF16)
     check_plan_covers(pl, 51202, window=1024, hkv=16, bs=64, tq=2)
-    min_s = -(-1025 // ((1040 - 2) * 16 // 32))     # LDS block-id limit per segment
+    min_s = -(-1025 // ((1040 - 2) * 16 // 32))     # LDS block-id limit per segment (16-slot pages)
     for S in (1, 2, 7, 63, 5000):
         pl = plan(32771, num_segments=S)
         check_plan_covers(pl, 32771)
@@ -276,9 +278,9 @@ def test_plan_ragged_batch():
 
 
 def test_plan_grid_limits_are_reported():
-    # 1-slot pages hold 32 steps per segment in the block-id table: 100M keys
+    # 1-slot pages hold 64 steps per segment in the block-id table: 200M keys
     # need more than 65535 segments (the grid's z limit)
-    big = 100_000_000
+    big = 200_000_000
     with pytest.raises(pav.PaVerifyError) as e:
         plan(big, block_size=1, max_blocks_per_seq=big, num_blocks=1 << 20)
     assert e.value.code == pav.PA_ERR_UNSUPPORTED
@@ -291,4 +293,5 @@ def test_plan_grid_limits_are_reported():
     # just inside the limits
     pl = plan(100_000, block_size=1, max_blocks_per_seq=100_000, num_blocks=1 << 20,
               num_seqs=600, num_tokens=600)
-    assert pl["grid"][2] == 600 * -(-3125 // 32) and pl["grid"][2] <= 65535
+    assert pl["max_steps_per_segment"] == 64
+    assert pl["grid"][2] == 600 * -(-3125 // 64) and pl["grid"][2] <= 65535

@@ -117,7 +117,7 @@ def test_contexts_where_the_block_id_table_sets_the_segment_count():
                             num_blocks=case.num_blocks, max_blocks_per_seq=case.max_blocks_per_seq,
                             q_dtype=case.q_dtype, kv_dtype=case.kv_dtype)
         plan = pav.pa_verify_make_plan(p, case.max_context_len, 256)
-        table_steps = (1040 - 2) * case.block_size // 32          # steps whose ids fit the table
+        table_steps = plan["max_steps_per_segment"]                # steps whose ids fit the table
         need = -(-plan["num_steps"] // table_steps)
         print(case.name, plan["num_segments"], need, flush=True)
         assert plan["num_segments"] == need and plan["steps_per_segment"] <= table_steps, plan

@@ -52,7 +52,7 @@ def test_worklist_chunks_fit_the_planned_grid(bs):
                    block_size=bs, max_blocks_per_seq=mbps, num_blocks=n * mbps, max_query_len=4),
             ctx, 256)
         assert pl["worklist"] == 1 and pl["grid"][:2] == [hkv, 1]
-        max_sps = (1040 - 2) * bs // 32
+        max_sps = pl["max_steps_per_segment"]
         steps = [cdiv(L + int(t), 32) for L, t in zip(Ls, Ts)]
         C = chunk_size(steps, pl["target_items"], pl["steps_per_segment"], max_sps)
         chunks = [cdiv(s, C) for s in steps]
