@@ -47,6 +47,13 @@ def workloads():
         "gqa4_d128_f16_L32768_bs4": lambda T: pi.config2(32768, T, block_size=4),
         "gqa4_d128_f16_L32768_bs8": lambda T: pi.config2(32768, T, block_size=8),
         "u8kv_d256_L32768": lambda T: pi.config3(32768, T),
+        # the same cache shapes at the other head sizes (not among the pages' workloads)
+        "gqa4_d64_f16_L32768": lambda T: pi.build_case(
+            [20, 32768, T], [32768], [T], num_q_heads=32, num_kv_heads=8, head_dim=64,
+            block_size=16, name=f"gqa4_d64_f16_L32768_T{T}"),
+        "u8kv_d128_L32768": lambda T: pi.build_case(
+            [21, 32768, T], [32768], [T], num_q_heads=16, num_kv_heads=4, head_dim=128,
+            block_size=16, kv_dtype=pi.U8, name=f"u8kv_d128_L32768_T{T}"),
         "swa_pair_global_L32768": lambda T: pi.config4(32768, window=0, T=T),
         "swa_pair_global_L51200": lambda T: pi.config4(51200, window=0, T=T),
         "swa_pair_window1024_L32768": lambda T: pi.config4(32768, window=1024, T=T),

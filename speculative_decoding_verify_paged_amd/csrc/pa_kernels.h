@@ -92,23 +92,28 @@ constexpr int combine_threads(int S, int D) {
 }
 
 // Per (cache dtype, head_dim, row blocks, block size): wavefronts per SIMD
-// the segment kernel is compiled for (its register budget, no spills), the
-// steps each wavefront keeps loaded (1: load then compute; 2: the next
-// step's loads in flight during this step's math), the segment workgroups
-// the planner puts on each CU (at most the resident count, 4 SIMDs per CU)
-// and the wavefronts per workgroup.  Measured on MI355X at 32k context:
+// the segment kernel is compiled for (its register budget, no spills; each
+// wavefront holds one step in registers: load, then compute), the segment
+// workgroups the planner puts on each CU (at most the resident count, 4
+// SIMDs per CU) and the wavefronts per workgroup.  Measured on MI355X at 32k
+// context:
 // head_dim 128 (16-bit) and u8 head_dim 256 run best as one 8-wavefront
 // workgroup per CU, two wavefronts per SIMD with one step each (C2 shape
 // 27.6 vs 28.2 µs per call for 4 wavefronts with two steps each; u8 21.4 vs
 // 22.5 µs) — two workgroups of 4 instead would double the partials the
-// combine reads.  Two row blocks at head_dim <= 128 still fit two
+// combine reads.  The same holds elsewhere (C2-shaped calls at 32k, µs per
+// call): head_dim 64 as two 8-wavefront workgroups per CU at four
+// wavefronts per SIMD, 17.4 vs 17.7 for four 4-wavefront ones (one
+// 16-wavefront one: 18.6); u8 head_dim 128 (16 q / 4 KV heads) as one
+// 8-wavefront workgroup at two per SIMD, 14.5 vs 15.4 for one 4-wavefront
+// workgroup with two steps in flight (12 wavefronts at three per SIMD:
+// 15.2).  Two row blocks at head_dim <= 128 still fit two
 // wavefronts per SIMD (T = 5 and 8 at 32k: 30.0 and 30.7 us per call against
 // 30.35 and 31.3 at one); more row blocks, or head_dim 256, need the whole
 // register file of one wavefront per SIMD (and the LDS merge buffer allows
 // one workgroup per CU).
 struct SegConfig {
   int waves_per_simd;
-  int prefetch;
   int groups_per_cu;
   int waves_per_group = kWavesPerGroup;
 };
@@ -116,11 +121,11 @@ constexpr SegConfig seg_config(int kv_dtype, int D, int rb, int bs = 16) {
   // Pages of fewer than 16 slots: one 8-wavefront workgroup per CU as for
   // 16-slot pages (C2 shape at 32k, us per call: 2 slots 29.8 vs 29.9 for two
   // 4-wavefront groups, 4 slots 27.6 vs 28.1, 8 slots 27.8 vs 28.0).
-  if (bs < 16) return D >= 256 ? SegConfig{1, 1, 1} : SegConfig{2, 1, 1, 8};
-  if (rb > 1) return rb == 2 && D <= 128 ? SegConfig{2, 1, 1, 8} : SegConfig{1, 1, 1};
+  if (bs < 16) return D >= 256 ? SegConfig{1, 1} : SegConfig{2, 1, 8};
+  if (rb > 1) return rb == 2 && D <= 128 ? SegConfig{2, 1, 8} : SegConfig{1, 1};
   if (kv_dtype == kU8)
-    return D >= 256 ? SegConfig{2, 1, 1, 8} : D >= 128 ? SegConfig{1, 2, 1} : SegConfig{4, 1, 4};
-  return D >= 256 ? SegConfig{1, 1, 1} : D >= 128 ? SegConfig{2, 1, 1, 8} : SegConfig{4, 1, 4};
+    return D >= 128 ? SegConfig{2, 1, 8} : SegConfig{4, 4};
+  return D >= 256 ? SegConfig{1, 1} : D >= 128 ? SegConfig{2, 1, 8} : SegConfig{4, 2, 8};
 }
 constexpr int groups_per_cu(int kv_dtype, int D, int rb, int bs) {
   return seg_config(kv_dtype, D, rb, bs).groups_per_cu;

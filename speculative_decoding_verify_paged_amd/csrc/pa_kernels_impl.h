@@ -325,7 +325,7 @@ __device__ __forceinline__ int wl_find(const SegmentArgs& a, int rows, int C, in
 // blocks of stacked query rows (G * T <= 16 * RB): each K/V operand a step
 // loads (and, for u8, converts) feeds one MFMA per row block.
 // ---------------------------------------------------------------------------
-template <int QT, int KV, int D, int BS, int NW, int WPE, int PF, int RB>
+template <int QT, int KV, int D, int BS, int NW, int WPE, int RB>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE)))
 void pa_segment(SegmentArgs a) {
   constexpr bool U8 = KV == kU8;
@@ -561,8 +561,8 @@ void pa_segment(SegmentArgs a) {
   // Every load is issued unconditionally: a sub-tile holding no key of
   // [lo0, ctx) reads the segment's first page instead (always a valid
   // address) and is masked out in compute_step.  Branch-free loads keep the
-  // outstanding-load count static, so the wait before a step's math covers
-  // that step's loads only, not the prefetch of the next one.
+  // outstanding-load count static, so the compiler's waits inside a step's
+  // math are for exactly the registers they need.
   // Pages of 1, 2, 4 or 8 slots: K pages are row-major [slot][d] and V pages
   // d-major [d][slot], so each lane gathers its own operand pieces: the K row
   // of its slot (the same 16 B chunks a tiled sub-tile load delivers), and
@@ -976,12 +976,9 @@ void pa_segment(SegmentArgs a) {
       pv(std::true_type{});
   };
 
-  // Steps st_begin + wave, + NW, ...  PF == 2: ping-pong between two register
-  // sets so the next step's loads are in flight while this step computes,
-  // with no register copies (a copy of a register still being loaded would
-  // wait).  PF == 1: one register set; the other wavefronts of the CU keep
-  // the memory system busy while this one computes.
-  if constexpr (PF == 1) {
+  // Steps st_begin + wave, + NW, ...: one register set; the other
+  // wavefronts of the CU keep the memory system busy while this one computes.
+  {
     Step ra;
     int st = st_begin + wave;
     if (st < st_end) {
@@ -991,29 +988,6 @@ void pa_segment(SegmentArgs a) {
       for (st += NW; st < st_end; st += NW) {
         load_step(st, ra);
         compute_step(st, ra);
-      }
-    }
-  } else {
-    int st = st_begin + wave;
-    if (st < st_end) {
-      Step ra, rb;
-      load_step(st, ra);
-      finish_q();
-      while (true) {
-        if (st + NW >= st_end) {
-          compute_step(st, ra);
-          break;
-        }
-        load_step(st + NW, rb);
-        compute_step(st, ra);
-        st += NW;
-        if (st + NW >= st_end) {
-          compute_step(st, rb);
-          break;
-        }
-        load_step(st + NW, ra);
-        compute_step(st, rb);
-        st += NW;
       }
     }
   }
@@ -1087,7 +1061,7 @@ template <int QT, int KV, int D, int BS, int RB>
 hipError_t launch_seg(const SegmentArgs& a, dim3 grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   constexpr SegConfig c = seg_config(KV, D, RB, BS);
   static_assert(c.waves_per_group <= 4 * c.waves_per_simd, "a workgroup must fit on one CU");
-  constexpr auto kern = pa_segment<QT, KV, D, BS, c.waves_per_group, c.waves_per_simd, c.prefetch, RB>;
+  constexpr auto kern = pa_segment<QT, KV, D, BS, c.waves_per_group, c.waves_per_simd, RB>;
   return launch_kernel(reinterpret_cast<const void*>(kern), grid, dim3(c.waves_per_group * kWave),
                        st, a, ev0, ev1);
 }
