@@ -51,6 +51,9 @@ def workloads():
         "gqa4_d64_f16_L32768": lambda T: pi.build_case(
             [20, 32768, T], [32768], [T], num_q_heads=32, num_kv_heads=8, head_dim=64,
             block_size=16, name=f"gqa4_d64_f16_L32768_T{T}"),
+        "u8kv_d64_L32768": lambda T: pi.build_case(
+            [22, 32768, T], [32768], [T], num_q_heads=32, num_kv_heads=8, head_dim=64,
+            block_size=16, kv_dtype=pi.U8, name=f"u8kv_d64_L32768_T{T}"),
         "u8kv_d128_L32768": lambda T: pi.build_case(
             [21, 32768, T], [32768], [T], num_q_heads=16, num_kv_heads=4, head_dim=128,
             block_size=16, kv_dtype=pi.U8, name=f"u8kv_d128_L32768_T{T}"),
