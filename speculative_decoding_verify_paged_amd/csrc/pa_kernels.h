@@ -109,7 +109,9 @@ constexpr int combine_threads(int S, int D) {
 // workgroup with two steps in flight (12 wavefronts at three per SIMD:
 // 15.2).  Two row blocks at head_dim <= 128 still fit two
 // wavefronts per SIMD (T = 5 and 8 at 32k: 30.0 and 30.7 us per call against
-// 30.35 and 31.3 at one); more row blocks, or head_dim 256, need the whole
+// 30.35 and 31.3 at one), and so do three or four at head_dim 64 (32 q / 8
+// KV heads, T = 12 and 16 at 32k: 21.7 and 25.0 us per call against 25.2
+// and 28.6 at one); more row blocks at head_dim 128, or head_dim 256, need the whole
 // register file of one wavefront per SIMD (and the LDS merge buffer allows
 // one workgroup per CU).
 struct SegConfig {
@@ -122,7 +124,7 @@ constexpr SegConfig seg_config(int kv_dtype, int D, int rb, int bs = 16) {
   // 16-slot pages (C2 shape at 32k, us per call: 2 slots 29.8 vs 29.9 for two
   // 4-wavefront groups, 4 slots 27.6 vs 28.1, 8 slots 27.8 vs 28.0).
   if (bs < 16) return D >= 256 ? SegConfig{1, 1} : SegConfig{2, 1, 8};
-  if (rb > 1) return rb == 2 && D <= 128 ? SegConfig{2, 1, 8} : SegConfig{1, 1};
+  if (rb > 1) return (rb == 2 && D <= 128) || D <= 64 ? SegConfig{2, 1, 8} : SegConfig{1, 1};
   if (kv_dtype == kU8)
     return D >= 128 ? SegConfig{2, 1, 8} : SegConfig{4, 4};
   return D >= 256 ? SegConfig{1, 1} : D >= 128 ? SegConfig{2, 1, 8} : SegConfig{4, 2, 8};
