@@ -415,6 +415,22 @@ def test_wide_T_other_shapes():
         _full(case)
 
 
+def test_wide_T_head_dim_64_two_wavefronts_per_simd():
+    """Three and four row blocks at head_dim 64 (8-wavefront workgroups, two
+    wavefronts per SIMD): the 32k shapes timed, a u8 cache, a ragged batch."""
+    cases = [pi.build_case([710, 0], [32768], [12], num_q_heads=32, num_kv_heads=8, head_dim=64,
+                           block_size=16, name="wide_d64_f16_L32768_T12"),
+             pi.build_case([710, 1], [8192], [16], num_q_heads=16, num_kv_heads=4, head_dim=64,
+                           block_size=16, q_dtype=pi.F16, kv_dtype=pi.U8, poison=True,
+                           name="wide_d64_u8_L8192_T16"),
+             pi.build_case([710, 2], [5000, 17, 900], [10, 12, 9], num_q_heads=8, num_kv_heads=2,
+                           head_dim=64, block_size=32, q_dtype=pi.BF16, kv_dtype=pi.BF16,
+                           poison=True, name="wide_d64_bf16_ragged")]
+    _full(cases[0])
+    _full(cases[1])
+    _full(cases[2], rounding_aware=True)       # 17..30-key rows reach |out| ~ 1 in bf16
+
+
 def test_wide_T_ragged_and_short():
     rng = np.random.default_rng(123)
     for rep in range(3):
