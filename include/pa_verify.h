@@ -80,9 +80,11 @@
  * Errors.  Host-checkable problems return a nonzero pa_status before anything
  * is enqueued and leave `out` untouched.  Problems that only the device can see
  * (T_s outside [1, max_query_len], L_s < 0, L_s + T_s > max_context_len, a physical block id
- * outside [0, num_blocks), non-monotone subsequence_begins) set the sticky
- * device status word PA_ERR_DEVICE_CONTRACT in the workspace and make the
- * affected sequence's output rows NaN; pa_verify_read_status reports it.
+ * outside [0, num_blocks), non-monotone subsequence_begins, and with an f16 q
+ * a u8 V scale whose weighted product overflows f16, see pa_verify_forward_u8)
+ * set the sticky device status word PA_ERR_DEVICE_CONTRACT in the workspace
+ * and make the affected sequence's output rows NaN; pa_verify_read_status
+ * reports it.
  */
 #ifndef PA_VERIFY_H
 #define PA_VERIFY_H
@@ -204,7 +206,15 @@ int pa_verify_forward(const void* q, const void* k_cache, const void* v_cache,
 /* The same operation over a u8 KV cache (kv_dtype == PA_U8): a cached value u
  * of token t, KV head g stands for (u - zp) * scale with (scale, zp) read as
  * f16 from k_scale_zp / v_scale_zp[block, g, slot, 0..1].  Dequantisation
- * follows that formula exactly in f32/f16 arithmetic inside the kernel. */
+ * follows that formula exactly in f32/f16 arithmetic inside the kernel.
+ * Range: with an f16 q, the PV product takes each softmax weight (at most
+ * 256 relative to the kernel's running reference) times the key's V scale as
+ * an f16 operand, so V scales up to 255.875 (65504 / 256; a V row range up to
+ * 65248 quantised by pa_kv_append_u8) always give the result.  A larger V
+ * scale is outside the contract: where its product overflows f16, the rows
+ * of that KV head become NaN and the device status word is set
+ * (PA_ERR_DEVICE_CONTRACT); a wrong finite result is never returned.  A bf16
+ * q has no such bound. */
 int pa_verify_forward_u8(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
                          const void* k_scale_zp, const void* v_scale_zp,
                          const int32_t* block_tables, const int32_t* past_lens,

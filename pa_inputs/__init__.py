@@ -395,6 +395,69 @@ def _poison(k, v, ksz, vsz, kv_dtype, bt, past_lens, Ts, bs, W, spare):
         kill(int(blk), np.arange(bs))
 
 
+def peaked(case: Case, seed: Sequence[int], *, stairs: int = 8, gap: float = 7.0,
+           base: float = 8.0, cluster: bool = True) -> Case:
+    """A copy of ``case`` whose softmax is sharply peaked late in each row's keys.
+
+    For every KV head g a random unit direction u_g is drawn; every q row of the
+    group becomes sqrt(D) * u_g + N(0, 1) noise, and a staircase of keys along
+    u_g is planted in every sequence's cache: key j of the staircase is
+    c_j * u_g with c_j = base + (j + 1) * gap, so with the usual scale 1/sqrt(D)
+    its logit is about c_j (natural units) and each stair tops the one before
+    by about ``gap`` (7 natural units is about 10 in log2 units), while the
+    other keys' logits stay around N(0, 2).  The stairs sit at increasing
+    positions of the keys every row of the sequence sees (the window's start
+    for a sliding-window layer, up to the last cached position), the last ones
+    late in the context; with ``cluster`` a few more follow the second-to-last
+    at 32, 64, 128 and 256 positions, so one scan meets several consecutive
+    jumps.  The value rows are left as drawn.  Drawn with its own generator
+    from ``seed``; q, the planted K rows (re-quantised for a u8 cache) and the
+    name change, nothing else."""
+    rng = np.random.default_rng([991] + list(seed))
+    D, Hkv, Hq, bs = case.head_dim, case.num_kv_heads, case.num_q_heads, case.block_size
+    G = Hq // Hkv
+    u8 = case.kv_dtype == U8
+    u = rng.standard_normal((Hkv, D))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    qf = (math.sqrt(D) * np.repeat(u, G, axis=0)[None] +
+          rng.standard_normal((case.num_tokens, Hq, D))).astype(np.float32)
+    q = f32_to_bits(qf, case.q_dtype)
+    kl, vl = case.logical_pages()
+    kl = kl.copy()
+    ksz = None if case.k_scale_zp is None else case.k_scale_zp.copy()
+    for s in range(case.num_seqs):
+        L = int(case.past_lens[s])
+        lo0 = max(0, L + 1 - case.sliding_window) if case.sliding_window > 0 else 0
+        if L - lo0 < 1:
+            continue                                  # no past key every row sees
+        span = L - lo0
+        pos = [lo0 + (span * (j + 1)) // (stairs + 1) for j in range(stairs - 1)] + [L - 1]
+        if cluster:
+            extra = [pos[-2] + o for o in (32, 64, 128, 256) if pos[-2] + o < L - 1]
+            pos = pos[:-1] + extra + pos[-1:]
+        seen = []
+        for t in pos:                                  # strictly increasing, distinct
+            if not seen or t > seen[-1]:
+                seen.append(t)
+        for j, t in enumerate(seen):
+            c = base + (j + 1) * gap
+            blk, slot = case.block_tables[s, t // bs], t % bs
+            row = (c * u).astype(np.float32)           # [Hkv, D]
+            if u8:
+                codes, s16, z16 = quantize_u8(row)
+                kl[blk, :, slot, :] = codes
+                ksz[blk, :, slot, 0] = s16
+                ksz[blk, :, slot, 1] = z16
+            else:
+                kl[blk, :, slot, :] = f32_to_bits(row, case.kv_dtype)
+    out = Case(**{f.name: getattr(case, f.name) for f in dataclasses.fields(case)})
+    out.q = q
+    out.k_cache = tile_k(kl, u8).reshape(case.k_cache.shape)
+    out.k_scale_zp = ksz
+    out.name = case.name + "_peaked"
+    return out
+
+
 # ----------------------------------------------------------------------------
 # the five workloads
 # ----------------------------------------------------------------------------

@@ -139,6 +139,10 @@ def pa_verify_workspace_bytes(params: PaVerifyParams, max_context_len: int) -> i
 # torch-facing calls
 # ---------------------------------------------------------------------------
 _ws_cache = {}
+# Workspaces the cached one replaced, kept allocated until the process ends: a
+# HIP graph captured before a growth still holds their pointers and writes its
+# partials and status word there on every replay.
+_ws_retired = {}
 
 
 def _torch():
@@ -166,7 +170,10 @@ def workspace(nbytes: int, device):
     workspaces.  Allocating or growing it synchronises the device (no call
     still uses the old buffer, and the zeroed status word is in place before
     any stream runs on the new one), so it cannot happen during graph capture:
-    make one eager call with the largest shape first."""
+    make one eager call with the largest shape first.  Growth at least doubles
+    the buffer, and a replaced buffer stays allocated (a graph captured
+    earlier keeps using it; ``pa_verify_read_status`` reads its status word
+    too), so the memory held is at most twice the largest need."""
     torch = _torch()
     key = (str(device),)
     old = _ws_cache.get(key)
@@ -175,9 +182,10 @@ def workspace(nbytes: int, device):
             raise RuntimeError("the cached workspace must be sized before graph capture: make one "
                                "eager call with the largest shape first, or pass workspace=")
         torch.cuda.synchronize(device)
-        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        size = max(nbytes, 1 << 20, 0 if old is None else 2 * old.numel())
+        buf = torch.zeros(size, dtype=torch.uint8, device=device)
         if old is not None:
-            buf[:4].copy_(old[:4])                  # a pending sticky status survives the growth
+            _ws_retired.setdefault(key, []).append(old)
         torch.cuda.synchronize(device)
         _ws_cache[key] = buf
         return buf
@@ -276,6 +284,8 @@ def _call(u8, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_le
     if ws is None:
         with torch.cuda.device(dev):
             ws = workspace(need, dev)
+    else:
+        _check(ws, "workspace", dtype=torch.uint8, ndim=1, device=dev)
     params.workspace = ws.data_ptr()
     params.workspace_bytes = ws.numel() * ws.element_size()
     if prof_events is not None:
@@ -337,21 +347,26 @@ def pa_verify_forward_u8(q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tabl
 
 
 def pa_verify_read_status(device=None) -> int:
-    """Synchronise and read-and-clear the sticky device status word of the cached workspace."""
+    """Synchronise and read-and-clear the sticky device status word of the
+    cached workspace and of the workspaces it replaced (graphs captured
+    before a growth still write there); PA_ERR_DEVICE_CONTRACT if any was set."""
     torch = _torch()
     dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
-    buf = _ws_cache.get((str(dev),))
-    if buf is None:
-        return PA_OK
-    p = PaVerifyParams()
-    p.workspace = buf.data_ptr()
-    p.workspace_bytes = buf.numel()
-    p.stream = torch.cuda.current_stream(dev).cuda_stream or None
-    st = ctypes.c_int32(0)
-    rc = lib().pa_verify_read_status(ctypes.byref(p), ctypes.byref(st))
-    if rc != PA_OK:
-        raise PaVerifyError(rc)
-    return int(st.value)
+    key = (str(dev),)
+    bufs = list(_ws_retired.get(key, [])) + ([_ws_cache[key]] if key in _ws_cache else [])
+    result = PA_OK
+    for buf in bufs:
+        p = PaVerifyParams()
+        p.workspace = buf.data_ptr()
+        p.workspace_bytes = buf.numel()
+        p.stream = torch.cuda.current_stream(dev).cuda_stream or None
+        st = ctypes.c_int32(0)
+        rc = lib().pa_verify_read_status(ctypes.byref(p), ctypes.byref(st))
+        if rc != PA_OK:
+            raise PaVerifyError(rc)
+        if st.value != PA_OK:
+            result = int(st.value)
+    return result
 
 
 def prepare_forward(q, k_cache, v_cache, block_tables, past_lens, subsequence_begins,

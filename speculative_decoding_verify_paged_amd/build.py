@@ -73,5 +73,46 @@ def build(extra_flags=(), verbose: bool = False) -> str:
     return LIB
 
 
+# The host-side sanitizers for the checked build below: each flag goes to the
+# host compilation only (the kernels are built as usual).
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def build_host_checked(out_dir: str) -> str:
+    """A copy of libpa_verify.so whose host code (argument checks, planner,
+    launch set-up: csrc/pa_verify.hip) is built with AddressSanitizer and
+    UndefinedBehaviorSanitizer, linked with the kernel objects of the regular
+    build (which must exist: run build() first).  Load it only in a process
+    that preloads clang's ASan runtime (``asan_runtime()``).  Returns its path."""
+    os.makedirs(out_dir, exist_ok=True)
+    host = os.path.join(CSRC, "pa_verify.hip")
+    kernels = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in sources() if s != host]
+    missing = [k for k in kernels if not os.path.exists(k)]
+    if missing:
+        raise RuntimeError(f"regular build objects missing ({missing[0]}): run build() first")
+    obj = os.path.join(out_dir, "pa_verify_checked.o")
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g", "-fno-omit-frame-pointer"]
+    r = subprocess.run([hipcc(), *flags, *HOST_SANITIZE, "-c", host, "-o", obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {host}:\n{r.stderr}")
+    out = os.path.join(out_dir, "libpa_verify_checked.so")
+    _link([obj] + kernels, out)
+    return out
+
+
+def asan_runtime() -> str:
+    """clang's shared ASan runtime (it carries the UBSan handlers too)."""
+    import glob
+    root = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    for base in (os.path.join(root, "llvm"), root, "/opt/rocm/llvm"):
+        hits = sorted(glob.glob(os.path.join(base, "lib", "clang", "*", "lib", "linux",
+                                             "libclang_rt.asan-x86_64.so")))
+        if hits:
+            return hits[-1]
+    raise RuntimeError("clang's ASan runtime not found")
+
+
 if __name__ == "__main__":
     build(sys.argv[1:], verbose=True)

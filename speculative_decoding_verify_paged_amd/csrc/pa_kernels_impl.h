@@ -999,13 +999,19 @@ void pa_segment(SegmentArgs a) {
   for (int rb = 0; rb < RB; ++rb) {
     l_run[rb] += __shfl_xor(l_run[rb], 16, kWave);
     l_run[rb] += __shfl_xor(l_run[rb], 32, kWave);
+    const int r = rb * kRows + n16;
     if constexpr (U8) {
       c_run[rb] += __shfl_xor(c_run[rb], 16, kWave);
       c_run[rb] += __shfl_xor(c_run[rb], 32, kWave);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[rb][dt] -= c_run[rb];
+      // f16 q: a weight (at most 2^kRescaleLog2 against the reference max)
+      // times a V scale above 65504 / 256 can round to inf in f16; the row
+      // sum of those products is then inf or NaN for good.  Never silent:
+      // the workgroup's partials become NaN and the status word is set.
+      if constexpr (QT == kF16)
+        if (r < R && !__builtin_isfinite(c_run[rb])) s_bad = 1;
     }
-    const int r = rb * kRows + n16;
     if (q4 == 0) {
       s_m[wave][r] = m_run[rb];
       s_l[wave][r] = l_run[rb];

@@ -93,13 +93,3 @@ def excess(case, got: np.ndarray, ref: np.ndarray) -> float:
     ulp of bf16 alone is 2e-3)."""
     bound = tol(case) + half_ulp(ref, case.q_dtype)
     return float(np.max(np.abs(got - ref) - bound))
-
-
-def sample_pairs(case, n, seed=0):
-    """n (token, q head) pairs spread over the batch, always including the
-    first and last token and the first and last head."""
-    rng = np.random.default_rng(seed)
-    pairs = {(0, 0), (case.num_tokens - 1, case.num_q_heads - 1)}
-    while len(pairs) < min(n, case.num_tokens * case.num_q_heads):
-        pairs.add((int(rng.integers(case.num_tokens)), int(rng.integers(case.num_q_heads))))
-    return np.array(sorted(pairs), dtype=np.int32)

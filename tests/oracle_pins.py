@@ -31,6 +31,12 @@ What pins what:
                   equals the causal rows bitwise; a mask without the row's own
                   bit changes nothing; causal rows with up to 16 new tokens
                   against SDPA.
+  * pairs       — the subset form (a list of (token, q head) rows, as the
+                  sampled checks at large sizes use it) against torch SDPA on
+                  the same rows, and bit for bit against the full output
+                  indexed at those rows: single, ragged, windowed and tree
+                  cases, pairs unsorted and repeated, token and head indices
+                  that differ.
 """
 from __future__ import annotations
 
@@ -478,8 +484,49 @@ def pin_append(orc):
         assert np.array_equal(ks2[~touched], case.k_scale_zp[~touched])
 
 
+def pin_pairs(orc):
+    rng = np.random.default_rng(29)
+    cases = [c for c in tiny_random_cases(24, seed=31) if c.num_tokens * c.num_q_heads >= 4]
+    for k, case in enumerate(cases):
+        parents = None
+        if k % 3 == 2 and case.sliding_window == 0:
+            parents = [pi.random_parents(rng, T) for T in case.Ts]
+            case = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+            case.tree_mask = pi.tree_masks(parents)
+        n = case.num_tokens * case.num_q_heads
+        # unsorted, with repeats; the last token's last head and the first
+        # token's first head always among them
+        idx = rng.integers(0, n, size=max(4, n // 2))
+        idx = np.concatenate([idx, [n - 1, 0, idx[0]]])
+        pairs = np.stack([idx // case.num_q_heads, idx % case.num_q_heads], axis=1).astype(np.int32)
+        got = orc.forward(case, pairs=pairs)
+        assert got.shape == (len(pairs), case.head_dim), case.name
+        full = orc.forward(case)
+        assert np.array_equal(got, full[pairs[:, 0], pairs[:, 1]]), case.name
+        ref = sdpa_reference(case, parents)[pairs[:, 0], pairs[:, 1]]
+        err = np.max(np.abs(got - ref))
+        assert np.all(np.isfinite(got)) and err <= 1e-12, f"{case.name} pairs: max err {err}"
+    # rows where the token index exceeds the head count and the other way
+    # round: a token/head mix-up cannot hide behind square index ranges
+    case = pi.build_case([130], [40, 7, 90], [4, 2, 3], num_q_heads=2, num_kv_heads=1,
+                         head_dim=32, block_size=16, name="pairs_tall")
+    pairs = np.array([[8, 1], [5, 0], [1, 1], [0, 1], [6, 0]], np.int32)
+    got = orc.forward(case, pairs=pairs)
+    assert np.array_equal(got, orc.forward(case)[pairs[:, 0], pairs[:, 1]]), case.name
+    err = np.max(np.abs(got - sdpa_reference(case)[pairs[:, 0], pairs[:, 1]]))
+    assert err <= 1e-12, f"pairs_tall: max err {err}"
+    # out-of-range pairs are refused
+    assert orc.run(pairs=np.array([[case.num_tokens, 0]], np.int32), **oracle_fields(case))[0] != 0
+    assert orc.run(pairs=np.array([[0, case.num_q_heads]], np.int32), **oracle_fields(case))[0] != 0
+
+
+def oracle_fields(case):
+    import oracle
+    return oracle.case_fields(case)
+
+
 ALL_PINS = {
     "sdpa": pin_sdpa, "hand": pin_hand, "closed": pin_closed, "rows": pin_rows,
     "permutation": pin_permutation, "window": pin_window, "gqa": pin_gqa, "u8": pin_u8,
-    "ragged": pin_ragged, "tree": pin_tree, "append": pin_append,
+    "ragged": pin_ragged, "tree": pin_tree, "append": pin_append, "pairs": pin_pairs,
 }

@@ -62,10 +62,17 @@ MUTANTS = [
                               "const size_t q_off = ((size_t)h * a->num_tokens + n) * D;")]),
     ("k_dims_reversed", [("page + k_offset(slot, d, D, u8, bs), row);",
                           "page + k_offset(slot, D - 1 - d, D, u8, bs), row);")]),
+    # the subset form (rows given as (token, q head) pairs); the indices are
+    # reduced into range so the mistake stays in bounds
+    ("pairs_token_head_swapped", [("n = a->pairs[2 * it];\n      h = a->pairs[2 * it + 1];",
+                                   "n = a->pairs[2 * it + 1] % a->num_tokens;\n"
+                                   "      h = a->pairs[2 * it] % a->num_q_heads;")]),
+    ("pairs_first_item_only", [("n = a->pairs[2 * it];\n      h = a->pairs[2 * it + 1];",
+                                "n = a->pairs[0];\n      h = a->pairs[1];")]),
 ]
 
 PIN_ORDER = ["hand", "closed", "rows", "window", "gqa", "u8", "permutation", "ragged", "sdpa", "tree",
-             "append"]
+             "append", "pairs"]
 
 
 def _source():

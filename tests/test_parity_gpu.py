@@ -10,7 +10,8 @@ import pytest
 
 import oracle
 import pa_inputs as pi
-from gpu_util import (excess, max_err, run_gpu, sample_pairs, to_f64, tol)
+from gpu_util import (excess, max_err, run_gpu, to_f64, tol)
+from gpu_util import half_ulp as gpu_half_ulp
 
 pytestmark = pytest.mark.gpu
 
@@ -28,18 +29,6 @@ def _full(case, rounding_aware=False, **kw):
     else:
         assert err <= tol(case), f"{case.name}: max err {err}"
     return got, ref
-
-
-def _sampled(case, n=96, **kw):
-    pairs = sample_pairs(case, n)
-    ref = oracle.forward(case, pairs=pairs)
-    got = to_f64(run_gpu(case, **kw))
-    g = got[pairs[:, 0], pairs[:, 1]]
-    err = float(np.max(np.abs(g - ref)))
-    print(f"{case.name}: max err over {len(pairs)} sampled rows {err:.3e}", flush=True)
-    assert np.all(np.isfinite(got)), case.name
-    assert err <= tol(case), f"{case.name}: max err {err}"
-    return got
 
 
 def test_tiny():
@@ -87,41 +76,87 @@ def test_u8_small_shapes():
 
 
 def test_ragged_batch():
-    _sampled(pi.config5(poison=True), n=160)
+    _full(pi.config5(poison=True))
 
 
 def test_max_context():
     case = pi.build_case([9, 131068, 4], [131068], [4], num_q_heads=32, num_kv_heads=8,
                          head_dim=128, block_size=16, q_dtype=pi.BF16, kv_dtype=pi.BF16,
                          name="ctx131072_T4")
-    _sampled(case, n=48)
+    _full(case)
 
 
-def test_contexts_where_the_block_id_table_sets_the_segment_count():
+def _peaked_cases():
+    """Each workload with its softmax peaked on a staircase of keys late in the
+    context (pa_inputs.peaked): the running max jumps by about 10 log2 units
+    at every stair, past the kernel's lazy-rescale margin, in later steps of a
+    wavefront's scan, and segment maxima differ by up to ~130 log2 units.
+    Builders, so a test makes only its own case."""
+    return [lambda: pi.peaked(pi.config2(32768, 3), [1]),
+            lambda: pi.peaked(pi.config2(32768, 1), [1]),
+            lambda: pi.peaked(pi.config3(32768, 3, poison=True), [2]),
+            lambda: pi.peaked(pi.config4(32768, window=0), [3]),
+            lambda: pi.peaked(pi.config4(32768, window=1024, poison=True), [4]),
+            lambda: pi.peaked(pi.config5(poison=True), [5]),
+            # gaps of 6 natural units (8.7 log2, just past the margin) with the
+            # top stair low enough that the ~32k background keys still weigh
+            # in at the 1e-3 level
+            lambda: pi.peaked(pi.config2(32768, 4, tree=True), [6], stairs=3, gap=6.0, base=0.0),
+            lambda: pi.peaked(pi.config3(8192, 4), [7], stairs=3, gap=6.0, base=0.0),
+            lambda: pi.peaked(pi.config2(8192, 3, block_size=1), [8]),
+            lambda: pi.peaked(pi.build_case([11, 8000], [8000], [16], num_q_heads=16,
+                                            num_kv_heads=4, head_dim=64, block_size=32,
+                                            q_dtype=pi.BF16, kv_dtype=pi.BF16,
+                                            name="wide_d64_T16"), [9])]
+
+
+@pytest.mark.parametrize("k", range(10))
+def test_peaked_softmax(k):
+    """Outputs are dominated by one or two keys (|out| up to ~4), so the bar
+    adds half an ulp of the output dtype at the reference value."""
+    case = _peaked_cases()[k]()
+    got, ref = _full(case, rounding_aware=True)
+    if k < 2:
+        # a single segment (no combine merge: every jump meets the in-scan
+        # rescale) and one segment per step
+        for S in (1, 10 ** 6):
+            g2 = to_f64(run_gpu(case, num_segments=S))
+            assert excess(case, g2, ref) <= 0.0, (case.name, S, max_err(g2, ref))
+
+
+_TABLE_BOUND_CASES = {
+    "ctx600k_bs16_T2": lambda: pi.build_case([9, 600000, 2], [600000], [2], num_q_heads=8,
+                                             num_kv_heads=8, head_dim=128, block_size=16,
+                                             name="ctx600k_bs16_T2"),
+    "ctx140k_bs2_T3": lambda: pi.build_case([9, 140000, 3], [140000], [3], num_q_heads=16,
+                                            num_kv_heads=8, head_dim=64, block_size=2,
+                                            q_dtype=pi.BF16, kv_dtype=pi.BF16,
+                                            name="ctx140k_bs2_T3"),
+    "ctx131072_bs1_T3": lambda: pi.build_case([9, 131069, 3], [131069], [3], num_q_heads=32,
+                                              num_kv_heads=8, head_dim=64, block_size=1,
+                                              name="ctx131072_bs1_T3"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_TABLE_BOUND_CASES))
+def test_contexts_where_the_block_id_table_sets_the_segment_count(name):
     """Contexts long enough that a segment's block ids, not the CU count, set
     the number of segments, so segments fill the LDS block-id table almost to
     its end: 600k keys on 16-slot pages, 140k on 2-slot and 131k on 1-slot
     pages (one block id per key), 8 KV heads each."""
     import speculative_decoding_verify_paged_amd as pav
-    cases = [pi.build_case([9, 600000, 2], [600000], [2], num_q_heads=8, num_kv_heads=8,
-                           head_dim=128, block_size=16, name="ctx600k_bs16_T2"),
-             pi.build_case([9, 140000, 3], [140000], [3], num_q_heads=16, num_kv_heads=8,
-                           head_dim=64, block_size=2, q_dtype=pi.BF16, kv_dtype=pi.BF16,
-                           name="ctx140k_bs2_T3"),
-             pi.build_case([9, 131069, 3], [131069], [3], num_q_heads=32, num_kv_heads=8,
-                           head_dim=64, block_size=1, name="ctx131072_bs1_T3")]
-    for case in cases:
-        p = pav.make_params(num_seqs=1, num_tokens=case.num_tokens,
-                            num_q_heads=case.num_q_heads, num_kv_heads=case.num_kv_heads,
-                            head_dim=case.head_dim, block_size=case.block_size,
-                            num_blocks=case.num_blocks, max_blocks_per_seq=case.max_blocks_per_seq,
-                            q_dtype=case.q_dtype, kv_dtype=case.kv_dtype)
-        plan = pav.pa_verify_make_plan(p, case.max_context_len, 256)
-        table_steps = plan["max_steps_per_segment"]                # steps whose ids fit the table
-        need = -(-plan["num_steps"] // table_steps)
-        print(case.name, plan["num_segments"], need, flush=True)
-        assert plan["num_segments"] == need and plan["steps_per_segment"] <= table_steps, plan
-        _sampled(case, n=24)
+    case = _TABLE_BOUND_CASES[name]()
+    p = pav.make_params(num_seqs=1, num_tokens=case.num_tokens,
+                        num_q_heads=case.num_q_heads, num_kv_heads=case.num_kv_heads,
+                        head_dim=case.head_dim, block_size=case.block_size,
+                        num_blocks=case.num_blocks, max_blocks_per_seq=case.max_blocks_per_seq,
+                        q_dtype=case.q_dtype, kv_dtype=case.kv_dtype)
+    plan = pav.pa_verify_make_plan(p, case.max_context_len, 256)
+    table_steps = plan["max_steps_per_segment"]                    # steps whose ids fit the table
+    need = -(-plan["num_steps"] // table_steps)
+    print(case.name, plan["num_segments"], need, flush=True)
+    assert plan["num_segments"] == need and plan["steps_per_segment"] <= table_steps, plan
+    _full(case)
 
 
 def _small_cases():
@@ -304,6 +339,69 @@ def test_cached_workspace_growth_keeps_a_pending_status():
     got = to_f64(run_gpu(base))
     assert pav.pa_verify_read_status() == pav.PA_OK
     assert np.max(np.abs(got - ref)) <= 2e-3
+
+
+def test_graph_captured_before_a_workspace_growth_stays_valid():
+    """A graph captured on the cached workspace keeps its pointer; growing
+    the cache afterwards must not free that buffer.  Replays after the growth
+    match the eager result, and tensors allocated after the growth (same
+    size as the old buffer, where a freed block would be handed out again)
+    are never written by the replays."""
+    import torch
+    from gpu_util import to_device
+    import speculative_decoding_verify_paged_amd as pav
+    case = pi.config2(2048, 3, rep=9)
+    d = to_device(case)
+    out = torch.empty_like(d["q"])
+    run_gpu(case, dev=d, out=out)
+    eager = to_f64(out)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_gpu(case, dev=d, out=out, sync=False,
+                stream=torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    dev = torch.device("cuda", torch.cuda.current_device())
+    old = pav.workspace(0, dev)
+    n_old = old.numel()
+    del old
+    new = pav.workspace(n_old + 1, dev)
+    assert new.numel() >= 2 * n_old
+    sentinels = [torch.full((n_old,), 0x5A, dtype=torch.uint8, device=dev) for _ in range(3)]
+    big = pi.config5(rep=9, lo=1000, hi=40000)
+    want_big = oracle.forward(big)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_f64(out), eager), rep
+        assert all(bool(torch.all(x == 0x5A)) for x in sentinels), rep
+        assert max_err(run_gpu(big), want_big) <= tol(big), rep      # eager, new buffer
+    assert pav.pa_verify_read_status() == pav.PA_OK
+
+
+def test_caller_workspace_is_checked():
+    """A workspace= tensor that is on the host, of another dtype or not
+    contiguous is refused before anything runs."""
+    import torch
+    from gpu_util import to_device
+    import speculative_decoding_verify_paged_amd as pav
+    case = pi.config2(1024, 2)
+    d = to_device(case)
+    bad = [torch.zeros(1 << 22, dtype=torch.uint8),                      # host memory
+           torch.zeros(1 << 20, dtype=torch.int32, device="cuda"),         # not bytes
+           torch.zeros((1 << 22) * 2, dtype=torch.uint8, device="cuda")[::2]]   # strided
+    for ws in bad:
+        with pytest.raises(ValueError):
+            pav.pa_verify_forward(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                  d["past_lens"], d["subsequence_begins"], case.max_context_len,
+                                  case.scale, workspace=ws)
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device="cuda")
+    got = pav.pa_verify_forward(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                d["past_lens"], d["subsequence_begins"], case.max_context_len,
+                                case.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert max_err(got, oracle.forward(case)) <= tol(case)
 
 
 def test_graph_capture_replays_match_eager():
@@ -615,7 +713,7 @@ def test_small_pages_all_instances():
 
 @pytest.mark.parametrize("bs", [1, 4, 8])
 def test_small_pages_32k(bs):
-    _sampled(pi.config2(32768, 3, block_size=bs), n=64)
+    _full(pi.config2(32768, 3, block_size=bs))
 
 
 def test_small_pages_ragged_tree_u8():
@@ -680,3 +778,72 @@ def test_random_feature_combinations():
                              name=f"combo{k}_D{D}_kv{kv}_q{qd}_bs{bs}_G{G}_H{Hkv}_T{Ts}_W{W}"
                                   f"_S{S}" + ("_tree" if tree else ""))
         _full(case, rounding_aware=True, num_segments=S)
+
+
+# ---------------------------------------------------------------------------
+# u8 cache with an f16 q: the V-scale bound of the f16 weight products
+# ---------------------------------------------------------------------------
+def _u8_ramp_case(v_scale, seed):
+    """A u8 head_dim-256 cache whose logits climb linearly by ~7.9 log2 units
+    from the first key to the last (every q row is sqrt(D) * u_g plus noise,
+    key t is (7.9 / log2 e) * t / L * u_g), so within one scan the softmax
+    weights against the first step's maximum grow to nearly 2^8, just short of
+    the kernel's rescale margin; V codes are random with every V scale
+    `v_scale` and zero point 127.5 (values up to +-127.5 * v_scale)."""
+    case = pi.build_case([960, seed], [4096], [3], num_q_heads=16, num_kv_heads=4,
+                         head_dim=256, block_size=16, q_dtype=pi.F16, kv_dtype=pi.U8,
+                         spare_blocks=1, name=f"u8_ramp_vs{v_scale}")
+    rng = np.random.default_rng([961, seed])
+    D, Hkv, bs = 256, 4, 16
+    u = rng.standard_normal((Hkv, D))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    G = case.num_q_heads // Hkv
+    qf = np.sqrt(D) * np.repeat(u, G, axis=0)[None] + rng.standard_normal((case.num_tokens, 16, D))
+    case.q = pi.f32_to_bits(qf.astype(np.float32), pi.F16)
+    kl, vl = case.logical_pages()
+    ksz, vsz = case.k_scale_zp.copy(), case.v_scale_zp.copy()
+    L = int(case.past_lens[0]) + case.Ts[0]
+    for t in range(L):
+        blk, slot = case.block_tables[0, t // bs], t % bs
+        c = (7.9 / np.log2(np.e)) * t / L
+        codes, s16, z16 = pi.quantize_u8((c * u).astype(np.float32))
+        kl[blk, :, slot] = codes
+        ksz[blk, :, slot, 0], ksz[blk, :, slot, 1] = s16, z16
+    vl = rng.integers(0, 256, size=vl.shape).astype(np.uint8)
+    vsz[..., 0] = pi.f32_to_f16_bits(np.float32(v_scale))
+    vsz[..., 1] = pi.f32_to_f16_bits(np.float32(127.5))
+    case.k_cache = pi.tile_k(kl, True).reshape(case.k_cache.shape)
+    case.v_cache = pi.tile_v(vl, True).reshape(case.v_cache.shape)
+    case.k_scale_zp, case.v_scale_zp = ksz, vsz
+    return case
+
+
+def test_u8_f16q_largest_v_scale():
+    """V scale 255.875, the largest the f16-q path admits: the exact result,
+    to the u8 bar relative to the largest |v| (values reach +-32623; the bar
+    of the N(0,1) workloads scales with the data) plus half an ulp of the f16
+    output, with one segment (weights near 2^8 in one scan) and the planner's."""
+    import speculative_decoding_verify_paged_amd as pav
+    case = _u8_ramp_case(255.875, 0)
+    ref = oracle.forward(case)
+    vmax = 127.5 * 255.875
+    assert pav.pa_verify_read_status() in (pav.PA_OK, pav.PA_ERR_DEVICE_CONTRACT)
+    for S in (1, 0):
+        got = to_f64(run_gpu(case, num_segments=S))
+        assert pav.pa_verify_read_status() == pav.PA_OK, S
+        err = np.abs(got - ref) - (tol(case) * vmax + gpu_half_ulp(ref, pi.F16))
+        print(f"S={S}: max err {max_err(got, ref):.3e} (|ref| <= {np.abs(ref).max():.1f})", flush=True)
+        assert np.all(np.isfinite(got)) and float(err.max()) <= 0.0, S
+
+
+def test_u8_f16q_v_scale_overflow_is_loud():
+    """V scale 1023.5, beyond the bound: the f16 products of weights near 2^8
+    overflow, and every affected row comes back NaN with the status word set,
+    never a wrong finite value."""
+    import speculative_decoding_verify_paged_amd as pav
+    case = _u8_ramp_case(1023.5, 1)
+    assert pav.pa_verify_read_status() in (pav.PA_OK, pav.PA_ERR_DEVICE_CONTRACT)
+    got = to_f64(run_gpu(case, num_segments=1))
+    assert pav.pa_verify_read_status() == pav.PA_ERR_DEVICE_CONTRACT
+    assert np.all(np.isnan(got))
+    assert pav.pa_verify_read_status() == pav.PA_OK
