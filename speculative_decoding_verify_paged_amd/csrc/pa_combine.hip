@@ -5,23 +5,32 @@
 namespace pav {
 
 // ---------------------------------------------------------------------------
-// Combine kernel: one workgroup per (token, q head) (placed by CombineArgs::xcds
-// on the XCD that wrote the pair's partials), NT threads with NT sized
-// by the host so all S partials are loaded in one batch of K per thread.  Thread t owns d columns
-// [c4, c4 + 4) of the segments sub, sub + NSUB, ...; it merges them with the
-// same online rescaling as the segment kernel (every load independent of the
-// previous iteration's arithmetic, so they all go out at once), then the
-// NSUB partial states are merged through LDS in a fixed order.
+// Combine kernel: one workgroup per (token, q head) row, placed by
+// CombineArgs::xcds on the XCD that wrote the row's partials; one wavefront
+// for head_dim <= 128, two for 256, each lane owning D / threads columns.
+// Every segment's (m, l) and every lane's columns of every segment's O go
+// out as one batch of independent loads (64 segments per batch); the row
+// max and the weighted sum of l are wavefront reductions, and each
+// segment's weight reaches all lanes by readlane, so the merge is one
+// dependent round trip to memory with no LDS and no barrier.
 // ---------------------------------------------------------------------------
+constexpr int kCombineBatch = 64;                             // segments per batch: one per lane
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
 template <int D, int OUT, int NT>
 __global__ __launch_bounds__(NT) void pa_combine(CombineArgs a) {
-  constexpr int LPS = D / 4;                                  // threads per segment row
-  constexpr int NSUB = NT / LPS;                              // segment rows in flight
-  constexpr int K = 8;                                        // partials per thread per batch
-  __shared__ float s_m[NSUB];
-  __shared__ float s_den[NSUB];
-  __shared__ __attribute__((aligned(16))) f32x4 s_acc[NSUB][LPS];
-
+  constexpr int CPL = D / NT;                                 // columns per lane
+  static_assert(CPL >= 1 && CPL <= 2 && NT % kWave == 0, "one or two columns per lane");
   int pair = blockIdx.x;                                      // token * Hq + q head
   if (a.xcds > 0) {
     // the pairs of KV heads x, x + xcds, ... in (token, KV head, group) order
@@ -30,10 +39,8 @@ __global__ __launch_bounds__(NT) void pa_combine(CombineArgs a) {
     const int g = k % G, t = k / G;
     pair = (t / HX) * a.Hq + ((t % HX) * X + x) * G + g;
   }
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int sub = tid / LPS;
-  const int col = tid % LPS;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int col = threadIdx.x * CPL;
   const int n = pair / a.Hq;
   const int S = a.seg.S;
 
@@ -43,39 +50,62 @@ __global__ __launch_bounds__(NT) void pa_combine(CombineArgs a) {
   const int sb_next = lane < nseq ? a.seg.sb[lane + 1] : 0;
   const int sb_this = lane < nseq ? a.seg.sb[lane] : 0;
 
-  // Every segment of a valid sequence wrote its partial (empty ones as
-  // (-inf, 0)), so these loads depend on nothing but the grid position.  They
-  // are unconditional (clamped index) so they all go out together.
+  // Every segment of a valid sequence wrote its (m, l) (empty ones as
+  // (-inf, 0)); a segment in which the row saw no key left its O unwritten,
+  // so its O is never read into the sum.  The loads depend on nothing but
+  // the grid position and go out together.
   const float* ml = a.seg.ws_ml + (size_t)pair * S * 2;
-  const float* op = a.seg.ws_o + (size_t)pair * S * D + col * 4;
-  float m = -INFINITY, den = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const float* op = a.seg.ws_o + (size_t)pair * S * D + col;
+  float M = -INFINITY, den = 0.f;
+  float acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
   bool nan_seen = false;
-  for (int b = 0; b < S; b += NSUB * K) {
-    float mj[K], lj[K];
-    f32x4 oj[K];
+  // one batch of up to NB segments starting at b (NB: the smallest of 8, 16,
+  // 32, 64 that holds the rest, so no more loads than needed go out)
+  auto batch = [&](auto nb_tag, int b) {
+    constexpr int NB = decltype(nb_tag)::value;
+    const int nb = min(NB, S - b);
+    const int j = b + (lane < nb ? lane : 0);
+    float2 mlj = *reinterpret_cast<const float2*>(ml + (size_t)j * 2);
+    float o[NB][CPL];
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int jj = b + sub + k * NSUB;
-      const int jc = jj < S ? jj : 0;
-      mj[k] = ml[jc * 2];
-      lj[k] = ml[jc * 2 + 1];
-      oj[k] = *reinterpret_cast<const f32x4*>(op + (size_t)jc * D);
-      mj[k] = jj < S ? mj[k] : -INFINITY;
+    for (int k = 0; k < NB; ++k) {
+      const size_t jc = (size_t)(b + (k < nb ? k : 0));      // in bounds; unused when k >= nb
+      if constexpr (CPL == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(op + jc * D);
+        o[k][0] = v.x;
+        o[k][1] = v.y;
+      } else {
+        o[k][0] = op[jc * D];
+      }
     }
+    if (lane >= nb) mlj = float2{-INFINITY, 0.f};
+    nan_seen |= mlj.x != mlj.x;
+    const float m_new = fmaxf(M, wave_max(mlj.x));
+    const float base = m_new == -INFINITY ? 0.f : m_new;
+    const float sc = __builtin_amdgcn_exp2f(M - base);
+    // weight of this lane's segment; 0 for an empty one (its O is unwritten)
+    const float w = mlj.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mlj.x - base);
+    den = den * sc + wave_sum(w * mlj.y);
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      nan_seen |= mj[k] != mj[k];
-      const float m_new = fmaxf(m, mj[k]);
-      const float base = m_new == -INFINITY ? 0.f : m_new;
-      const float sc = __builtin_amdgcn_exp2f(m - base);
-      const float f = __builtin_amdgcn_exp2f(mj[k] - base);
-      // a segment in which this row saw no key left its O slot unwritten
-      const f32x4 o = mj[k] == -INFINITY ? f32x4{0.f, 0.f, 0.f, 0.f} : oj[k];
-      den = den * sc + f * lj[k];
-      acc = acc * sc + f * o;
-      m = m_new;
+    for (int c = 0; c < CPL; ++c) acc[c] *= sc;
+    M = m_new;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
+      if (wk != 0.f) {                                        // uniform; skips empty segments
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[c] += wk * o[k][c];
+      }
     }
+  };
+  for (int b = 0; b < S; b += kCombineBatch) {
+    const int rest = S - b;
+    if (rest <= 8) batch(std::integral_constant<int, 8>{}, b);
+    else if (rest <= 16) batch(std::integral_constant<int, 16>{}, b);
+    else if (rest <= 32) batch(std::integral_constant<int, 32>{}, b);
+    else batch(std::integral_constant<int, kCombineBatch>{}, b);
   }
 
   // subsequence_begins must start at 0, never decrease and end at
@@ -100,64 +130,37 @@ __global__ __launch_bounds__(NT) void pa_combine(CombineArgs a) {
     if (s < 0 && hit) s = b + __builtin_ctzll(hit);
   }
   ok &= s >= 0;
-  if (col == 0) {
-    s_m[sub] = m;
-    s_den[sub] = den;
-  }
-  s_acc[sub][col] = acc;
-  const bool bad = __syncthreads_or(nan_seen || !ok);
-  if (bad && tid == 0) atomicExch(a.seg.status, kDeviceContract);
-  if (tid >= LPS) return;
-  float M = -INFINITY;
+  const bool bad = __any(nan_seen) || !ok;
+  if (bad && threadIdx.x == 0) atomicExch(a.seg.status, kDeviceContract);
+  float res[CPL];
 #pragma unroll
-  for (int k = 0; k < NSUB; ++k) M = fmaxf(M, s_m[k]);
-  f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  float dsum = 0.f;
-#pragma unroll
-  for (int k = 0; k < NSUB; ++k) {
-    const float f = s_m[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[k] - M);
-    num += f * s_acc[k][tid];
-    dsum += f * s_den[k];
-  }
-  float res[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) res[k] = bad ? NAN : num[k] / dsum;
+  for (int c = 0; c < CPL; ++c) res[c] = bad ? NAN : acc[c] / den;
   if constexpr (OUT == kF16) {
-    _Float16* out = reinterpret_cast<_Float16*>(a.out) + (size_t)pair * D + tid * 4;
+    _Float16* out = reinterpret_cast<_Float16*>(a.out) + (size_t)pair * D + col;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) out[k] = (_Float16)res[k];
+    for (int c = 0; c < CPL; ++c) out[c] = (_Float16)res[c];
   } else {
-    __bf16* out = reinterpret_cast<__bf16*>(a.out) + (size_t)pair * D + tid * 4;
+    __bf16* out = reinterpret_cast<__bf16*>(a.out) + (size_t)pair * D + col;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) out[k] = (__bf16)res[k];
+    for (int c = 0; c < CPL; ++c) out[c] = (__bf16)res[c];
   }
 }
 
-
-template <int D, int NT>
-static hipError_t launch_combine_nt(const CombineArgs& a, int out_dtype, dim3 grid, hipStream_t st) {
+template <int D>
+static hipError_t launch_combine_d(const CombineArgs& a, int out_dtype, dim3 grid, hipStream_t st) {
+  constexpr int NT = D >= 256 ? 128 : 64;
   const void* fn = out_dtype == kF16 ? reinterpret_cast<const void*>(pa_combine<D, kF16, NT>)
                                      : reinterpret_cast<const void*>(pa_combine<D, kBF16, NT>);
   return launch_kernel(fn, grid, dim3(NT), st, a);
 }
 
-template <int D>
-static hipError_t launch_combine_d(const CombineArgs& a, int out_dtype, int threads, dim3 grid,
-                                   hipStream_t st) {
-  switch (threads) {
-    case 256: return launch_combine_nt<D, 256>(a, out_dtype, grid, st);
-    case 512: return launch_combine_nt<D, 512>(a, out_dtype, grid, st);
-    case 1024: return launch_combine_nt<D, 1024>(a, out_dtype, grid, st);
-  }
-  return hipErrorInvalidValue;
-}
-
 hipError_t launch_combine(const CombineArgs& a, int out_dtype, int D, int threads, dim3 grid,
                           hipStream_t st) {
+  if (threads != combine_threads(D)) return hipErrorInvalidValue;
   switch (D) {
-    case 64: return launch_combine_d<64>(a, out_dtype, threads, grid, st);
-    case 128: return launch_combine_d<128>(a, out_dtype, threads, grid, st);
-    case 256: return launch_combine_d<256>(a, out_dtype, threads, grid, st);
+    case 64: return launch_combine_d<64>(a, out_dtype, grid, st);
+    case 128: return launch_combine_d<128>(a, out_dtype, grid, st);
+    case 256: return launch_combine_d<256>(a, out_dtype, grid, st);
   }
   return hipErrorInvalidValue;
 }

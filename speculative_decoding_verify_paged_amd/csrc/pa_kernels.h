@@ -85,11 +85,9 @@ hipError_t launch_append(const AppendArgs& a, int q_dtype, int kv_dtype, int D, 
 // the seg_block_slots(bs)-entry LDS table.
 constexpr int max_steps_per_segment(int bs) { return (seg_block_slots(bs) - 2) * bs / kKeysPerStep; }
 
-// Combine workgroup size: enough threads that each loads at most 8 of the S
-// partials of its (token, q head) row (one batch of loads), 256..1024.
-constexpr int combine_threads(int S, int D) {
-  return S * (D / 4) <= 256 * 8 ? 256 : S * (D / 4) <= 512 * 8 ? 512 : 1024;
-}
+// Combine workgroup size: one wavefront per (token, q head) row for head_dim
+// up to 128, two for 256 (at most two output columns per lane).
+constexpr int combine_threads(int D) { return D >= 256 ? 128 : 64; }
 
 // Per (cache dtype, head_dim, row blocks, block size): wavefronts per SIMD
 // the segment kernel is compiled for (its register budget, no spills; each

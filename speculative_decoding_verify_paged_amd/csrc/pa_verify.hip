@@ -141,7 +141,7 @@ int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_ve
   pl->combine_grid[0] = (int32_t)rows;
   pl->combine_grid[1] = 1;
   pl->combine_grid[2] = 1;
-  pl->combine_threads = pav::combine_threads((int)S, p->head_dim);
+  pl->combine_threads = pav::combine_threads(p->head_dim);
   const size_t ml_bytes = (size_t)rows * S * 2 * sizeof(float);
   const size_t o_bytes = (size_t)rows * S * p->head_dim * sizeof(float);
   pl->workspace_bytes = 256 + ((ml_bytes + 255) / 256) * 256 + o_bytes;
