@@ -203,6 +203,25 @@ int pa_verify_forward(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* subsequence_begins, int32_t max_context_len,
                       float scale, void* out, const pa_verify_params* p);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * pa_verify_forward with the same arguments, whose segment partials and
+ * status word live in a static device array of the library instead of a
+ * caller workspace (p->workspace and p->workspace_bytes are ignored).  The
+ * array holds 32 MiB on each GPU the library runs on, until the process
+ * ends; a call that needs more (pa_verify_workspace_bytes > 33554432)
+ * returns PA_ERR_WORKSPACE before anything is enqueued.  The call allocates
+ * nothing and enqueues the same two kernels.  All calls on one GPU share its
+ * array: calls that may overlap on one GPU (other streams, other threads)
+ * race and must be ordered by the caller.  The array's status word is never
+ * reported: a device-side contract violation shows as NaN in the affected
+ * rows of `out`.  The first call on each device resolves the array's address
+ * (no allocation); make it outside graph capture. */
+int pa_verify_forward_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* past_lens,
+                              const int32_t* subsequence_begins, int32_t max_context_len,
+                              float scale, void* out, const pa_verify_params* p);
+
 /* The same operation over a u8 KV cache (kv_dtype == PA_U8): a cached value u
  * of token t, KV head g stands for (u - zp) * scale with (scale, zp) read as
  * f16 from k_scale_zp / v_scale_zp[block, g, slot, 0..1].  Dequantisation

@@ -10,6 +10,7 @@ Functions keep the C names:
   pa_verify_forward(q, k_cache, v_cache, block_tables, past_lens,
                     subsequence_begins, max_context_len, scale, out=None, ...)
   pa_verify_forward_u8(q, k_cache, v_cache, k_scale_zp, v_scale_zp, ...)
+  pa_verify_forward_noalloc(q, ..., out, ...)  (static scratch, no workspace)
   pa_verify_workspace_bytes(...), pa_verify_make_plan(...),
   pa_verify_read_status(...), pa_verify_status_string(code)
 """
@@ -28,8 +29,10 @@ PA_F16, PA_BF16, PA_U8 = 0, 1, 2
 
 # every symbol include/pa_verify.h declares
 EXPORTS = ("pa_verify_make_plan", "pa_verify_workspace_bytes", "pa_verify_forward",
-           "pa_verify_forward_u8", "pa_kv_append", "pa_kv_append_u8", "pa_verify_read_status",
-           "pa_verify_status_string")
+           "pa_verify_forward_noalloc", "pa_verify_forward_u8", "pa_kv_append", "pa_kv_append_u8",
+           "pa_verify_read_status", "pa_verify_status_string")
+# bytes of the static device scratch pa_verify_forward_noalloc works in
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class PaVerifyParams(ctypes.Structure):
@@ -92,6 +95,9 @@ def lib():
                 L.pa_verify_workspace_bytes.restype = ctypes.c_size_t
                 L.pa_verify_forward.argtypes = [vp, vp, vp, vp, vp, vp, i32, ctypes.c_float, vp, P]
                 L.pa_verify_forward.restype = ctypes.c_int
+                L.pa_verify_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, ctypes.c_float,
+                                                        vp, P]
+                L.pa_verify_forward_noalloc.restype = ctypes.c_int
                 L.pa_verify_forward_u8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                                    ctypes.c_float, vp, P]
                 L.pa_verify_forward_u8.restype = ctypes.c_int
@@ -232,7 +238,8 @@ class PreparedCall:
 
 def _call(u8, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
           subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
-          ws, stream, prof_events, prepare=False, max_query_len=0, tree_mask=None):
+          ws, stream, prof_events, prepare=False, max_query_len=0, tree_mask=None,
+          noalloc=False):
     torch = _torch()
     dev = q.device
     _check(q, "q", ndim=3, device=dev)
@@ -277,17 +284,22 @@ def _call(u8, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_le
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     params.stream = stream or None
-    need = pa_verify_workspace_bytes(params, max_context_len)
-    if need == 0:
-        # let the library name the problem
-        need = 256
-    if ws is None:
-        with torch.cuda.device(dev):
-            ws = workspace(need, dev)
+    if noalloc:
+        if ws is not None:
+            raise ValueError("the no-allocation call works in the library's static scratch: "
+                             "pass no workspace")
     else:
-        _check(ws, "workspace", dtype=torch.uint8, ndim=1, device=dev)
-    params.workspace = ws.data_ptr()
-    params.workspace_bytes = ws.numel() * ws.element_size()
+        need = pa_verify_workspace_bytes(params, max_context_len)
+        if need == 0:
+            # let the library name the problem
+            need = 256
+        if ws is None:
+            with torch.cuda.device(dev):
+                ws = workspace(need, dev)
+        else:
+            _check(ws, "workspace", dtype=torch.uint8, ndim=1, device=dev)
+        params.workspace = ws.data_ptr()
+        params.workspace_bytes = ws.numel() * ws.element_size()
     if prof_events is not None:
         params.prof_event_begin = prof_events[0]
         params.prof_event_end = prof_events[1]
@@ -298,7 +310,7 @@ def _call(u8, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_le
                 v_scale_zp.data_ptr(), block_tables.data_ptr(), past_lens.data_ptr(),
                 subsequence_begins.data_ptr(), int(max_context_len), float(scale), out.data_ptr())
     else:
-        fn = L.pa_verify_forward
+        fn = L.pa_verify_forward_noalloc if noalloc else L.pa_verify_forward
         args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
                 past_lens.data_ptr(), subsequence_begins.data_ptr(), int(max_context_len),
                 float(scale), out.data_ptr())
@@ -333,6 +345,22 @@ def pa_verify_forward(q, k_cache, v_cache, block_tables, past_lens, subsequence_
     return _call(False, q, k_cache, v_cache, None, None, block_tables, past_lens,
                  subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
                  workspace, stream, prof_events, max_query_len=max_query_len, tree_mask=tree_mask)
+
+
+def pa_verify_forward_noalloc(q, k_cache, v_cache, block_tables, past_lens, subsequence_begins,
+                              max_context_len: int, scale: float, out, *, sliding_window: int = 0,
+                              num_segments: int = 0, stream: Optional[int] = None,
+                              max_query_len: int = 0, tree_mask=None):
+    """pa_verify_forward without any workspace: the library works in its static
+    device scratch (32 MiB per GPU), so nothing is allocated by the call or
+    here — ``out`` must be given.  Calls on one GPU share that scratch and
+    must not overlap; a contract violation shows only as NaN rows."""
+    if out is None:
+        raise ValueError("pass out: the no-allocation call allocates nothing")
+    return _call(False, q, k_cache, v_cache, None, None, block_tables, past_lens,
+                 subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
+                 None, stream, None, max_query_len=max_query_len, tree_mask=tree_mask,
+                 noalloc=True)
 
 
 def pa_verify_forward_u8(q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,

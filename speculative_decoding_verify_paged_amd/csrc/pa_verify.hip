@@ -203,9 +203,42 @@ void maybe_log(const pa_verify_params* p, const pa_verify_plan& pl, int32_t max_
                pl.combine_grid[0], pl.combine_threads, pl.workspace_bytes);
 }
 
+// The forward call.  Its partials and status word go to ws_base (ws_bytes):
+// the caller's workspace, or for the no-allocation entry point the static
+// scratch array, whose address is resolved only once the call is known to
+// fit (get_scratch).
+// ---------------------------------------------------------------------------
+// Static scratch for pa_verify_forward_noalloc: the status word and the
+// segment partials of one call, for callers that cannot allocate.  One copy
+// per GPU, held until the process ends.  In host code `scratch` only names
+// the symbol; its device address on the current device comes from
+// hipGetSymbolAddress, once per device, and only that address is ever passed
+// to a kernel.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];                  // device address per device, once resolved
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_HIP;
+  std::lock_guard<std::mutex> g(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PA_ERR_HIP;
+    scratch_ptr[dev] = ptr;
+  }
+  *out = scratch_ptr[dev];
+  return PA_OK;
+}
+
 int run(const void* q, const void* k, const void* v, const void* ksz, const void* vsz,
         const int32_t* bt, const int32_t* past_lens, const int32_t* sb, int32_t max_ctx,
-        float scale, void* out, const pa_verify_params* p, bool u8_entry) {
+        float scale, void* out, const pa_verify_params* p, bool u8_entry,
+        int (*get_scratch)(void**) = nullptr) {
   int rc = validate(p, max_ctx, u8_entry);
   if (rc) return rc;
   if (!q || !k || !v || !bt || !past_lens || !sb || !out) return PA_ERR_INVALID_ARG;
@@ -215,7 +248,7 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
       !aligned(bt, 4) || !aligned(past_lens, 4) || !aligned(sb, 4) || !aligned(p->tree_mask, 4))
     return PA_ERR_INVALID_ARG;
   if (u8_entry && (!aligned(ksz, 16) || !aligned(vsz, 16))) return PA_ERR_INVALID_ARG;
-  if (!aligned(p->workspace, 16)) return PA_ERR_WORKSPACE;
+  if (!get_scratch && !aligned(p->workspace, 16)) return PA_ERR_WORKSPACE;
   if (!(scale == scale)) return PA_ERR_INVALID_ARG;
   int cus = 0;
   rc = device_cus(&cus);
@@ -223,10 +256,17 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
   pa_verify_plan pl;
   rc = make_plan(p, max_ctx, cus, &pl);                      // grid limits
   if (rc) return rc;
-  if (!p->workspace || p->workspace_bytes < pl.workspace_bytes) return PA_ERR_WORKSPACE;
+  void* ws_base = p->workspace;
+  if (get_scratch) {
+    if (pl.workspace_bytes > kScratchBytes) return PA_ERR_WORKSPACE;
+    rc = get_scratch(&ws_base);
+    if (rc) return rc;
+  } else if (!p->workspace || p->workspace_bytes < pl.workspace_bytes) {
+    return PA_ERR_WORKSPACE;
+  }
   maybe_log(p, pl, max_ctx);
 
-  char* ws = static_cast<char*>(p->workspace);
+  char* ws = static_cast<char*>(ws_base);
   const size_t rows = (size_t)p->num_tokens * p->num_q_heads;
   const size_t ml_bytes = ((rows * pl.num_segments * 2 * sizeof(float) + 255) / 256) * 256;
   pav::SegmentArgs a;
@@ -364,6 +404,14 @@ int pa_verify_forward(const void* q, const void* k_cache, const void* v_cache,
                       void* out, const pa_verify_params* p) {
   return run(q, k_cache, v_cache, nullptr, nullptr, block_tables, past_lens, subsequence_begins,
              max_context_len, scale, out, p, false);
+}
+
+int pa_verify_forward_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* past_lens,
+                              const int32_t* subsequence_begins, int32_t max_context_len,
+                              float scale, void* out, const pa_verify_params* p) {
+  return run(q, k_cache, v_cache, nullptr, nullptr, block_tables, past_lens, subsequence_begins,
+             max_context_len, scale, out, p, false, scratch_address);
 }
 
 int pa_verify_forward_u8(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,

@@ -121,6 +121,31 @@ def test_null_pointers_and_entry_mismatch():
     assert call(params(), max_ctx=0) == pav.PA_ERR_INVALID_ARG
 
 
+def test_noalloc_host_errors():
+    """The no-allocation entry point runs the same host checks before it
+    touches a device.  (Every call here fails a check: with valid arguments
+    it would launch, and these pointers are fake.)"""
+    L = pav.lib()
+
+    def na(p, null=None, max_ctx=32771):
+        args = [FAKE] * 6
+        if null is not None:
+            args[null] = None
+        return L.pa_verify_forward_noalloc(*args, max_ctx, 0.1, FAKE, ctypes.byref(p))
+    for k in range(6):
+        assert na(params(), null=k) == pav.PA_ERR_INVALID_ARG
+    assert L.pa_verify_forward_noalloc(*[FAKE] * 6, 100, 0.1, None, ctypes.byref(params())) \
+        == pav.PA_ERR_INVALID_ARG
+    assert L.pa_verify_forward_noalloc(*[FAKE] * 6, 100, 0.1, FAKE, None) == pav.PA_ERR_INVALID_ARG
+    assert na(params(head_dim=96)) == pav.PA_ERR_UNSUPPORTED
+    assert na(params(kv_dtype=pav.PA_U8)) == pav.PA_ERR_UNSUPPORTED       # u8 cache: not this entry
+    assert na(params(), max_ctx=0) == pav.PA_ERR_INVALID_ARG
+    a = [FAKE] * 6
+    a[0] = FAKE + 8                                                       # q: 16 B
+    assert L.pa_verify_forward_noalloc(*a, 32771, 0.1, FAKE, ctypes.byref(params())) \
+        == pav.PA_ERR_INVALID_ARG
+
+
 def test_append_host_errors():
     L = pav.lib()
     ok = params(num_q_heads=8, workspace=FAKE, workspace_bytes=256)
