@@ -40,14 +40,7 @@ __device__ __forceinline__ float in_value(const uint16_t* p) {
   return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 
-__device__ __forceinline__ float wave_min(float v) {
-  for (int m = 1; m < kWave; m <<= 1) v = fminf(v, __shfl_xor(v, m, kWave));
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-  for (int m = 1; m < kWave; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  return v;
-}
+__device__ __forceinline__ float wave_min(float v) { return wave_reduce(v, fmin_op); }
 
 }  // namespace
 
@@ -68,8 +61,8 @@ __global__ __launch_bounds__(kWave) void pa_append(AppendArgs a) {
     const int nx = k < a.num_seqs ? a.sb[k + 1] : 0;
     const int th = k < a.num_seqs ? a.sb[k] : 0;
     ok &= !__any(k < a.num_seqs && th > nx);
-    if (b == 0) ok &= __shfl(th, 0, kWave) == 0;
-    if (b + kWave >= a.num_seqs) ok &= __shfl(nx, a.num_seqs - 1 - b, kWave) == a.num_tokens;
+    if (b == 0) ok &= __builtin_amdgcn_readlane(th, 0) == 0;
+    if (b + kWave >= a.num_seqs) ok &= __builtin_amdgcn_readlane(nx, a.num_seqs - 1 - b) == a.num_tokens;
     const unsigned long long hit = __ballot(k < a.num_seqs && n < nx);
     if (s < 0 && hit) s = b + __builtin_ctzll(hit);
   }

@@ -5,42 +5,38 @@
 namespace pav {
 
 // ---------------------------------------------------------------------------
-// Combine kernel: one workgroup per (token, q head) row, placed by
-// CombineArgs::xcds on the XCD that wrote the row's partials; one wavefront
-// for head_dim <= 128, two for 256, each lane owning D / threads columns.
-// Every segment's (m, l) and every lane's columns of every segment's O go
-// out as one batch of independent loads (64 segments per batch); the row
-// max and the weighted sum of l are wavefront reductions, and each
-// segment's weight reaches all lanes by readlane, so the merge is one
-// dependent round trip to memory with no LDS and no barrier.
+// Combine kernel: one wavefront per (token, q head) row and 64-column slice
+// of it, each lane owning one output column; the slices of a row are placed
+// by CombineArgs::xcds on the XCD that wrote the row's partials.  Every
+// segment's (m, l) and the slice's columns of every segment's O go out as
+// one batch of independent loads (up to 64 segments per batch); the row max
+// and the weighted sum of l are wavefront reductions, and each segment's
+// weight reaches all lanes by readlane, so the merge is one dependent round
+// trip to memory with no LDS and no barrier.  Slicing the row spreads its
+// partials over D / 64 workgroups (and CUs) instead of one.
 // ---------------------------------------------------------------------------
 constexpr int kCombineBatch = 64;                             // segments per batch: one per lane
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
-  return v;
-}
-
-template <int D, int OUT, int NT>
-__global__ __launch_bounds__(NT) void pa_combine(CombineArgs a) {
-  constexpr int CPL = D / NT;                                 // columns per lane
-  static_assert(CPL >= 1 && CPL <= 2 && NT % kWave == 0, "one or two columns per lane");
-  int pair = blockIdx.x;                                      // token * Hq + q head
+template <int D, int OUT>
+__global__ __launch_bounds__(kWave) void pa_combine(CombineArgs a) {
+  constexpr int CPL = 1;                                      // columns per lane
+  constexpr int NSL = D / kWave;                              // slices per row
+  int pair, slice;                                            // pair = token * Hq + q head
   if (a.xcds > 0) {
-    // the pairs of KV heads x, x + xcds, ... in (token, KV head, group) order
+    // the pairs of KV heads x, x + xcds, ... in (token, KV head, group) order,
+    // all slices of a pair on the same XCD
     const int X = a.xcds, x = (int)blockIdx.x % X, k = (int)blockIdx.x / X;
+    slice = k % NSL;
+    const int kk = k / NSL;
     const int G = a.seg.G, HX = a.seg.Hkv / X;
-    const int g = k % G, t = k / G;
+    const int g = kk % G, t = kk / G;
     pair = (t / HX) * a.Hq + ((t % HX) * X + x) * G + g;
+  } else {
+    pair = (int)blockIdx.x / NSL;
+    slice = (int)blockIdx.x % NSL;
   }
   const int lane = threadIdx.x & (kWave - 1);
-  const int col = threadIdx.x * CPL;
+  const int col = slice * kWave + lane;
   const int n = pair / a.Hq;
   const int S = a.seg.S;
 
@@ -115,8 +111,8 @@ __global__ __launch_bounds__(NT) void pa_combine(CombineArgs a) {
   int s = -1;
   {
     ok &= !__any(lane < nseq && sb_this > sb_next);
-    ok &= __shfl(sb_this, 0, kWave) == 0;
-    if (nseq <= kWave) ok &= __shfl(sb_next, nseq - 1, kWave) == a.seg.num_tokens;
+    ok &= __builtin_amdgcn_readlane(sb_this, 0) == 0;
+    if (nseq <= kWave) ok &= __builtin_amdgcn_readlane(sb_next, nseq - 1) == a.seg.num_tokens;
     const unsigned long long hit = __ballot(lane < nseq && n < sb_next);
     if (hit) s = __builtin_ctzll(hit);
   }
@@ -125,7 +121,7 @@ __global__ __launch_bounds__(NT) void pa_combine(CombineArgs a) {
     const int nx = k < nseq ? a.seg.sb[k + 1] : 0;
     const int th = k < nseq ? a.seg.sb[k] : 0;
     ok &= !__any(k < nseq && th > nx);
-    if (b + kWave >= nseq) ok &= __shfl(nx, nseq - 1 - b, kWave) == a.seg.num_tokens;
+    if (b + kWave >= nseq) ok &= __builtin_amdgcn_readlane(nx, nseq - 1 - b) == a.seg.num_tokens;
     const unsigned long long hit = __ballot(k < nseq && n < nx);
     if (s < 0 && hit) s = b + __builtin_ctzll(hit);
   }
@@ -148,15 +144,14 @@ __global__ __launch_bounds__(NT) void pa_combine(CombineArgs a) {
 
 template <int D>
 static hipError_t launch_combine_d(const CombineArgs& a, int out_dtype, dim3 grid, hipStream_t st) {
-  constexpr int NT = D >= 256 ? 128 : 64;
-  const void* fn = out_dtype == kF16 ? reinterpret_cast<const void*>(pa_combine<D, kF16, NT>)
-                                     : reinterpret_cast<const void*>(pa_combine<D, kBF16, NT>);
-  return launch_kernel(fn, grid, dim3(NT), st, a);
+  const void* fn = out_dtype == kF16 ? reinterpret_cast<const void*>(pa_combine<D, kF16>)
+                                     : reinterpret_cast<const void*>(pa_combine<D, kBF16>);
+  return launch_kernel(fn, grid, dim3(kWave), st, a);
 }
 
 hipError_t launch_combine(const CombineArgs& a, int out_dtype, int D, int threads, dim3 grid,
                           hipStream_t st) {
-  if (threads != combine_threads(D)) return hipErrorInvalidValue;
+  if (threads != kWave || grid.x % (D / kWave) != 0) return hipErrorInvalidValue;
   switch (D) {
     case 64: return launch_combine_d<64>(a, out_dtype, grid, st);
     case 128: return launch_combine_d<128>(a, out_dtype, grid, st);

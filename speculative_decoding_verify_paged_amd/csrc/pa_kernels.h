@@ -85,9 +85,9 @@ hipError_t launch_append(const AppendArgs& a, int q_dtype, int kv_dtype, int D, 
 // the seg_block_slots(bs)-entry LDS table.
 constexpr int max_steps_per_segment(int bs) { return (seg_block_slots(bs) - 2) * bs / kKeysPerStep; }
 
-// Combine workgroup size: one wavefront per (token, q head) row for head_dim
-// up to 128, two for 256 (at most two output columns per lane).
-constexpr int combine_threads(int D) { return D >= 256 ? 128 : 64; }
+// Combine grid: one 64-thread workgroup per (token, q head) row and 64-column
+// slice of it (same-box A/B, us per call: see the combine kernel).
+constexpr int combine_slices(int D) { return D / 64; }
 
 // Per (cache dtype, head_dim, row blocks, block size): wavefronts per SIMD
 // the segment kernel is compiled for (its register budget, no spills; each

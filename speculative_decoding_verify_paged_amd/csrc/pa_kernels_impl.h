@@ -168,8 +168,93 @@ __device__ __forceinline__ u32x2 u8x4_to_16(uint32_t w) {
 // compiler from moving LDS accesses across it.
 __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ float xor_max(float v, int m) {
-  return fmaxf(v, __shfl_xor(v, m, kWave));
+// ---------------------------------------------------------------------------
+// Cross-lane exchanges without LDS.  Each pairs every lane with one partner
+// (an involution), so a reduction built from them leaves the same bits in
+// every lane (a + b and b + a round alike).  DPP quad permutes and row
+// mirrors stay inside a 16-lane row; gfx950's permlane swaps cross rows.
+// v_permlane16_swap a, b exchanges a's odd rows with b's even rows, so with
+// a = b = x it leaves a = rows (0,0,2,2) and b = rows (1,1,3,3) of x;
+// v_permlane32_swap likewise leaves a = halves (0,0), b = (1,1).  Combining
+// a and b then pairs each lane with lane ^ 16 or lane ^ 32.  The swaps are
+// issued as inline asm on two tied registers: the compiler's builtins for
+// them fold the swap of two equal operands into a copy, which is wrong
+// across lanes.  The asm carries its own wait states (a VALU write of an
+// operand needs two before a permlane swap reads it).
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within 8
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within 16
+
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+template <typename F>
+__device__ __forceinline__ float pair16(float v, F op) {
+  uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
+  swap16(a, b);
+  return op(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+template <typename F>
+__device__ __forceinline__ float pair32(float v, F op) {
+  uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
+  swap32(a, b);
+  return op(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ float fmax_op(float a, float b) { return fmaxf(a, b); }
+__device__ __forceinline__ float fmin_op(float a, float b) { return fminf(a, b); }
+__device__ __forceinline__ float fadd_op(float a, float b) { return a + b; }
+
+// v combined with lane ^ 16, then lane ^ 32 (the four lane groups of a row)
+__device__ __forceinline__ float group_max(float v) {
+  return pair32(pair16(v, fmax_op), fmax_op);
+}
+__device__ __forceinline__ float group_sum(float v) {
+  return pair32(pair16(v, fadd_op), fadd_op);
+}
+
+// all 64 lanes
+template <typename F>
+__device__ __forceinline__ float wave_reduce(float v, F op) {
+  v = op(v, __builtin_bit_cast(float, dpp_u32<kDppXor1>(__builtin_bit_cast(uint32_t, v))));
+  v = op(v, __builtin_bit_cast(float, dpp_u32<kDppXor2>(__builtin_bit_cast(uint32_t, v))));
+  v = op(v, __builtin_bit_cast(float, dpp_u32<kDppHalfMirror>(__builtin_bit_cast(uint32_t, v))));
+  v = op(v, __builtin_bit_cast(float, dpp_u32<kDppMirror>(__builtin_bit_cast(uint32_t, v))));
+  return pair32(pair16(v, op), op);
+}
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, fmax_op); }
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, fadd_op); }
+
+// integer sum over all 64 lanes (exact, every lane gets it)
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  v += (int)dpp_u32<kDppXor1>((uint32_t)v);
+  v += (int)dpp_u32<kDppXor2>((uint32_t)v);
+  v += (int)dpp_u32<kDppHalfMirror>((uint32_t)v);
+  v += (int)dpp_u32<kDppMirror>((uint32_t)v);
+  uint32_t a = (uint32_t)v, b = a;
+  swap16(a, b);
+  a = b = a + b;
+  swap32(a, b);
+  return (int)(a + b);
+}
+__device__ __forceinline__ int wave_max_i32(int v) {
+  v = max(v, (int)dpp_u32<kDppXor1>((uint32_t)v));
+  v = max(v, (int)dpp_u32<kDppXor2>((uint32_t)v));
+  v = max(v, (int)dpp_u32<kDppHalfMirror>((uint32_t)v));
+  v = max(v, (int)dpp_u32<kDppMirror>((uint32_t)v));
+  uint32_t a = (uint32_t)v, b = a;
+  swap16(a, b);
+  a = b = (uint32_t)max((int)a, (int)b);
+  swap32(a, b);
+  return max((int)a, (int)b);
 }
 
 __device__ __forceinline__ float lo_f16(uint32_t w) {
@@ -252,8 +337,7 @@ __device__ __forceinline__ int wl_count(const SegmentArgs& a, int rows, int C, c
 #pragma unroll
   for (int p = 0; p < kWlCached; ++p) n += wl_items(w.code[p], C);
   for (int b = kWlCached * kWave; b < a.num_seqs; b += kWave) n += wl_items(wl_code(a, b + lane, rows), C);
-  for (int m = 1; m < kWave; m <<= 1) n += __shfl_xor(n, m, kWave);
-  return n;
+  return wave_sum_i32(n);
 }
 
 __device__ __forceinline__ int wl_chunk(const SegmentArgs& a, int rows, const WorkList& w) {
@@ -268,10 +352,15 @@ __device__ __forceinline__ int wl_chunk(const SegmentArgs& a, int rows, const Wo
 #pragma unroll
   for (int p = 0; p < kWlCached; ++p) add(w.code[p]);
   for (int b = kWlCached * kWave; b < a.num_seqs; b += kWave) add(wl_code(a, b + lane, rows));
-  for (int m = 1; m < kWave; m <<= 1) {
-    total += __shfl_xor(total, m, kWave);
-    longest = max(longest, __shfl_xor(longest, m, kWave));
+  // a lane's share of the total stays below 2^47 (at most 1024 sequences of
+  // at most 2^26 steps each): summed as 16-bit high and low parts, each of
+  // whose totals fits 32 bits
+  {
+    const int hi = wave_sum_i32((int)(total >> 16));
+    const int lo = wave_sum_i32((int)(total & 0xffff));
+    total = ((long long)hi << 16) + lo;
   }
+  longest = wave_max_i32(longest);
   const long long want = (total + a.target_items - 1) / a.target_items;
   int hi = max(1, min(longest, a.max_sps));               // a chunk's block ids fit LDS
   int lo = (int)min<long long>(max<long long>(a.steps_per_seg, want), hi);
@@ -508,19 +597,23 @@ void pa_segment(SegmentArgs a) {
   // d = c*32 + q4*8 + 0..7 (u8: chunk 2*c2 + half: d = c2*64 + q4*16 + half*8 + 0..7).
   u32x4 qreg[RB][QC];
   float qsum[RB];                                             // u8: sum of this lane's q values
+  // Issued after the wavefront's first K loads (not before the barrier that
+  // publishes the block ids), so the first KV request does not wait a memory
+  // round trip for q.
+  auto load_q = [&]() {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    qsum[rb] = 0.f;
-    const char* qp = reinterpret_cast<const char*>(a.q) + ((size_t)tok[rb] * a.Hq + qh[rb]) * D * 2;
+    for (int rb = 0; rb < RB; ++rb) {
+      qsum[rb] = 0.f;
+      const char* qp = reinterpret_cast<const char*>(a.q) + ((size_t)tok[rb] * a.Hq + qh[rb]) * D * 2;
 #pragma unroll
-    for (int c = 0; c < QC; ++c) {
-      const int d0 = U8 ? (c / 2) * 64 + q4 * 16 + (c % 2) * 8 : c * 32 + q4 * 8;
-      const u32x4 v = ld16(qp + d0 * 2);
-      qreg[rb][c] = row_ok[rb] ? v : u32x4{0, 0, 0, 0};
+      for (int c = 0; c < QC; ++c) {
+        const int d0 = U8 ? (c / 2) * 64 + q4 * 16 + (c % 2) * 8 : c * 32 + q4 * 8;
+        const u32x4 v = ld16(qp + d0 * 2);
+        qreg[rb][c] = row_ok[rb] ? v : u32x4{0, 0, 0, 0};
+      }
     }
-  }
-  // u8: the row sum of q, taken once the first KV loads are in flight so
-  // the Q loads' latency hides behind theirs.
+  };
+  // u8: the row sum of q, taken once the first KV loads are in flight.
   auto finish_q = [&]() {
     if constexpr (U8) {
 #pragma unroll
@@ -537,8 +630,7 @@ void pa_segment(SegmentArgs a) {
             }
           }
         }
-        qsum[rb] += __shfl_xor(qsum[rb], 16, kWave);
-        qsum[rb] += __shfl_xor(qsum[rb], 32, kWave);
+        qsum[rb] = group_sum(qsum[rb]);
       }
     }
   };
@@ -673,30 +765,45 @@ void pa_segment(SegmentArgs a) {
     }
   };
 
-  auto load_step = [&](int st, Step& r) {
-    if constexpr (BS < 16) {
-      load_step_small(st, r);
-      return;
-    }
-    const int key0 = si.base + st * kKeysPerStep;
+  // 16-slot pages: the K loads of both sub-tiles, then (between: the q rows
+  // on a wavefront's first step) the V and scale loads.
+  auto tile_of = [&](int st, int tau) {
+    const int t0 = si.base + st * kKeysPerStep + tau * 16;    // first key of the sub-tile
+    const bool present = t0 < si.ctx && t0 + 16 > si.lo0;
+    const int page = __builtin_amdgcn_readfirstlane(s_bt[present ? t0 / BS - blk_lo : 0]);
+    const int sub = present ? (t0 % BS) / 16 : 0;
+    return ((size_t)page * Hkv + h) * BS + (size_t)sub * 16;  // first slot row of the sub-tile
+  };
+  auto load_k = [&](int st, Step& r) {
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      const int t0 = key0 + tau * 16;                         // first key of the sub-tile
-      const bool present = t0 < si.ctx && t0 + 16 > si.lo0;
-      const int page = __builtin_amdgcn_readfirstlane(s_bt[present ? t0 / BS - blk_lo : 0]);
-      const int sub = present ? (t0 % BS) / 16 : 0;
-      const size_t tile = (((size_t)page * Hkv + h) * BS + (size_t)sub * 16) * D;   // elements
-      const char* kp = kb + tile * EB + lane * 16;
-      const char* vp = vb + tile * EB + lane * 16;
+      const char* kp = kb + tile_of(st, tau) * D * EB + lane * 16;
 #pragma unroll
       for (int c = 0; c < LK; ++c) r.k[tau][c] = ld16_stream(kp + c * 1024);
+    }
+  };
+  auto load_v = [&](int st, Step& r) {
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const size_t row0 = tile_of(st, tau);
+      const char* vp = vb + row0 * D * EB + lane * 16;
 #pragma unroll
       for (int c = 0; c < LV; ++c) r.v[tau][c] = ld16_stream(vp + c * 1024);
       if constexpr (U8) {
-        const size_t srow = (((size_t)page * Hkv + h) * BS + (size_t)sub * 16 + q4 * 4) * 4;
+        const size_t srow = (row0 + q4 * 4) * 4;
         r.ks[tau] = ld16_stream(kszb + srow);
         r.vs[tau] = ld16_stream(vszb + srow);
       }
+    }
+  };
+  auto load_step = [&](int st, Step& r, bool with_q) {
+    if constexpr (BS < 16) {
+      load_step_small(st, r);
+      if (with_q) load_q();
+    } else {
+      load_k(st, r);
+      if (with_q) load_q();
+      load_v(st, r);
     }
   };
 
@@ -880,8 +987,7 @@ void pa_segment(SegmentArgs a) {
       float mx = sv[rb][0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[rb][e]);
-      mx = xor_max(mx, 16);
-      mx = xor_max(mx, 32);
+      mx = group_max(mx);
       // Lazy rescaling: weights are taken relative to a reference max m_run
       // that only moves when a logit passes it by more than 2^kRescaleLog2,
       // so weights stay <= 256 and the O rescale runs in few steps.  The
@@ -982,11 +1088,11 @@ void pa_segment(SegmentArgs a) {
     Step ra;
     int st = st_begin + wave;
     if (st < st_end) {
-      load_step(st, ra);
+      load_step(st, ra, true);
       finish_q();
       compute_step(st, ra);
       for (st += NW; st < st_end; st += NW) {
-        load_step(st, ra);
+        load_step(st, ra, false);
         compute_step(st, ra);
       }
     }
@@ -997,12 +1103,10 @@ void pa_segment(SegmentArgs a) {
   // rescaled by 2^(m_w - M), in a fixed order (bitwise repeatable).
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    l_run[rb] += __shfl_xor(l_run[rb], 16, kWave);
-    l_run[rb] += __shfl_xor(l_run[rb], 32, kWave);
+    l_run[rb] = group_sum(l_run[rb]);
     const int r = rb * kRows + n16;
     if constexpr (U8) {
-      c_run[rb] += __shfl_xor(c_run[rb], 16, kWave);
-      c_run[rb] += __shfl_xor(c_run[rb], 32, kWave);
+      c_run[rb] = group_sum(c_run[rb]);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[rb][dt] -= c_run[rb];
       // f16 q: a weight (at most 2^kRescaleLog2 against the reference max)
@@ -1016,9 +1120,11 @@ void pa_segment(SegmentArgs a) {
       s_m[wave][r] = m_run[rb];
       s_l[wave][r] = l_run[rb];
     }
+    if (r < R) {                                              // padding rows are never read
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<f32x4*>(&s_o[wave][r][dt * 16 + q4 * 4]) = o[rb][dt];
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<f32x4*>(&s_o[wave][r][dt * 16 + q4 * 4]) = o[rb][dt];
+    }
   }
   __syncthreads();
 

@@ -67,6 +67,8 @@ int validate(const pa_verify_params* p, int32_t max_ctx, bool u8_entry) {
   // sizes that index 32-bit device arithmetic stay in range
   if ((int64_t)p->num_blocks * p->num_kv_heads * p->block_size > INT32_MAX) return PA_ERR_UNSUPPORTED;
   if ((int64_t)p->num_tokens * p->num_q_heads > INT32_MAX / 4) return PA_ERR_UNSUPPORTED;
+  // the combine launches one thread per output element
+  if ((int64_t)p->num_tokens * p->num_q_heads * p->head_dim > UINT32_MAX) return PA_ERR_UNSUPPORTED;
   if (p->num_seqs > 65535 || p->num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;   // grid y, x limits
   if (p->max_query_len < 0) return PA_ERR_INVALID_ARG;
   if (p->max_query_len > pav::kMaxT) return PA_ERR_UNSUPPORTED;
@@ -138,10 +140,10 @@ int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_ve
   }
   pl->block_threads = nw * 64;
   const int64_t rows = (int64_t)p->num_tokens * p->num_q_heads;
-  pl->combine_grid[0] = (int32_t)rows;
+  pl->combine_grid[0] = (int32_t)(rows * pav::combine_slices(p->head_dim));
   pl->combine_grid[1] = 1;
   pl->combine_grid[2] = 1;
-  pl->combine_threads = pav::combine_threads(p->head_dim);
+  pl->combine_threads = 64;
   const size_t ml_bytes = (size_t)rows * S * 2 * sizeof(float);
   const size_t o_bytes = (size_t)rows * S * p->head_dim * sizeof(float);
   pl->workspace_bytes = 256 + ((ml_bytes + 255) / 256) * 256 + o_bytes;
