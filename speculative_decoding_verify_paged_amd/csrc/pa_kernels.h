@@ -18,6 +18,10 @@ constexpr int kWavesPerGroup = 4;    // wavefronts per segment workgroup (defaul
 constexpr int seg_block_slots(int bs) { return bs == 1 ? 2080 : 1040; }
 constexpr int kDeviceContract = 5;   // value of PA_ERR_DEVICE_CONTRACT
 constexpr float kRescaleLog2 = 8.f;  // softmax reference max moves only past this margin
+#ifndef PA_HALF_RING_U8
+#define PA_HALF_RING_U8 2
+#endif
+constexpr int kHalfRingU8 = PA_HALF_RING_U8;   // register sets of the u8 head_dim-256 half-step path
 
 struct SegmentArgs {
   const void* q;
@@ -116,6 +120,7 @@ struct SegConfig {
   int waves_per_simd;
   int groups_per_cu;
   int waves_per_group = kWavesPerGroup;
+  int half_ring = 0;   // > 0: half-step path with this many register sets (16-slot pages)
 };
 constexpr SegConfig seg_config(int kv_dtype, int D, int rb, int bs = 16) {
   // Pages of fewer than 16 slots: one 8-wavefront workgroup per CU as for
@@ -124,7 +129,7 @@ constexpr SegConfig seg_config(int kv_dtype, int D, int rb, int bs = 16) {
   if (bs < 16) return D >= 256 ? SegConfig{1, 1} : SegConfig{2, 1, 8};
   if (rb > 1) return (rb == 2 && D <= 128) || D <= 64 ? SegConfig{2, 1, 8} : SegConfig{1, 1};
   if (kv_dtype == kU8)
-    return D >= 128 ? SegConfig{2, 1, 8} : SegConfig{4, 4};
+    return D >= 256 ? SegConfig{2, 1, 8, kHalfRingU8} : D >= 128 ? SegConfig{2, 1, 8} : SegConfig{4, 4};
   return D >= 256 ? SegConfig{1, 1} : D >= 128 ? SegConfig{2, 1, 8} : SegConfig{4, 2, 8};
 }
 constexpr int groups_per_cu(int kv_dtype, int D, int rb, int bs) {

@@ -118,6 +118,41 @@ __device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
   }
 }
 
+// 16x16x16: A and B hold 4 consecutive k values per lane (PV over the 16 keys
+// of one sub-tile in the half-step path).
+template <int QT>
+__device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
+  if constexpr (QT == kF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+  }
+}
+
+// The four softmax weights of a lane for one sub-tile (half-step path), as
+// pack_p below.
+template <int QT>
+__device__ __forceinline__ void pack_p4(const float (&p)[4], u32x2& hi, u32x2& lo) {
+  if constexpr (QT == kF16) {
+    f16x4 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = (_Float16)p[e];
+    hi = __builtin_bit_cast(u32x2, h);
+    lo = u32x2{0, 0};
+  } else {
+    bf16x4 h, l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h[e] = (__bf16)p[e];
+      l[e] = (__bf16)(p[e] - (float)h[e]);
+    }
+    hi = __builtin_bit_cast(u32x2, h);
+    lo = __builtin_bit_cast(u32x2, l);
+  }
+}
+
 // The eight softmax weights of a lane — keys 4*q4 + 0..3 of sub-tile 0, then
 // of sub-tile 1 — as the B operand of a 16x16x32 product.  f16: one
 // round-to-nearest per weight (at most 2^-11 relative).  bf16 keeps only 8
@@ -414,7 +449,7 @@ __device__ __forceinline__ int wl_find(const SegmentArgs& a, int rows, int C, in
 // blocks of stacked query rows (G * T <= 16 * RB): each K/V operand a step
 // loads (and, for u8, converts) feeds one MFMA per row block.
 // ---------------------------------------------------------------------------
-template <int QT, int KV, int D, int BS, int NW, int WPE, int RB>
+template <int QT, int KV, int D, int BS, int NW, int WPE, int RB, int HR>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE)))
 void pa_segment(SegmentArgs a) {
   constexpr bool U8 = KV == kU8;
@@ -1082,9 +1117,211 @@ void pa_segment(SegmentArgs a) {
       pv(std::true_type{});
   };
 
-  // Steps st_begin + wave, + NW, ...: one register set; the other
-  // wavefronts of the CU keep the memory system busy while this one computes.
-  {
+  // -------------------------------------------------------------------------
+  // Half-step path (HR > 0, 16-slot pages): the wavefront's steps are taken
+  // one sub-tile (16 keys) at a time through a ring of HR register sets, and
+  // the loads of half-step j + HR are issued as soon as half-step j has been
+  // computed, so loads stay in flight while the wavefront computes.  Half-
+  // steps past the wavefront's last are still issued (the count of
+  // outstanding loads stays static, so the compiler's waits are exact) but
+  // every lane of them reads the same 16 bytes of the segment's first page:
+  // one cache line, no bandwidth.  PV runs as 16x16x16 products over the
+  // sub-tile's 16 keys.
+  // -------------------------------------------------------------------------
+  struct Half {
+    u32x4 k[LK];
+    u32x4 v[LV];
+    u32x4 ks, vs;
+  };
+  auto load_half = [&](int st, int tau, Half& r, bool real, bool with_q) {
+    size_t row0;
+    int lane_off;
+    if (real) {
+      row0 = tile_of(st, tau);
+      lane_off = lane * 16;
+    } else {
+      row0 = ((size_t)s_bt[0] * Hkv + h) * BS;           // a valid page; one line for all lanes
+      lane_off = 0;
+    }
+    const char* kp = kb + row0 * D * EB + lane_off;
+#pragma unroll
+    for (int c = 0; c < LK; ++c) r.k[c] = ld16_stream(kp + (real ? c * 1024 : 0));
+    if (with_q) load_q();
+    const char* vp = vb + row0 * D * EB + lane_off;
+#pragma unroll
+    for (int c = 0; c < LV; ++c) r.v[c] = ld16_stream(vp + (real ? c * 1024 : 0));
+    if constexpr (U8) {
+      const size_t srow = (row0 + (real ? q4 * 4 : 0)) * 4;
+      r.ks = ld16_stream(kszb + srow);
+      r.vs = ld16_stream(vszb + srow);
+    }
+  };
+
+  auto compute_half = [&](int st, int tau, Half& r) {
+    const int key0 = si.base + st * kKeysPerStep + tau * 16;
+    // S^T for the sub-tile: lane (row, q4) gets keys key0 + 4*q4 + 0..3
+    float sv[RB][4];
+    {
+      f32x4 acc0[RB], acc1[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) acc0[rb] = acc1[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (U8) {
+#pragma unroll
+        for (int c2 = 0; c2 < LK; ++c2) {
+          const u32x4 w = r.k[c2];
+          const u32x2 a0 = u8x4_to_16<QT>(w[0]), a1 = u8x4_to_16<QT>(w[1]);
+          const u32x2 a2 = u8x4_to_16<QT>(w[2]), a3 = u8x4_to_16<QT>(w[3]);
+          const u32x4 k0 = {a0[0], a0[1], a1[0], a1[1]}, k1 = {a2[0], a2[1], a3[0], a3[1]};
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            acc0[rb] = mfma32<QT>(k0, qreg[rb][2 * c2], acc0[rb]);
+            acc1[rb] = mfma32<QT>(k1, qreg[rb][2 * c2 + 1], acc1[rb]);
+          }
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const f32x4 acc = acc0[rb] + acc1[rb];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float sk = lo_f16(r.ks[e]), zk = hi_f16(r.ks[e]) + kU8Bias<QT>;
+            sv[rb][e] = sk * (acc[e] - zk * qsum[rb]) * a.scale_log2;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < QC; c += 2) {
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            acc0[rb] = mfma32<QT>(r.k[c], qreg[rb][c], acc0[rb]);
+            if (c + 1 < QC) acc1[rb] = mfma32<QT>(r.k[c + 1], qreg[rb][c + 1], acc1[rb]);
+          }
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const f32x4 acc = acc0[rb] + acc1[rb];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sv[rb][e] = acc[e] * a.scale_log2;
+        }
+      }
+    }
+    const bool interior = key0 >= lo_max && key0 + 16 <= all_see;
+    bool kvalid[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kvalid[e] = true;
+    if (!interior) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = key0 + q4 * 4 + e;
+        kvalid[e] = t >= si.lo0 && t < si.ctx;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const bool seen = t >= lo_r[rb] && (t < si.L || (t < si.ctx && ((vis_r[rb] >> (t - si.L)) & 1u)));
+          sv[rb][e] = seen ? sv[rb][e] : -INFINITY;
+        }
+      }
+    }
+    u32x2 pb_hi[RB], pb_lo[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float mx = fmaxf(fmaxf(sv[rb][0], sv[rb][1]), fmaxf(sv[rb][2], sv[rb][3]));
+      mx = group_max(mx);
+      const bool need = mx > m_run[rb] + kRescaleLog2;
+      if (__any(need)) {
+        const float m_new = need ? mx : m_run[rb];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - (m_new == -INFINITY ? 0.f : m_new));
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[rb][dt] *= alpha;
+        l_run[rb] *= alpha;
+        c_run[rb] *= alpha;
+        m_run[rb] = m_new;
+      }
+      const float m_use = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
+      float p[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(sv[rb][e] - m_use);
+        psum += p[e];
+      }
+      l_run[rb] += psum;
+      if constexpr (U8) {
+        float csum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = r.vs[e];
+          float sp = kvalid[e] ? p[e] * lo_f16(w) : 0.f;
+          if constexpr (QT == kF16) sp = (float)(_Float16)sp;
+          csum += kvalid[e] ? sp * (hi_f16(w) + kU8Bias<QT>) : 0.f;
+          p[e] = sp;
+        }
+        c_run[rb] += csum;
+      }
+      pack_p4<QT>(p, pb_hi[rb], pb_lo[rb]);
+    }
+    // PV over the sub-tile's 16 keys: A of lane (d, q4) is V of keys
+    // 4*q4 + 0..3 at d, B the lane's four weights
+    auto pv = [&](auto masked) {
+      u32x2 vmask;
+      if constexpr (decltype(masked)::value) {
+        vmask[0] = (kvalid[0] ? 0x0000FFFFu : 0u) | (kvalid[1] ? 0xFFFF0000u : 0u);
+        vmask[1] = (kvalid[2] ? 0x0000FFFFu : 0u) | (kvalid[3] ? 0xFFFF0000u : 0u);
+      }
+      auto vop = [&](int dt) {
+        u32x2 va;
+        if constexpr (U8) {
+          va = u8x4_to_16<QT>(r.v[dt / 4][dt % 4]);
+        } else {
+          const u32x4 w = r.v[dt / 2];
+          va = (dt % 2) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
+          if constexpr (decltype(masked)::value) va &= vmask;
+        }
+        return va;
+      };
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const u32x2 va = vop(dt);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[rb][dt] = mfma16<QT>(va, pb_hi[rb], o[rb][dt]);
+      }
+      if constexpr (QT == kBF16) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const u32x2 va = vop(dt);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) o[rb][dt] = mfma16<QT>(va, pb_lo[rb], o[rb][dt]);
+        }
+      }
+    };
+    if (U8 || interior)
+      pv(std::false_type{});
+    else
+      pv(std::true_type{});
+  };
+
+  if constexpr (HR > 0 && BS >= 16) {
+    // the wavefront's half-steps j = 0 .. nh - 1: step st_begin + wave +
+    // (j / 2) * NW, sub-tile j % 2
+    const int first = st_begin + wave;
+    const int nh = first < st_end ? 2 * ((st_end - 1 - first) / NW + 1) : 0;
+    if (nh > 0) {
+      Half ring[HR];
+#pragma unroll
+      for (int i = 0; i < HR; ++i)
+        load_half(first + (i >> 1) * NW, i & 1, ring[i], i < nh, i == 0);
+      finish_q();
+      for (int j0 = 0; j0 < nh; j0 += HR) {
+#pragma unroll
+        for (int i = 0; i < HR; ++i) {
+          const int j = j0 + i;
+          if (j < nh) compute_half(first + (j >> 1) * NW, j & 1, ring[i]);
+          const int jn = j + HR;
+          load_half(first + (jn >> 1) * NW, jn & 1, ring[i], jn < nh, false);
+        }
+      }
+    }
+  } else {
+    // Steps st_begin + wave, + NW, ...: one register set; the other
+    // wavefronts of the CU keep the memory system busy while this one computes.
     Step ra;
     int st = st_begin + wave;
     if (st < st_end) {
@@ -1173,7 +1410,7 @@ template <int QT, int KV, int D, int BS, int RB>
 hipError_t launch_seg(const SegmentArgs& a, dim3 grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   constexpr SegConfig c = seg_config(KV, D, RB, BS);
   static_assert(c.waves_per_group <= 4 * c.waves_per_simd, "a workgroup must fit on one CU");
-  constexpr auto kern = pa_segment<QT, KV, D, BS, c.waves_per_group, c.waves_per_simd, RB>;
+  constexpr auto kern = pa_segment<QT, KV, D, BS, c.waves_per_group, c.waves_per_simd, RB, c.half_ring>;
   return launch_kernel(reinterpret_cast<const void*>(kern), grid, dim3(c.waves_per_group * kWave),
                        st, a, ev0, ev1);
 }
