@@ -122,6 +122,12 @@ struct SegConfig {
   int waves_per_group = kWavesPerGroup;
   int half_ring = 0;   // > 0: half-step path with this many register sets (16-slot pages)
 };
+// The half-step path (two register sets of one 16-slot sub-tile each, see the
+// segment kernel) is used where it measured faster, same-box A/B of graph-
+// replayed us per call: u8 head_dim 256, 21.08 -> 20.76 (three sets 21.99);
+// 16-bit head_dim 128, ragged batch 64.19 -> 63.85, 32k 26.20 -> 26.13.  Not
+// at 16-bit head_dim 256 (window layer 8.63 -> 10.12, global 83.98 -> 84.69)
+// or head_dim 64 (16.54 -> 17.05).
 constexpr SegConfig seg_config(int kv_dtype, int D, int rb, int bs = 16) {
   // Pages of fewer than 16 slots: one 8-wavefront workgroup per CU as for
   // 16-slot pages (C2 shape at 32k, us per call: 2 slots 29.8 vs 29.9 for two
@@ -130,7 +136,7 @@ constexpr SegConfig seg_config(int kv_dtype, int D, int rb, int bs = 16) {
   if (rb > 1) return (rb == 2 && D <= 128) || D <= 64 ? SegConfig{2, 1, 8} : SegConfig{1, 1};
   if (kv_dtype == kU8)
     return D >= 256 ? SegConfig{2, 1, 8, kHalfRingU8} : D >= 128 ? SegConfig{2, 1, 8} : SegConfig{4, 4};
-  return D >= 256 ? SegConfig{1, 1} : D >= 128 ? SegConfig{2, 1, 8} : SegConfig{4, 2, 8};
+  return D >= 256 ? SegConfig{1, 1} : D >= 128 ? SegConfig{2, 1, 8, 2} : SegConfig{4, 2, 8};
 }
 constexpr int groups_per_cu(int kv_dtype, int D, int rb, int bs) {
   return seg_config(kv_dtype, D, rb, bs).groups_per_cu;
