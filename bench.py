@@ -42,6 +42,11 @@ def workloads():
         "gqa4_d128_f16_L32768": lambda T: pi.config2(32768, T),
         "gqa4_d128_f16_L8192": lambda T: pi.config2(8192, T),
         "gqa4_d128_f16_L32768_tree": lambda T: pi.config2(32768, T, tree=True),
+        # the same cache in row-major pages ([num_blocks, Hkv, block_size, D])
+        "gqa4_d128_f16_L32768_rowmajor": lambda T: pi.with_layout(pi.config2(32768, T), 1),
+        "u8kv_d256_L32768_rowmajor": lambda T: pi.with_layout(pi.config3(32768, T), 1),
+        "swa_pair_global_L32768_rowmajor": lambda T: pi.with_layout(pi.config4(32768, window=0, T=T), 1),
+        "ragged8_bf16_rowmajor": lambda T: pi.with_layout(pi.config5(), 1),
         "gqa4_d128_f16_L32768_bs1": lambda T: pi.config2(32768, T, block_size=1),
         "gqa4_d128_f16_L32768_bs2": lambda T: pi.config2(32768, T, block_size=2),
         "gqa4_d128_f16_L32768_bs4": lambda T: pi.config2(32768, T, block_size=4),
@@ -115,7 +120,7 @@ class Runner:
         c = case
         self.prepared = []
         opts = dict(sliding_window=c.sliding_window, max_query_len=max(c.Ts),
-                    tree_mask=self.dev.get("tree_mask"))
+                    tree_mask=self.dev.get("tree_mask"), page_layout=c.page_layout)
         for d in self.pools:
             if c.kv_dtype == 2:
                 pc = pav.prepare_forward_u8(d["q"], d["k_cache"], d["v_cache"], d["k_scale_zp"],
@@ -211,11 +216,12 @@ def time_append(case, steps, warmup, repeats):
         if case.kv_dtype == 2:
             pav.pa_kv_append_u8(k_new, v_new, dev["k_cache"], dev["v_cache"], dev["k_scale_zp"],
                                 dev["v_scale_zp"], dev["block_tables"], dev["past_lens"],
-                                dev["subsequence_begins"], max_query_len=max(case.Ts), stream=stream)
+                                dev["subsequence_begins"], max_query_len=max(case.Ts), stream=stream,
+                                page_layout=case.page_layout)
         else:
             pav.pa_kv_append(k_new, v_new, dev["k_cache"], dev["v_cache"], dev["block_tables"],
                              dev["past_lens"], dev["subsequence_begins"], max_query_len=max(case.Ts),
-                             stream=stream)
+                             stream=stream, page_layout=case.page_layout)
 
     for _ in range(warmup):
         one(torch.cuda.current_stream().cuda_stream)

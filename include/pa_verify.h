@@ -53,6 +53,16 @@
  *     V u8:       (((((s/16)*(D/64) + d/64)*4 + (s%16)/4)*16 + d%16)*4 + (d%64)/16)*4 + s%4
  *                Pages of 1, 2, 4 or 8 slots hold K row-major (s*D + d) and V
  *                d-major (d*block_size + s), for every cache dtype.
+ *                With params->page_layout = PA_PAGES_ROW_MAJOR every page is
+ *                instead row-major for K and V, element (s, d) at s*D + d: the
+ *                conventional [num_blocks, Hkv, block_size, D] cache.  The
+ *                tiled order is the default because every load instruction then
+ *                reads 1 KB of contiguous memory straight into MFMA operand
+ *                order, while row-major V has to be reordered through LDS.
+ *                Measured on MI355X, us per call tiled vs row-major: 32k
+ *                context, 32 q / 8 KV heads, head_dim 128, f16: 26.2 vs 27.8;
+ *                bf16 head_dim 256 (16 KV heads): 84.8 vs 102.9; ragged bf16
+ *                batch: 64.1 vs 69.3; u8 head_dim 256: 20.8 vs 51.3.
  *  k_scale_zp,   [num_blocks, Hkv, block_size, 2]     f16 (scale, zero_point) per
  *  v_scale_zp    token per KV head, u8 variant only; dequant = (u - zp) * scale
  *  block_tables  [num_seqs, max_blocks_per_seq] int32 physical block ids
@@ -105,6 +115,11 @@ typedef enum pa_status {
   PA_ERR_DEVICE_CONTRACT = 5   /* device-side metadata violated the contract (see above) */
 } pa_status;
 
+typedef enum pa_page_layout {
+  PA_PAGES_TILED = 0,      /* the MFMA-operand order above (default) */
+  PA_PAGES_ROW_MAJOR = 1   /* every page [block_size][D] for K and V */
+} pa_page_layout;
+
 typedef enum pa_dtype {
   PA_F16 = 0,
   PA_BF16 = 1,
@@ -148,6 +163,8 @@ typedef struct pa_verify_params {
                                   rule; the row's own bit is implied, bits >= T_s are ignored,
                                   every past position stays visible.  NULL = causal rows.
                                   Requires sliding_window == 0 (else PA_ERR_UNSUPPORTED) */
+  int32_t page_layout;         /* pa_page_layout of k_cache and v_cache (forward and append
+                                  calls); anything else is PA_ERR_INVALID_ARG */
 } pa_verify_params;
 
 /* The launch plan, a pure function of host scalars: segment count S, keys per
@@ -245,7 +262,7 @@ int pa_verify_forward_u8(const void* q, const uint8_t* k_cache, const uint8_t* v
  * the op's cache holds the new tokens, u8 with f16 compute).  Token b_s + i
  * of sequence s goes to position L_s + i: block
  * block_tables[s][(L_s + i) / block_size], slot (L_s + i) % block_size, in
- * the tiled page layout above.  k_new, v_new: device [num_tokens, Hkv, D] in
+ * the page layout p->page_layout names.  k_new, v_new: device [num_tokens, Hkv, D] in
  * p->q_dtype.  Uses p's sizes, dtypes, max_query_len, stream and the status
  * word at the head of p->workspace (>= 4 bytes); not max_context_len.
  * Device-side contract violations (as for the forward call, with positions

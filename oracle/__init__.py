@@ -44,6 +44,7 @@ class _Args(ctypes.Structure):
         ("subsequence_begins", ctypes.c_void_p), ("tree_mask", ctypes.c_void_p),
         ("pairs", ctypes.c_void_p),
         ("num_pairs", ctypes.c_int64), ("num_threads", ctypes.c_int32),
+        ("page_layout", ctypes.c_int32),
     ]
 
 
@@ -68,7 +69,7 @@ class _AppendArgs(ctypes.Structure):
         ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
         ("k_scale_zp", ctypes.c_void_p), ("v_scale_zp", ctypes.c_void_p),
         ("block_tables", ctypes.c_void_p), ("past_lens", ctypes.c_void_p),
-        ("subsequence_begins", ctypes.c_void_p),
+        ("subsequence_begins", ctypes.c_void_p), ("page_layout", ctypes.c_int32),
     ]
 
 
@@ -115,7 +116,8 @@ class Oracle:
                         case.kv_dtype, kn.ctypes.data, vn.ctypes.data, k.ctypes.data, v.ctypes.data,
                         None if ksz is None else ksz.ctypes.data,
                         None if vsz is None else vsz.ctypes.data,
-                        bt.ctypes.data, pl.ctypes.data, sb.ctypes.data)
+                        bt.ctypes.data, pl.ctypes.data, sb.ctypes.data,
+                        int(getattr(case, "page_layout", 0)))
         st = self.lib.pa_oracle_kv_append(ctypes.byref(a))
         return int(st), k, v, ksz, vsz
 
@@ -126,7 +128,7 @@ class Oracle:
             num_blocks, max_blocks_per_seq, sliding_window, max_context_len, q_dtype, kv_dtype,
             scale, q, k_cache, v_cache, block_tables, past_lens, subsequence_begins,
             k_scale_zp=None, v_scale_zp=None, tree_mask=None, pairs=None, threads=0,
-            **_ignored):
+            page_layout=0, **_ignored):
         """Return (status, out).  out is fp64 [num_tokens, Hq, D] or [len(pairs), D]."""
         keep = []
 
@@ -144,7 +146,7 @@ class Oracle:
                   ptr(q), ptr(k_cache), ptr(v_cache), ptr(k_scale_zp), ptr(v_scale_zp),
                   ptr(block_tables, np.int32), ptr(past_lens, np.int32),
                   ptr(subsequence_begins, np.int32), ptr(tree_mask, np.uint32), ptr(pairs_arr),
-                  0 if pairs_arr is None else pairs_arr.shape[0], int(threads))
+                  0 if pairs_arr is None else pairs_arr.shape[0], int(threads), int(page_layout))
         rows = num_tokens * num_q_heads if pairs_arr is None else pairs_arr.shape[0]
         out = np.full((rows, head_dim), np.nan, dtype=np.float64)
         st = self.lib.pa_oracle_forward(ctypes.byref(a), out.ctypes.data)
@@ -173,7 +175,8 @@ def case_fields(case) -> dict:
                 v_cache=case.v_cache, k_scale_zp=case.k_scale_zp, v_scale_zp=case.v_scale_zp,
                 block_tables=case.block_tables, past_lens=case.past_lens,
                 subsequence_begins=case.subsequence_begins,
-                tree_mask=getattr(case, "tree_mask", None))
+                tree_mask=getattr(case, "tree_mask", None),
+                page_layout=int(getattr(case, "page_layout", 0)))
 
 
 _default: Optional[Oracle] = None

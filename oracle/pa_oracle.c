@@ -35,8 +35,9 @@
  * Layouts (the library's C ABI defines them; restated here on purpose):
  *   q [num_tokens][Hq][D]; k and v [nb][Hkv][page], each page holding the
  *   block_size x D elements of one (block, KV head) in the order of
- *   k_offset / v_offset below (tiled for block_size % 16 == 0; K row-major
- *   and V d-major for pages of 1, 2, 4 or 8 slots); scale/zero point
+ *   k_offset / v_offset below (row-major for layout 1; for layout 0 tiled
+ *   when block_size % 16 == 0, K row-major and V d-major for pages of 1, 2,
+ *   4 or 8 slots); scale/zero point
  *   [nb][Hkv][bs][2] (f16); block_tables [num_seqs][mbps].  Requires
  *   D % 32 == 0 (D % 64 == 0 for u8).
  * Element codes: 0 = f16 bits, 1 = bf16 bits, 2 = u8 code with f16
@@ -84,19 +85,22 @@ static double dec_elem(const void* base, size_t idx, int code) {
   }
 }
 
-/* Offsets of element (slot, d) inside one page.  Pages of 1-8 slots: K is
- * [slot][d], V is [d][slot].  Otherwise sub-tiles of 16 slots; in
- * each, K is ordered [d/32][(d%32)/8][slot%16][d%8] (u8: [d/64][(d%64)/16]
+/* Offsets of element (slot, d) inside one page.  Row-major pages (layout 1):
+ * [slot][d] for K and V.  Tiled pages (layout 0): pages of 1-8 slots hold K
+ * as [slot][d] and V as [d][slot]; larger ones are sub-tiles of 16 slots, in
+ * each of which K is ordered [d/32][(d%32)/8][slot%16][d%8] (u8: [d/64][(d%64)/16]
  * [slot%16][d%16]) and V [d/32][(slot%16)/4][d%16][(d%32)/16][slot%4] (u8:
  * [d/64][(slot%16)/4][d%16][(d%64)/16][slot%4]). */
-static size_t k_offset(int slot, int d, int D, int u8, int bs) {
+static size_t k_offset(int slot, int d, int D, int u8, int bs, int layout) {
+  if (layout == 1) return (size_t)slot * D + d;    /* row-major page */
   if (bs < 16) return (size_t)slot * D + d;        /* small pages: [slot][d] */
   const size_t st = (size_t)(slot / 16), m = (size_t)(slot % 16);
   if (u8) return (((st * (D / 64) + d / 64) * 4 + (d % 64) / 16) * 16 + m) * 16 + d % 16;
   return (((st * (D / 32) + d / 32) * 4 + (d % 32) / 8) * 16 + m) * 8 + d % 8;
 }
 
-static size_t v_offset(int slot, int d, int D, int u8, int bs) {
+static size_t v_offset(int slot, int d, int D, int u8, int bs, int layout) {
+  if (layout == 1) return (size_t)slot * D + d;    /* row-major page */
   if (bs < 16) return (size_t)d * bs + slot;       /* small pages: [d][slot] */
   const size_t st = (size_t)(slot / 16), qq = (size_t)((slot % 16) / 4);
   if (u8) return ((((st * (D / 64) + d / 64) * 4 + qq) * 16 + d % 16) * 4 + (d % 64) / 16) * 4 + slot % 4;
@@ -132,6 +136,7 @@ static int check_args(const pa_oracle_args* a) {
     return PA_ORACLE_ERR_ARG;
   if (a->kv_dtype == PA_ORACLE_U8 && (!a->k_scale_zp || !a->v_scale_zp)) return PA_ORACLE_ERR_ARG;
   if (a->tree_mask && a->sliding_window > 0) return PA_ORACLE_ERR_ARG;
+  if (a->page_layout != 0 && a->page_layout != 1) return PA_ORACLE_ERR_ARG;
   if (a->subsequence_begins[0] != 0 || a->subsequence_begins[a->num_seqs] != a->num_tokens)
     return PA_ORACLE_ERR_META;
   for (int s = 0; s < a->num_seqs; ++s) {
@@ -194,7 +199,7 @@ static void attend_one(const pa_oracle_args* a, int n, int h, double* z, double*
     double dot = 0.0;
     for (int d = 0; d < D; ++d)
       dot += dec_elem(a->q, q_off + d, a->q_dtype) *
-             kv_value(a, a->k_cache, a->k_scale_zp, page + k_offset(slot, d, D, u8, bs), row);
+             kv_value(a, a->k_cache, a->k_scale_zp, page + k_offset(slot, d, D, u8, bs, a->page_layout), row);
     z[t - lo] = a->scale * dot;
     if (z[t - lo] > m) m = z[t - lo];
   }
@@ -210,7 +215,7 @@ static void attend_one(const pa_oracle_args* a, int n, int h, double* z, double*
     const size_t row = (blk * Hkv + g) * bs + slot;
     const size_t page = (blk * Hkv + g) * (size_t)bs * D;
     for (int d = 0; d < D; ++d) {
-      const size_t vidx = page + v_offset(slot, d, D, u8, bs);
+      const size_t vidx = page + v_offset(slot, d, D, u8, bs, a->page_layout);
       out_row[d] += w * kv_value(a, a->v_cache, a->v_scale_zp, vidx, row);
     }
   }
@@ -359,6 +364,7 @@ int pa_oracle_kv_append(const pa_oracle_append_args* a) {
   const int u8 = a->kv_dtype == PA_ORACLE_U8;
   if (a->new_dtype != PA_ORACLE_F16 && a->new_dtype != PA_ORACLE_BF16) return PA_ORACLE_ERR_ARG;
   if (!u8 && a->kv_dtype != a->new_dtype) return PA_ORACLE_ERR_ARG;
+  if (a->page_layout != 0 && a->page_layout != 1) return PA_ORACLE_ERR_ARG;
   if (u8 && (!a->k_scale_zp || !a->v_scale_zp)) return PA_ORACLE_ERR_ARG;
   const int D = a->head_dim, bs = a->block_size, Hkv = a->num_kv_heads;
   if ((bs % 16 != 0 && bs != 1 && bs != 2 && bs != 4 && bs != 8) || D % (u8 ? 64 : 32) != 0)
@@ -401,7 +407,8 @@ int pa_oracle_kv_append(const pa_oracle_append_args* a) {
           void* cache = kv ? a->v_cache : a->k_cache;
           if (!u8) {
             for (int d = 0; d < D; ++d) {
-              const size_t off = page + (kv ? v_offset(slot, d, D, 0, bs) : k_offset(slot, d, D, 0, bs));
+              const size_t off = page + (kv ? v_offset(slot, d, D, 0, bs, a->page_layout)
+                                                : k_offset(slot, d, D, 0, bs, a->page_layout));
               ((uint16_t*)cache)[off] = in[src + d];
             }
             continue;
@@ -410,7 +417,8 @@ int pa_oracle_kv_append(const pa_oracle_append_args* a) {
           uint16_t sb, zb;
           pa_oracle_quantize_row(row, D, codes, &sb, &zb);
           for (int d = 0; d < D; ++d) {
-            const size_t off = page + (kv ? v_offset(slot, d, D, 1, bs) : k_offset(slot, d, D, 1, bs));
+            const size_t off = page + (kv ? v_offset(slot, d, D, 1, bs, a->page_layout)
+                                                : k_offset(slot, d, D, 1, bs, a->page_layout));
             ((uint8_t*)cache)[off] = codes[d];
           }
           uint16_t* sz = kv ? a->v_scale_zp : a->k_scale_zp;

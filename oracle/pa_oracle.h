@@ -16,8 +16,8 @@ typedef struct pa_oracle_args {
   int32_t q_dtype, kv_dtype;          /* element codes above */
   double scale;
   const void* q;                      /* [num_tokens][Hq][D] */
-  const void* k_cache;                /* [nb][Hkv][bs * D], tiled pages (see pa_oracle.c) */
-  const void* v_cache;                /* [nb][Hkv][bs * D], tiled pages */
+  const void* k_cache;                /* [nb][Hkv][bs * D] pages (see pa_oracle.c) */
+  const void* v_cache;                /* [nb][Hkv][bs * D] pages */
   const void* k_scale_zp;             /* f16 [nb][Hkv][bs][2], u8 only */
   const void* v_scale_zp;
   const int32_t* block_tables;        /* [num_seqs][max_blocks_per_seq] */
@@ -29,6 +29,8 @@ typedef struct pa_oracle_args {
   const int32_t* pairs;               /* optional [num_pairs][2] (token, q head) subset */
   int64_t num_pairs;
   int32_t num_threads;                /* 0 = all online host cores */
+  int32_t page_layout;                /* 0: tiled pages (see pa_oracle.c); 1: every page
+                                         row-major [slot][d] for K and V */
 } pa_oracle_args;
 
 /* Writing the new tokens into the cache (the step before the attention):
@@ -44,13 +46,14 @@ typedef struct pa_oracle_append_args {
   int32_t new_dtype, kv_dtype;
   const void* k_new;
   const void* v_new;
-  void* k_cache;                      /* [nb][Hkv][bs * D] tiled pages */
+  void* k_cache;                      /* [nb][Hkv][bs * D] pages */
   void* v_cache;
   uint16_t* k_scale_zp;               /* f16 [nb][Hkv][bs][2], u8 only */
   uint16_t* v_scale_zp;
   const int32_t* block_tables;
   const int32_t* past_lens;
   const int32_t* subsequence_begins;
+  int32_t page_layout;                /* as in pa_oracle_args */
 } pa_oracle_append_args;
 
 int pa_oracle_kv_append(const pa_oracle_append_args* a);

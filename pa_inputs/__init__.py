@@ -28,7 +28,8 @@ Recipe (also the basis of every parity case and of the benchmark):
 Layouts match the C ABI header: every (block, KV head) page of K and V holds
 its block_size x D elements in the tiled order of ``k_page_offset`` /
 ``v_page_offset`` (16-slot sub-tiles in MFMA operand order; pages of 1-8
-slots: K row-major, V d-major); scale/zp
+slots: K row-major, V d-major), or, for ``page_layout=1``, row-major
+[slot][d] (``with_layout`` converts a case); scale/zp
 [nb, Hkv, bs, 2] f16; q [num_tokens, Hq, D].  ``tile_k`` / ``tile_v`` turn
 [..., bs, D] pages into that order and ``untile_k`` / ``untile_v`` back.
 """
@@ -41,6 +42,7 @@ from typing import List, Optional, Sequence
 import numpy as np
 
 F16, BF16, U8 = 0, 1, 2          # same integer codes as the C ABI's pa_dtype
+PAGES_TILED, PAGES_ROW_MAJOR = 0, 1   # the C ABI's pa_page_layout
 DTYPE_NAMES = {F16: "f16", BF16: "bf16", U8: "u8"}
 BAD_BLOCK_ID = 0x7FFFFFF0        # block-table filler past a sequence's last block
 _CHUNK_VALUES = 1 << 22          # pools are drawn in chunks of whole blocks of about this size
@@ -201,6 +203,7 @@ class Case:
     past_lens: np.ndarray         # int32 [num_seqs]
     subsequence_begins: np.ndarray  # int32 [num_seqs + 1]
     tree_mask: Optional[np.ndarray] = None  # uint32 [num_tokens] (tree verify), None = causal
+    page_layout: int = 0          # 0: tiled pages (tile_k / tile_v); 1: row-major [slot][d]
 
     @property
     def Ts(self) -> List[int]:
@@ -227,6 +230,9 @@ class Case:
         """K and V pools as logical [nb, Hkv, bs, D] arrays of stored codes."""
         u8 = self.kv_dtype == U8
         bs, D = self.block_size, self.head_dim
+        if self.page_layout == PAGES_ROW_MAJOR:
+            shape = self.k_cache.shape[:2] + (bs, D)
+            return self.k_cache.reshape(shape).copy(), self.v_cache.reshape(shape).copy()
         flat = self.k_cache.shape[:2] + (bs * D,)
         return (untile_k(self.k_cache.reshape(flat), bs, D, u8),
                 untile_v(self.v_cache.reshape(flat), bs, D, u8))
@@ -309,7 +315,8 @@ def build_case(seed: Sequence[int], past_lens: Sequence[int], Ts: Sequence[int],
                spare_blocks: int = 0, poison: bool = False,
                scale: Optional[float] = None, max_blocks_per_seq: Optional[int] = None,
                max_context_len: Optional[int] = None, name: str = "case",
-               rng: Optional[np.random.Generator] = None, tree: bool = False) -> Case:
+               rng: Optional[np.random.Generator] = None, tree: bool = False,
+               page_layout: int = PAGES_TILED) -> Case:
     """Build one call's inputs following the module recipe.  tree=True adds
     a random draft tree per sequence (drawn after everything else, so the
     other arrays are those of the same case without a tree)."""
@@ -351,10 +358,13 @@ def build_case(seed: Sequence[int], past_lens: Sequence[int], Ts: Sequence[int],
         _poison(k_log, v_log, k_sz, v_sz, kv_dtype, bt, past_lens, Ts, bs,
                 sliding_window, spare)
     u8 = kv_dtype == U8
-    k_cache = tile_k(k_log, u8).reshape(k_log.shape)
-    del k_log
-    v_cache = tile_v(v_log, u8).reshape(v_log.shape)
-    del v_log
+    if page_layout == PAGES_ROW_MAJOR:
+        k_cache, v_cache = k_log, v_log
+    else:
+        k_cache = tile_k(k_log, u8).reshape(k_log.shape)
+        del k_log
+        v_cache = tile_v(v_log, u8).reshape(v_log.shape)
+        del v_log
     tm = tree_masks([random_parents(rng, T) for T in Ts]) if tree else None
 
     return Case(name=name, num_seqs=num_seqs, num_tokens=num_tokens,
@@ -365,7 +375,7 @@ def build_case(seed: Sequence[int], past_lens: Sequence[int], Ts: Sequence[int],
                 max_context_len=int(max_context_len), q=q, k_cache=k_cache, v_cache=v_cache,
                 k_scale_zp=k_sz, v_scale_zp=v_sz, block_tables=bt,
                 past_lens=np.asarray(past_lens, dtype=np.int32), subsequence_begins=sb,
-                tree_mask=tm)
+                tree_mask=tm, page_layout=int(page_layout))
 
 
 def _poison(k, v, ksz, vsz, kv_dtype, bt, past_lens, Ts, bs, W, spare):
@@ -393,6 +403,26 @@ def _poison(k, v, ksz, vsz, kv_dtype, bt, past_lens, Ts, bs, W, spare):
                 kill(bt[s, b], slots)
     for blk in spare:
         kill(int(blk), np.arange(bs))
+
+
+def pages_to_cache(k_log, v_log, u8: bool, page_layout: int):
+    """Logical [nb, Hkv, bs, D] K and V code pools stored in a page layout."""
+    if page_layout == PAGES_ROW_MAJOR:
+        return np.ascontiguousarray(k_log), np.ascontiguousarray(v_log)
+    return tile_k(k_log, u8).reshape(k_log.shape), tile_v(v_log, u8).reshape(v_log.shape)
+
+
+def with_layout(case: Case, page_layout: int) -> Case:
+    """The same logical cache (every page's codes) in the other page layout."""
+    if page_layout == case.page_layout:
+        return case
+    u8 = case.kv_dtype == U8
+    kl, vl = case.logical_pages()
+    out = Case(**{f.name: getattr(case, f.name) for f in dataclasses.fields(case)})
+    out.k_cache, out.v_cache = pages_to_cache(kl, vl, u8, page_layout)
+    out.page_layout = int(page_layout)
+    out.name = case.name + ("_rowmajor" if page_layout == PAGES_ROW_MAJOR else "_tiled")
+    return out
 
 
 def peaked(case: Case, seed: Sequence[int], *, stairs: int = 8, gap: float = 7.0,
@@ -452,7 +482,7 @@ def peaked(case: Case, seed: Sequence[int], *, stairs: int = 8, gap: float = 7.0
                 kl[blk, :, slot, :] = f32_to_bits(row, case.kv_dtype)
     out = Case(**{f.name: getattr(case, f.name) for f in dataclasses.fields(case)})
     out.q = q
-    out.k_cache = tile_k(kl, u8).reshape(case.k_cache.shape)
+    out.k_cache = kl if case.page_layout == PAGES_ROW_MAJOR else tile_k(kl, u8).reshape(case.k_cache.shape)
     out.k_scale_zp = ksz
     out.name = case.name + "_peaked"
     return out

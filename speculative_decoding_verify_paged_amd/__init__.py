@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(PKG, "libpa_verify.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_DEVICE_CONTRACT = range(6)
 PA_F16, PA_BF16, PA_U8 = 0, 1, 2
+PA_PAGES_TILED, PA_PAGES_ROW_MAJOR = 0, 1
 
 # every symbol include/pa_verify.h declares
 EXPORTS = ("pa_verify_make_plan", "pa_verify_workspace_bytes", "pa_verify_forward",
@@ -48,6 +49,7 @@ class PaVerifyParams(ctypes.Structure):
         ("stream", ctypes.c_void_p),
         ("prof_event_begin", ctypes.c_void_p), ("prof_event_end", ctypes.c_void_p),
         ("tree_mask", ctypes.c_void_p),
+        ("page_layout", ctypes.c_int32),
     ]
 
 
@@ -120,12 +122,13 @@ def pa_verify_status_string(code: int) -> str:
 def make_params(*, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, block_size,
                 num_blocks, max_blocks_per_seq, q_dtype, kv_dtype, sliding_window=0,
                 num_segments=0, max_query_len=0, workspace=0, workspace_bytes=0, stream=0,
-                prof_event_begin=0, prof_event_end=0, tree_mask=0) -> PaVerifyParams:
+                prof_event_begin=0, prof_event_end=0, tree_mask=0,
+                page_layout=PA_PAGES_TILED) -> PaVerifyParams:
     return PaVerifyParams(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, block_size,
                           num_blocks, max_blocks_per_seq, sliding_window, num_segments,
                           q_dtype, kv_dtype, max_query_len, workspace or None, workspace_bytes,
                           stream or None, prof_event_begin or None, prof_event_end or None,
-                          tree_mask or None)
+                          tree_mask or None, page_layout)
 
 
 def pa_verify_make_plan(params: PaVerifyParams, max_context_len: int, num_cus: int) -> dict:
@@ -239,7 +242,7 @@ class PreparedCall:
 def _call(u8, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
           subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
           ws, stream, prof_events, prepare=False, max_query_len=0, tree_mask=None,
-          noalloc=False):
+          noalloc=False, page_layout=PA_PAGES_TILED):
     torch = _torch()
     dev = q.device
     _check(q, "q", ndim=3, device=dev)
@@ -252,7 +255,7 @@ def _call(u8, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_le
     nb, Hkv, bs, D2 = k_cache.shape
     if D2 != D or tuple(v_cache.shape) != (nb, Hkv, bs, D):
         raise ValueError("k_cache and v_cache must both be [nb, Hkv, bs, D] (page contents in "
-                         "the tiled order of include/pa_verify.h)")
+                         "the order page_layout names, see include/pa_verify.h)")
     if k_cache.dtype != v_cache.dtype:
         raise ValueError("k_cache and v_cache dtypes differ")
     if u8:
@@ -280,7 +283,8 @@ def _call(u8, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_le
                          max_blocks_per_seq=block_tables.shape[1], q_dtype=_dtype_code(q),
                          kv_dtype=_dtype_code(k_cache), sliding_window=int(sliding_window),
                          num_segments=int(num_segments), max_query_len=int(max_query_len),
-                         tree_mask=0 if tree_mask is None else tree_mask.data_ptr())
+                         tree_mask=0 if tree_mask is None else tree_mask.data_ptr(),
+                         page_layout=int(page_layout))
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     params.stream = stream or None
@@ -327,7 +331,8 @@ def _call(u8, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_le
 def pa_verify_forward(q, k_cache, v_cache, block_tables, past_lens, subsequence_begins,
                       max_context_len: int, scale: float, out=None, *, sliding_window: int = 0,
                       num_segments: int = 0, workspace=None, stream: Optional[int] = None,
-                      prof_events=None, max_query_len: int = 0, tree_mask=None):
+                      prof_events=None, max_query_len: int = 0, tree_mask=None,
+        page_layout: int = PA_PAGES_TILED):
     """Paged verify attention over an f16/bf16 cache; returns ``out``.
 
     q [num_tokens, Hq, D]; k_cache, v_cache [nb, Hkv, bs, D] with each page's
@@ -344,13 +349,15 @@ def pa_verify_forward(q, k_cache, v_cache, block_tables, past_lens, subsequence_
     ``workspace()``: calls that share it must be ordered)."""
     return _call(False, q, k_cache, v_cache, None, None, block_tables, past_lens,
                  subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
-                 workspace, stream, prof_events, max_query_len=max_query_len, tree_mask=tree_mask)
+                 workspace, stream, prof_events, max_query_len=max_query_len, tree_mask=tree_mask,
+                 page_layout=page_layout)
 
 
 def pa_verify_forward_noalloc(q, k_cache, v_cache, block_tables, past_lens, subsequence_begins,
                               max_context_len: int, scale: float, out, *, sliding_window: int = 0,
                               num_segments: int = 0, stream: Optional[int] = None,
-                              max_query_len: int = 0, tree_mask=None):
+                              max_query_len: int = 0, tree_mask=None,
+        page_layout: int = PA_PAGES_TILED):
     """pa_verify_forward without any workspace: the library works in its static
     device scratch (32 MiB per GPU), so nothing is allocated by the call or
     here — ``out`` must be given.  Calls on one GPU share that scratch and
@@ -360,18 +367,20 @@ def pa_verify_forward_noalloc(q, k_cache, v_cache, block_tables, past_lens, subs
     return _call(False, q, k_cache, v_cache, None, None, block_tables, past_lens,
                  subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
                  None, stream, None, max_query_len=max_query_len, tree_mask=tree_mask,
-                 noalloc=True)
+                 noalloc=True, page_layout=page_layout)
 
 
 def pa_verify_forward_u8(q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
                          subsequence_begins, max_context_len: int, scale: float, out=None, *,
                          sliding_window: int = 0, num_segments: int = 0, workspace=None,
                          stream: Optional[int] = None, prof_events=None, max_query_len: int = 0,
-                         tree_mask=None):
+                         tree_mask=None,
+        page_layout: int = PA_PAGES_TILED):
     """The same over a u8 cache with f16 (scale, zero point) per token per KV head."""
     return _call(True, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
                  subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
-                 workspace, stream, prof_events, max_query_len=max_query_len, tree_mask=tree_mask)
+                 workspace, stream, prof_events, max_query_len=max_query_len, tree_mask=tree_mask,
+                 page_layout=page_layout)
 
 
 def pa_verify_read_status(device=None) -> int:
@@ -400,28 +409,30 @@ def pa_verify_read_status(device=None) -> int:
 def prepare_forward(q, k_cache, v_cache, block_tables, past_lens, subsequence_begins,
                     max_context_len: int, scale: float, out=None, *, sliding_window: int = 0,
                     num_segments: int = 0, workspace=None, stream: Optional[int] = None,
-                    max_query_len: int = 0, tree_mask=None):
+                    max_query_len: int = 0, tree_mask=None,
+        page_layout: int = PA_PAGES_TILED):
     """pa_verify_forward's checks and marshalling done once: returns a
     PreparedCall that enqueues the same call each time it is called."""
     return _call(False, q, k_cache, v_cache, None, None, block_tables, past_lens,
                  subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
                  workspace, stream, None, prepare=True, max_query_len=max_query_len,
-                 tree_mask=tree_mask)
+                 tree_mask=tree_mask, page_layout=page_layout)
 
 
 def prepare_forward_u8(q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
                        subsequence_begins, max_context_len: int, scale: float, out=None, *,
                        sliding_window: int = 0, num_segments: int = 0, workspace=None,
-                       stream: Optional[int] = None, max_query_len: int = 0, tree_mask=None):
+                       stream: Optional[int] = None, max_query_len: int = 0, tree_mask=None,
+        page_layout: int = PA_PAGES_TILED):
     """pa_verify_forward_u8's checks and marshalling done once (see prepare_forward)."""
     return _call(True, q, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
                  subsequence_begins, max_context_len, scale, out, sliding_window, num_segments,
                  workspace, stream, None, prepare=True, max_query_len=max_query_len,
-                 tree_mask=tree_mask)
+                 tree_mask=tree_mask, page_layout=page_layout)
 
 
 def _append(u8, k_new, v_new, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
-            subsequence_begins, max_query_len, stream):
+            subsequence_begins, max_query_len, stream, page_layout=PA_PAGES_TILED):
     torch = _torch()
     dev = k_new.device
     _check(k_new, "k_new", ndim=3, device=dev)
@@ -448,7 +459,8 @@ def _append(u8, k_new, v_new, k_cache, v_cache, k_scale_zp, v_scale_zp, block_ta
     params = make_params(num_seqs=num_seqs, num_tokens=num_tokens, num_q_heads=Hkv,
                          num_kv_heads=Hkv, head_dim=D, block_size=bs, num_blocks=nb,
                          max_blocks_per_seq=block_tables.shape[1], q_dtype=_dtype_code(k_new),
-                         kv_dtype=_dtype_code(k_cache), max_query_len=int(max_query_len))
+                         kv_dtype=_dtype_code(k_cache), max_query_len=int(max_query_len),
+                         page_layout=int(page_layout))
     params.stream = (torch.cuda.current_stream(dev).cuda_stream if stream is None else stream) or None
     with torch.cuda.device(dev):
         ws = workspace(256, dev)
@@ -469,18 +481,19 @@ def _append(u8, k_new, v_new, k_cache, v_cache, k_scale_zp, v_scale_zp, block_ta
 
 
 def pa_kv_append(k_new, v_new, k_cache, v_cache, block_tables, past_lens, subsequence_begins, *,
-                 max_query_len: int = 0, stream: Optional[int] = None):
+                 max_query_len: int = 0, stream: Optional[int] = None,
+                 page_layout: int = PA_PAGES_TILED):
     """Write the new tokens' K/V ([num_tokens, Hkv, D], f16 or bf16) into an
     f16/bf16 cache of the same dtype at positions past_len + i (in place)."""
     _append(False, k_new, v_new, k_cache, v_cache, None, None, block_tables, past_lens,
-            subsequence_begins, max_query_len, stream)
+            subsequence_begins, max_query_len, stream, page_layout)
 
 
 def pa_kv_append_u8(k_new, v_new, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables,
                     past_lens, subsequence_begins, *, max_query_len: int = 0,
-                    stream: Optional[int] = None):
+                    stream: Optional[int] = None, page_layout: int = PA_PAGES_TILED):
     """The same into a u8 cache: each (token, KV head) row is quantised and its
     f16 (scale, zero point) written to k_scale_zp / v_scale_zp (in place)."""
     _append(True, k_new, v_new, k_cache, v_cache, k_scale_zp, v_scale_zp, block_tables, past_lens,
-            subsequence_begins, max_query_len, stream)
+            subsequence_begins, max_query_len, stream, page_layout)
 

@@ -97,7 +97,8 @@ __global__ __launch_bounds__(kWave) void pa_append(AppendArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int d = lane + e * kWave;
-      if (d < D) dst[kv ? v_off(slot, d, D, false, a.bs) : k_off(slot, d, D, false, a.bs)] = src[d];
+      if (d < D) dst[a.page_layout == kPagesRowMajor ? slot * D + d
+                    : kv ? v_off(slot, d, D, false, a.bs) : k_off(slot, d, D, false, a.bs)] = src[d];
     }
   } else {
     float mn = x[0], mx = x[0];
@@ -122,7 +123,8 @@ __global__ __launch_bounds__(kWave) void pa_append(AppendArgs a) {
     for (int e = 0; e < E; ++e) {
       const int d = lane + e * kWave;
       const float r = fminf(fmaxf(rintf(__fadd_rn(__fdiv_rn(x[e], sf), zf)), 0.f), 255.f);
-      if (d < D) dst[kv ? v_off(slot, d, D, true, a.bs) : k_off(slot, d, D, true, a.bs)] = (uint8_t)r;
+      if (d < D) dst[a.page_layout == kPagesRowMajor ? slot * D + d
+                    : kv ? v_off(slot, d, D, true, a.bs) : k_off(slot, d, D, true, a.bs)] = (uint8_t)r;
     }
     if (lane == 0) {
       uint16_t* sz = reinterpret_cast<uint16_t*>(kv ? a.vsz : a.ksz) +

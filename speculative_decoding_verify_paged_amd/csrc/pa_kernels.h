@@ -8,6 +8,7 @@
 namespace pav {
 
 enum : int { kF16 = 0, kBF16 = 1, kU8 = 2 };
+enum : int { kPagesTiled = 0, kPagesRowMajor = 1 };   // values of pa_page_layout
 
 constexpr int kKeysPerStep = 32;     // keys one wavefront consumes per iteration
 constexpr int kRows = 16;            // stacked query rows per MFMA tile (one row block)
@@ -44,6 +45,7 @@ struct SegmentArgs {
   int32_t target_items;              // work-list chunks per KV head the chunk size aims at
   int32_t max_sps;                   // most steps whose block ids fit the LDS table
   float scale_log2;                  // scale * log2(e)
+  int32_t page_layout;               // kPagesTiled or kPagesRowMajor
 };
 
 struct AppendArgs {
@@ -58,6 +60,7 @@ struct AppendArgs {
   const int32_t* sb;
   int32_t* status;                   // sticky device status word
   int32_t num_seqs, num_tokens, Hkv, bs, mbps, num_blocks, max_q;
+  int32_t page_layout;               // kPagesTiled or kPagesRowMajor
 };
 
 struct CombineArgs {

@@ -447,9 +447,11 @@ __device__ __forceinline__ int wl_find(const SegmentArgs& a, int rows, int C, in
 // Segment kernel.  QT: dtype of q (and of the MFMA operands); KV: cache dtype
 // (QT, or kU8 for codes with per-token f16 scale and zero point); RB: 16-row
 // blocks of stacked query rows (G * T <= 16 * RB): each K/V operand a step
-// loads (and, for u8, converts) feeds one MFMA per row block.
+// loads (and, for u8, converts) feeds one MFMA per row block; HR: register
+// sets of the half-step path (0: whole steps); PL: page layout (kPagesTiled,
+// or kPagesRowMajor: every page [slot][d] for K and V).
 // ---------------------------------------------------------------------------
-template <int QT, int KV, int D, int BS, int NW, int WPE, int RB, int HR>
+template <int QT, int KV, int D, int BS, int NW, int WPE, int RB, int HR, int PL>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE)))
 void pa_segment(SegmentArgs a) {
   constexpr bool U8 = KV == kU8;
@@ -466,19 +468,49 @@ void pa_segment(SegmentArgs a) {
   __shared__ int s_bt[kSegSlots];
   __shared__ float s_m[NW][ROWS];
   __shared__ float s_l[NW][ROWS];
-  __shared__ __attribute__((aligned(16))) float s_o[NW][ROWS][OSTRIDE];
   __shared__ int s_bad;
   // Pages of fewer than 16 slots: K (and for 1 or 2 slots, V) is loaded as
   // whole page rows (1 KB per instruction) and turned into the MFMA operand
-  // layout through this per-wavefront LDS area, K first, then V: each
+  // layout through a per-wavefront LDS area, K first, then V: each
   // sub-tile's 16/BS pages, page-major, each padded by 16 B against bank
-  // conflicts.
+  // conflicts.  Row-major pages hold V [slot][d], while the PV operand wants
+  // four keys of one d per lane: their V sub-tiles (16 rows, each padded by
+  // 16 B) take the same path at every page size.  Row-major K of a 16-slot
+  // sub-tile is loaded straight into the operand order (16 B of the lane's
+  // slot row).
+  constexpr bool ROWV = PL == kPagesRowMajor;
   constexpr bool WIDE_K = BS < 16;
-  constexpr bool WIDE_V = BS <= 2;
+  constexpr bool WIDE_V = BS <= 2 || ROWV;
+  constexpr bool STAGE = WIDE_K || WIDE_V;
   constexpr int kPageBytes = BS * D * EB;                 // one page of one KV head (K or V)
   constexpr int kPagePad = kPageBytes + 16;
-  constexpr int kVtTau = (16 / BS) * kPagePad;           // one sub-tile
-  __shared__ __attribute__((aligned(16))) char s_vt[WIDE_K ? NW * 2 * kVtTau : 16];
+  constexpr int kRowPad = D * EB + 16;                    // staged row of a 16-slot sub-tile
+  constexpr int kVtTau = BS < 16 ? (16 / BS) * kPagePad : 16 * kRowPad;   // one sub-tile
+  // With row-major pages the staging area and the merge buffer share LDS
+  // (used one after the other, a barrier between).
+  constexpr bool ALIAS = ROWV;
+  constexpr size_t kSoBytes = (size_t)NW * ROWS * OSTRIDE * 4;
+  constexpr size_t kVtBytes = STAGE ? (size_t)NW * 2 * kVtTau : 16;
+  __shared__ __attribute__((aligned(16))) char s_obuf[ALIAS && kVtBytes > kSoBytes ? kVtBytes : kSoBytes];
+  __shared__ __attribute__((aligned(16))) char s_vtbuf[ALIAS ? 16 : kVtBytes];
+  auto& s_o = *reinterpret_cast<float (*)[NW][ROWS][OSTRIDE]>(s_obuf);
+  char* const s_vt = ALIAS ? s_obuf : s_vtbuf;
+  // byte of (sub-tile slot s, dim d) in a staged sub-tile: K pages are
+  // row-major within the page in both layouts, V pages too with row-major
+  // pages, d-major for tiled pages of fewer than 16 slots
+  auto staged_k = [&](int s, int d) {
+    if constexpr (BS >= 16) return s * kRowPad + d * EB;
+    else return (s / BS) * kPagePad + ((s % BS) * D + d) * EB;
+  };
+  auto staged_v = [&](int s, int d) {
+    if constexpr (BS >= 16 || ROWV) return staged_k(s, d);
+    else return (s / BS) * kPagePad + (d * BS + s % BS) * EB;
+  };
+  // staging offset of byte L of a sub-tile loaded as rows (1 KB per load)
+  auto stage_off = [&](int L) {
+    if constexpr (BS >= 16) return (L / (D * EB)) * kRowPad + L % (D * EB);
+    else return (L / kPageBytes) * kPagePad + L % kPageBytes;
+  };
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -812,9 +844,17 @@ void pa_segment(SegmentArgs a) {
   auto load_k = [&](int st, Step& r) {
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      const char* kp = kb + tile_of(st, tau) * D * EB + lane * 16;
+      if constexpr (ROWV) {
+        // row-major: lane (slot n16, group q4) reads 16 B of its slot's row
+        const char* kp = kb + (tile_of(st, tau) + n16) * D * EB;
 #pragma unroll
-      for (int c = 0; c < LK; ++c) r.k[tau][c] = ld16_stream(kp + c * 1024);
+        for (int c = 0; c < LK; ++c)
+          r.k[tau][c] = ld16_stream(kp + (U8 ? c * 64 + q4 * 16 : c * 32 + q4 * 8) * EB);
+      } else {
+        const char* kp = kb + tile_of(st, tau) * D * EB + lane * 16;
+#pragma unroll
+        for (int c = 0; c < LK; ++c) r.k[tau][c] = ld16_stream(kp + c * 1024);
+      }
     }
   };
   auto load_v = [&](int st, Step& r) {
@@ -863,25 +903,23 @@ void pa_segment(SegmentArgs a) {
   // LDS accesses across them.
   auto to_operands = [&](Step& r) {
     char* vt = s_vt + wave * 2 * kVtTau;
-    // K: lane (slot n16, group q4) takes the 16 B of its slot's row that a
-    // tiled sub-tile load would give it
+    if constexpr (WIDE_K) {
+      // K: lane (slot n16, group q4) takes the 16 B of its slot's row that a
+      // tiled sub-tile load would give it
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
+      for (int tau = 0; tau < 2; ++tau) {
 #pragma unroll
-      for (int c = 0; c < LK; ++c) {
-        const int L = c * 1024 + lane * 16;
-        *reinterpret_cast<u32x4*>(vt + tau * kVtTau + (L / kPageBytes) * kPagePad + L % kPageBytes) =
-            r.k[tau][c];
+        for (int c = 0; c < LK; ++c)
+          *reinterpret_cast<u32x4*>(vt + tau * kVtTau + stage_off(c * 1024 + lane * 16)) = r.k[tau][c];
       }
-    }
-    wait_lgkmcnt0();
+      wait_lgkmcnt0();
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
+      for (int tau = 0; tau < 2; ++tau) {
 #pragma unroll
-      for (int c = 0; c < LK; ++c) {
-        const int d0 = U8 ? c * 64 + q4 * 16 : c * 32 + q4 * 8;
-        r.k[tau][c] = *reinterpret_cast<const u32x4*>(vt + tau * kVtTau + (n16 / BS) * kPagePad +
-                                                       ((n16 % BS) * D + d0) * EB);
+        for (int c = 0; c < LK; ++c) {
+          const int d0 = U8 ? c * 64 + q4 * 16 : c * 32 + q4 * 8;
+          r.k[tau][c] = *reinterpret_cast<const u32x4*>(vt + tau * kVtTau + staged_k(n16, d0));
+        }
       }
     }
     if constexpr (!WIDE_V) return;
@@ -889,18 +927,14 @@ void pa_segment(SegmentArgs a) {
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
 #pragma unroll
-      for (int c = 0; c < LV; ++c) {
-        const int L = c * 1024 + lane * 16;
-        *reinterpret_cast<u32x4*>(vt + tau * kVtTau + (L / kPageBytes) * kPagePad + L % kPageBytes) =
-            r.v[tau][c];
-      }
+      for (int c = 0; c < LV; ++c)
+        *reinterpret_cast<u32x4*>(vt + tau * kVtTau + stage_off(c * 1024 + lane * 16)) = r.v[tau][c];
     }
     wait_lgkmcnt0();
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       const char* base = vt + tau * kVtTau;
-      // byte of (slot s of the sub-tile, dim d): page s / BS, element d * BS + s % BS
-      auto at = [&](int s, int d) { return base + (s / BS) * kPagePad + (d * BS + s % BS) * EB; };
+      auto at = [&](int s, int d) { return base + staged_v(s, d); };
       const int s0 = 4 * q4;
       if constexpr (U8) {
 #pragma unroll
@@ -909,7 +943,7 @@ void pa_segment(SegmentArgs a) {
           for (int jd = 0; jd < 4; ++jd) {
             const int d = c * 64 + jd * 16 + n16;
             uint32_t w;
-            if constexpr (BS == 2)
+            if constexpr (BS == 2 && !ROWV)                   // two adjacent slots per read
               w = *reinterpret_cast<const uint16_t*>(at(s0, d)) |
                   ((uint32_t)*reinterpret_cast<const uint16_t*>(at(s0 + 2, d)) << 16);
             else
@@ -918,6 +952,9 @@ void pa_segment(SegmentArgs a) {
                   ((uint32_t)*reinterpret_cast<const uint8_t*>(at(s0 + 2, d)) << 16) |
                   ((uint32_t)*reinterpret_cast<const uint8_t*>(at(s0 + 3, d)) << 24);
             r.v[tau][c][jd] = w;
+            // row-major pages: four byte reads per word; keep the scheduler
+            // from hoisting all of a step's reads (their temporaries spill)
+            if constexpr (ROWV) __builtin_amdgcn_sched_barrier(0);
           }
         }
       } else {
@@ -927,7 +964,7 @@ void pa_segment(SegmentArgs a) {
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const int d = dp * 32 + hh * 16 + n16;
-            if constexpr (BS == 2) {
+            if constexpr (BS == 2 && !ROWV) {                 // two adjacent slots per read
               w[2 * hh] = *reinterpret_cast<const uint32_t*>(at(s0, d));
               w[2 * hh + 1] = *reinterpret_cast<const uint32_t*>(at(s0 + 2, d));
             } else {
@@ -938,13 +975,14 @@ void pa_segment(SegmentArgs a) {
             }
           }
           r.v[tau][dp] = u32x4{w[0], w[1], w[2], w[3]};
+          if constexpr (ROWV) __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
   };
 
   auto compute_step = [&](int st, Step& r) {
-    if constexpr (WIDE_K) to_operands(r);
+    if constexpr (STAGE) to_operands(r);
     const int key0 = si.base + st * kKeysPerStep;
     // S^T for both sub-tiles: lane (row, q4) gets keys key0 + 16*tau + 4*q4 + 0..3
     float sv[RB][8];
@@ -1335,6 +1373,9 @@ void pa_segment(SegmentArgs a) {
     }
   }
 
+  // the merge buffer reuses the staging area: every wavefront is done with it
+  if constexpr (ALIAS) __syncthreads();
+
   // Row sums: each lane group holds a quarter of the keys.  Then merge the
   // wavefronts of the workgroup: M = max_w m_w, then sum the partials
   // rescaled by 2^(m_w - M), in a fixed order (bitwise repeatable).
@@ -1406,44 +1447,59 @@ void pa_segment(SegmentArgs a) {
 // Launchers: one instance per (q dtype, cache dtype, D, block size, row
 // blocks); each pa_segment_*.hip instantiates one cache dtype.
 // ---------------------------------------------------------------------------
-template <int QT, int KV, int D, int BS, int RB>
+template <int QT, int KV, int D, int BS, int RB, int PL>
 hipError_t launch_seg(const SegmentArgs& a, dim3 grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   constexpr SegConfig c = seg_config(KV, D, RB, BS);
   static_assert(c.waves_per_group <= 4 * c.waves_per_simd, "a workgroup must fit on one CU");
-  constexpr auto kern = pa_segment<QT, KV, D, BS, c.waves_per_group, c.waves_per_simd, RB, c.half_ring>;
+  // the half-step path reads tiled pages only
+  constexpr int HR = PL == kPagesTiled ? c.half_ring : 0;
+  constexpr auto kern = pa_segment<QT, KV, D, BS, c.waves_per_group, c.waves_per_simd, RB, HR, PL>;
   return launch_kernel(reinterpret_cast<const void*>(kern), grid, dim3(c.waves_per_group * kWave),
                        st, a, ev0, ev1);
 }
 
-template <int QT, int KV, int D, int BS>
+template <int QT, int KV, int D, int BS, int PL>
 hipError_t dispatch_rb(const SegmentArgs& a, int rb, dim3 grid, hipStream_t st, hipEvent_t e0,
                        hipEvent_t e1) {
   switch (rb) {
-    case 1: return launch_seg<QT, KV, D, BS, 1>(a, grid, st, e0, e1);
+    case 1: return launch_seg<QT, KV, D, BS, 1, PL>(a, grid, st, e0, e1);
     case 2:
-      if constexpr (BS >= 16 && max_row_blocks(KV, D) >= 2) return launch_seg<QT, KV, D, BS, 2>(a, grid, st, e0, e1);
+      if constexpr (BS >= 16 && max_row_blocks(KV, D) >= 2) return launch_seg<QT, KV, D, BS, 2, PL>(a, grid, st, e0, e1);
       break;
     case 3:
-      if constexpr (BS >= 16 && max_row_blocks(KV, D) >= 3) return launch_seg<QT, KV, D, BS, 3>(a, grid, st, e0, e1);
+      if constexpr (BS >= 16 && max_row_blocks(KV, D) >= 3) return launch_seg<QT, KV, D, BS, 3, PL>(a, grid, st, e0, e1);
       break;
     case 4:
-      if constexpr (BS >= 16 && max_row_blocks(KV, D) >= 4) return launch_seg<QT, KV, D, BS, 4>(a, grid, st, e0, e1);
+      if constexpr (BS >= 16 && max_row_blocks(KV, D) >= 4) return launch_seg<QT, KV, D, BS, 4, PL>(a, grid, st, e0, e1);
       break;
   }
   return hipErrorInvalidValue;
 }
 
-template <int QT, int KV, int D>
+template <int QT, int KV, int D, int PL>
 hipError_t dispatch_bs(const SegmentArgs& a, int bs, int rb, dim3 grid, hipStream_t st,
                        hipEvent_t e0, hipEvent_t e1) {
   switch (bs) {
-    case 1: return dispatch_rb<QT, KV, D, 1>(a, rb, grid, st, e0, e1);
-    case 2: return dispatch_rb<QT, KV, D, 2>(a, rb, grid, st, e0, e1);
-    case 4: return dispatch_rb<QT, KV, D, 4>(a, rb, grid, st, e0, e1);
-    case 8: return dispatch_rb<QT, KV, D, 8>(a, rb, grid, st, e0, e1);
-    case 16: return dispatch_rb<QT, KV, D, 16>(a, rb, grid, st, e0, e1);
-    case 32: return dispatch_rb<QT, KV, D, 32>(a, rb, grid, st, e0, e1);
-    case 64: return dispatch_rb<QT, KV, D, 64>(a, rb, grid, st, e0, e1);
+    case 1:
+      // a 1-slot page is the same in both layouts
+      return dispatch_rb<QT, KV, D, 1, kPagesTiled>(a, rb, grid, st, e0, e1);
+    case 2: return dispatch_rb<QT, KV, D, 2, PL>(a, rb, grid, st, e0, e1);
+    case 4: return dispatch_rb<QT, KV, D, 4, PL>(a, rb, grid, st, e0, e1);
+    case 8: return dispatch_rb<QT, KV, D, 8, PL>(a, rb, grid, st, e0, e1);
+    case 16: return dispatch_rb<QT, KV, D, 16, PL>(a, rb, grid, st, e0, e1);
+    case 32: return dispatch_rb<QT, KV, D, 32, PL>(a, rb, grid, st, e0, e1);
+    case 64: return dispatch_rb<QT, KV, D, 64, PL>(a, rb, grid, st, e0, e1);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int QT, int KV, int PL>
+hipError_t dispatch_d_pl(const SegmentArgs& a, int D, int bs, int rb, dim3 grid, hipStream_t st,
+                         hipEvent_t e0, hipEvent_t e1) {
+  switch (D) {
+    case 64: return dispatch_bs<QT, KV, 64, PL>(a, bs, rb, grid, st, e0, e1);
+    case 128: return dispatch_bs<QT, KV, 128, PL>(a, bs, rb, grid, st, e0, e1);
+    case 256: return dispatch_bs<QT, KV, 256, PL>(a, bs, rb, grid, st, e0, e1);
   }
   return hipErrorInvalidValue;
 }
@@ -1451,12 +1507,9 @@ hipError_t dispatch_bs(const SegmentArgs& a, int bs, int rb, dim3 grid, hipStrea
 template <int QT, int KV>
 hipError_t dispatch_d(const SegmentArgs& a, int D, int bs, int rb, dim3 grid, hipStream_t st,
                       hipEvent_t e0, hipEvent_t e1) {
-  switch (D) {
-    case 64: return dispatch_bs<QT, KV, 64>(a, bs, rb, grid, st, e0, e1);
-    case 128: return dispatch_bs<QT, KV, 128>(a, bs, rb, grid, st, e0, e1);
-    case 256: return dispatch_bs<QT, KV, 256>(a, bs, rb, grid, st, e0, e1);
-  }
-  return hipErrorInvalidValue;
+  if (a.page_layout == kPagesRowMajor)
+    return dispatch_d_pl<QT, KV, kPagesRowMajor>(a, D, bs, rb, grid, st, e0, e1);
+  return dispatch_d_pl<QT, KV, kPagesTiled>(a, D, bs, rb, grid, st, e0, e1);
 }
 
 }  // namespace pav

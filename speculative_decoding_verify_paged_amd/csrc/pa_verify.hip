@@ -76,6 +76,7 @@ int validate(const pa_verify_params* p, int32_t max_ctx, bool u8_entry) {
       (int64_t)pav::kRows * pav::max_row_blocks(p->kv_dtype, p->head_dim, p->block_size))
     return PA_ERR_UNSUPPORTED;
   if (p->tree_mask && p->sliding_window > 0) return PA_ERR_UNSUPPORTED;
+  if (p->page_layout != PA_PAGES_TILED && p->page_layout != PA_PAGES_ROW_MAJOR) return PA_ERR_INVALID_ARG;
   return PA_OK;
 }
 
@@ -301,6 +302,7 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
   a.target_items = pl.target_items;
   a.max_sps = pav::max_steps_per_segment(p->block_size);
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.page_layout = p->page_layout;
 
   hipStream_t st = static_cast<hipStream_t>(p->stream);
   hipEvent_t e0 = static_cast<hipEvent_t>(p->prof_event_begin);
@@ -372,6 +374,7 @@ int run_append(const void* k_new, const void* v_new, void* k, void* v, void* ksz
   a.mbps = p->max_blocks_per_seq;
   a.num_blocks = p->num_blocks;
   a.max_q = (int32_t)query_bound(p);
+  a.page_layout = p->page_layout;
   const hipError_t e = pav::launch_append(a, p->q_dtype, p->kv_dtype, p->head_dim,
                                           static_cast<hipStream_t>(p->stream));
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;

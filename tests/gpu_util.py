@@ -50,7 +50,8 @@ def run_gpu(case: pi.Case, dev=None, *, num_segments=0, out=None, max_context_le
     mcl = case.max_context_len if max_context_len is None else max_context_len
     mql = max(case.Ts) if max_query_len is None else max_query_len
     common = dict(sliding_window=case.sliding_window, num_segments=num_segments,
-                  max_query_len=mql, tree_mask=dev.get("tree_mask"), **kw)
+                  max_query_len=mql, tree_mask=dev.get("tree_mask"),
+                  page_layout=getattr(case, "page_layout", 0), **kw)
     if case.kv_dtype == pi.U8:
         o = pav.pa_verify_forward_u8(dev["q"], dev["k_cache"], dev["v_cache"], dev["k_scale_zp"],
                                      dev["v_scale_zp"], dev["block_tables"], dev["past_lens"],

@@ -31,6 +31,9 @@ What pins what:
                   equals the causal rows bitwise; a mask without the row's own
                   bit changes nothing; causal rows with up to 16 new tokens
                   against SDPA.
+  * layout      — row-major pages: the same logical cache as tiled pages
+                  gives the same output bit for bit and matches torch SDPA;
+                  appends write the same logical cache in either layout.
   * pairs       — the subset form (a list of (token, q head) rows, as the
                   sampled checks at large sizes use it) against torch SDPA on
                   the same rows, and bit for bit against the full output
@@ -414,8 +417,7 @@ def _blank_new_tokens(case, rng):
             kb[blk, :, slot] = rng.integers(0, 1 << 14, size=kb[blk, :, slot].shape)
             vb[blk, :, slot] = rng.integers(0, 1 << 14, size=vb[blk, :, slot].shape)
     blank = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
-    blank.k_cache = pi.tile_k(kb, u8).reshape(case.k_cache.shape)
-    blank.v_cache = pi.tile_v(vb, u8).reshape(case.v_cache.shape)
+    blank.k_cache, blank.v_cache = pi.pages_to_cache(kb, vb, u8, case.page_layout)
     return kn, vn, blank
 
 
@@ -520,6 +522,46 @@ def pin_pairs(orc):
     assert orc.run(pairs=np.array([[0, case.num_q_heads]], np.int32), **oracle_fields(case))[0] != 0
 
 
+def pin_layout(orc):
+    """Row-major pages hold the same logical cache as tiled ones: the output
+    is bit for bit the same, and matches torch SDPA; appends write the same
+    logical cache in either layout."""
+    rng = np.random.default_rng(37)
+    for case in tiny_random_cases(24, seed=41):
+        rm = pi.with_layout(case, pi.PAGES_ROW_MAJOR)
+        # the stored pages differ (a 1-slot page is the same in both layouts;
+        # pages under 16 slots hold K row-major in both)
+        same = np.array_equal(rm.k_cache, case.k_cache) and np.array_equal(rm.v_cache, case.v_cache)
+        assert rm.page_layout == 1 and (not same or case.block_size == 1), case.name
+        got = orc.forward(rm)
+        assert np.array_equal(got, orc.forward(case)), case.name
+        err = np.max(np.abs(got - sdpa_reference(rm)))
+        assert err <= 1e-12, f"{case.name} row-major: max err {err}"
+    for k, (kv, D, bs) in enumerate([(pi.F16, 64, 16), (pi.BF16, 32, 4), (pi.U8, 64, 32),
+                                     (pi.U8, 128, 2)]):
+        case = pi.build_case([820, k], [37, 3], [3, 2], num_q_heads=4, num_kv_heads=2,
+                             head_dim=D, block_size=bs, q_dtype=pi.F16 if kv == pi.U8 else kv,
+                             kv_dtype=kv, spare_blocks=1)
+        rm = pi.with_layout(case, pi.PAGES_ROW_MAJOR)
+        if kv == pi.U8:
+            kn = pi.f32_to_bits(rng.standard_normal((case.num_tokens, 2, D)), pi.F16)
+            vn = pi.f32_to_bits(rng.standard_normal((case.num_tokens, 2, D)), pi.F16)
+            nd = pi.F16
+        else:
+            kn, vn, _ = _blank_new_tokens(case, rng)
+            nd = kv
+        st1, k1, v1, ks1, vs1 = orc.kv_append(case, kn, vn, nd)
+        st2, k2, v2, ks2, vs2 = orc.kv_append(rm, kn, vn, nd)
+        assert st1 == 0 and st2 == 0
+        done1 = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+        done1.k_cache, done1.v_cache, done1.k_scale_zp, done1.v_scale_zp = k1, v1, ks1, vs1
+        done2 = pi.Case(**{f: getattr(rm, f) for f in rm.__dataclass_fields__})
+        done2.k_cache, done2.v_cache, done2.k_scale_zp, done2.v_scale_zp = k2, v2, ks2, vs2
+        l1, l2 = done1.logical_pages(), done2.logical_pages()
+        assert np.array_equal(l1[0], l2[0]) and np.array_equal(l1[1], l2[1]), k
+        assert np.array_equal(orc.forward(done1), orc.forward(done2)), k
+
+
 def oracle_fields(case):
     import oracle
     return oracle.case_fields(case)
@@ -529,4 +571,5 @@ ALL_PINS = {
     "sdpa": pin_sdpa, "hand": pin_hand, "closed": pin_closed, "rows": pin_rows,
     "permutation": pin_permutation, "window": pin_window, "gqa": pin_gqa, "u8": pin_u8,
     "ragged": pin_ragged, "tree": pin_tree, "append": pin_append, "pairs": pin_pairs,
+    "layout": pin_layout,
 }

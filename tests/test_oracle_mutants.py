@@ -38,9 +38,9 @@ MUTANTS = [
                                  ("sz[2 * srow + 1] = zb;", "sz[2 * srow + 1] = sb;")]),
     ("tree_first_row_mask", [("return j == i || ((a->tree_mask[n] >> j) & 1u);",
                               "return j == i || ((a->tree_mask[n - i] >> j) & 1u);")]),
-    ("v_read_in_k_layout", [("const size_t vidx = page + v_offset(slot, d, D, u8, bs);",
-                             "const size_t vidx = page + k_offset(slot, d, D, u8, bs);")]),
-    ("k_page_row_major", [("page + k_offset(slot, d, D, u8, bs), row);",
+    ("v_read_in_k_layout", [("const size_t vidx = page + v_offset(slot, d, D, u8, bs, a->page_layout);",
+                             "const size_t vidx = page + k_offset(slot, d, D, u8, bs, a->page_layout);")]),
+    ("k_page_row_major", [("page + k_offset(slot, d, D, u8, bs, a->page_layout), row);",
                            "page + (size_t)slot * D + d, row);")]),
     ("v_slot_quads_swapped", [("return ((((st * (D / 32) + d / 32) * 4 + qq) * 16 + d % 16) * 2 + (d % 32) / 16) * 4 + slot % 4;",
                                "return ((((st * (D / 32) + d / 32) * 4 + slot % 4) * 16 + d % 16) * 2 + (d % 32) / 16) * 4 + qq;")]),
@@ -60,19 +60,23 @@ MUTANTS = [
     ("bf16_shift", [("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;")]),
     ("q_head_major_layout", [("const size_t q_off = ((size_t)n * Hq + h) * D;",
                               "const size_t q_off = ((size_t)h * a->num_tokens + n) * D;")]),
-    ("k_dims_reversed", [("page + k_offset(slot, d, D, u8, bs), row);",
-                          "page + k_offset(slot, D - 1 - d, D, u8, bs), row);")]),
+    ("k_dims_reversed", [("page + k_offset(slot, d, D, u8, bs, a->page_layout), row);",
+                          "page + k_offset(slot, D - 1 - d, D, u8, bs, a->page_layout), row);")]),
     # the subset form (rows given as (token, q head) pairs); the indices are
     # reduced into range so the mistake stays in bounds
     ("pairs_token_head_swapped", [("n = a->pairs[2 * it];\n      h = a->pairs[2 * it + 1];",
                                    "n = a->pairs[2 * it + 1] % a->num_tokens;\n"
                                    "      h = a->pairs[2 * it] % a->num_q_heads;")]),
+    ("rowmajor_v_read_d_major", [("static size_t v_offset(int slot, int d, int D, int u8, int bs, int layout) {\n  if (layout == 1) return (size_t)slot * D + d;",
+                                  "static size_t v_offset(int slot, int d, int D, int u8, int bs, int layout) {\n  if (layout == 1) return (size_t)d * bs + slot;")]),
+    ("rowmajor_ignored", [("static size_t k_offset(int slot, int d, int D, int u8, int bs, int layout) {\n  if (layout == 1) return (size_t)slot * D + d;",
+                           "static size_t k_offset(int slot, int d, int D, int u8, int bs, int layout) {\n  if (layout == 9) return (size_t)slot * D + d;")]),
     ("pairs_first_item_only", [("n = a->pairs[2 * it];\n      h = a->pairs[2 * it + 1];",
                                 "n = a->pairs[0];\n      h = a->pairs[1];")]),
 ]
 
 PIN_ORDER = ["hand", "closed", "rows", "window", "gqa", "u8", "permutation", "ragged", "sdpa", "tree",
-             "append", "pairs"]
+             "append", "pairs", "layout"]
 
 
 def _source():

@@ -590,10 +590,10 @@ def _append_gpu(case, kn, vn, new_dtype, max_query_len=None, table=None):
     if case.kv_dtype == pi.U8:
         pav.pa_kv_append_u8(k_new, v_new, dev["k_cache"], dev["v_cache"], dev["k_scale_zp"],
                             dev["v_scale_zp"], bt, dev["past_lens"], dev["subsequence_begins"],
-                            max_query_len=mql)
+                            max_query_len=mql, page_layout=case.page_layout)
     else:
         pav.pa_kv_append(k_new, v_new, dev["k_cache"], dev["v_cache"], bt, dev["past_lens"],
-                         dev["subsequence_begins"], max_query_len=mql)
+                         dev["subsequence_begins"], max_query_len=mql, page_layout=case.page_layout)
     torch.cuda.synchronize()
 
     def host(t):
@@ -847,3 +847,76 @@ def test_u8_f16q_v_scale_overflow_is_loud():
     assert pav.pa_verify_read_status() == pav.PA_ERR_DEVICE_CONTRACT
     assert np.all(np.isnan(got))
     assert pav.pa_verify_read_status() == pav.PA_OK
+
+
+# ---------------------------------------------------------------------------
+# Row-major pages (page_layout = PA_PAGES_ROW_MAJOR): the conventional
+# [num_blocks, Hkv, block_size, D] cache, read without a repack
+# ---------------------------------------------------------------------------
+def test_row_major_pages_all_instances():
+    rng = np.random.default_rng(1710)
+    k = 0
+    for bs in (2, 4, 8, 16, 32, 64):
+        for D in (64, 128, 256):
+            for kv in (pi.F16, pi.BF16, pi.U8):
+                qd = kv if kv != pi.U8 else (pi.F16 if k % 2 == 0 else pi.BF16)
+                G = int(rng.choice([1, 2, 4]))
+                rows = 16 if bs < 16 else _max_rows(kv, D, bs)
+                T = int(rng.integers(1, max(1, min(16, rows // G)) + 1))
+                L = int(rng.choice([0, 3, 31, 70, int(rng.integers(0, 1500))]))
+                W = int(rng.choice([0, 0, 5, 100]))
+                case = pi.build_case([1711, k], [L], [T], num_q_heads=2 * G, num_kv_heads=2,
+                                     head_dim=D, block_size=bs, q_dtype=qd, kv_dtype=kv,
+                                     sliding_window=W, spare_blocks=3, poison=True,
+                                     page_layout=pi.PAGES_ROW_MAJOR,
+                                     name=f"rowmajor_page{bs}_D{D}_kv{kv}_G{G}_T{T}_L{L}_W{W}")
+                _full(case, rounding_aware=True)
+                k += 1
+
+
+@pytest.mark.parametrize("name", ["c2_32k_T3", "c2_8k_T4_tree", "c3_u8", "c4_global", "c4_window",
+                                  "c5_ragged"])
+def test_row_major_workloads(name):
+    """The five workloads' shapes with row-major pages: against the oracle,
+    and within the bar of the tiled call on the same logical cache."""
+    mk = {"c2_32k_T3": lambda: pi.config2(32768, 3),
+          "c2_8k_T4_tree": lambda: pi.config2(8192, 4, tree=True, poison=True),
+          "c3_u8": lambda: pi.config3(32768, 3, poison=True),
+          "c4_global": lambda: pi.config4(32768, window=0),
+          "c4_window": lambda: pi.config4(32768, window=1024, poison=True),
+          "c5_ragged": lambda: pi.config5(poison=True)}[name]
+    tiled = mk()
+    rm = pi.with_layout(tiled, pi.PAGES_ROW_MAJOR)
+    got, ref = _full(rm)
+    assert max_err(to_f64(got), to_f64(run_gpu(tiled))) <= 2 * tol(tiled)
+
+
+def test_row_major_append_and_verify():
+    """Appends into row-major caches match the oracle bit for bit, and a
+    verify call over the result matches the oracle."""
+    from oracle_pins import _blank_new_tokens
+    rng = np.random.default_rng(1720)
+    for k, (kv, D, bs, Ls, Ts) in enumerate([(pi.F16, 128, 16, [8190], [3]),
+                                             (pi.BF16, 256, 64, [5, 3000], [2, 4]),
+                                             (pi.F16, 64, 4, [0, 17, 400], [8, 1, 5])]):
+        case = pi.build_case([1721, k], Ls, Ts, num_q_heads=8, num_kv_heads=2, head_dim=D,
+                             block_size=bs, q_dtype=kv, kv_dtype=kv, spare_blocks=2,
+                             page_layout=pi.PAGES_ROW_MAJOR)
+        kn, vn, blank = _blank_new_tokens(case, rng)
+        k2, v2, _, _ = _append_gpu(blank, kn, vn, kv)
+        assert np.array_equal(k2, case.k_cache) and np.array_equal(v2, case.v_cache), k
+    for k, (qd, D, bs, Ls, Ts) in enumerate([(pi.F16, 256, 16, [30000], [3]),
+                                             (pi.BF16, 128, 8, [0, 700], [4, 2])]):
+        case = pi.build_case([1722, k], Ls, Ts, num_q_heads=8, num_kv_heads=2, head_dim=D,
+                             block_size=bs, q_dtype=qd, kv_dtype=pi.U8, spare_blocks=2,
+                             page_layout=pi.PAGES_ROW_MAJOR)
+        kf = pi.f32_to_bits(rng.standard_normal((case.num_tokens, 2, D)), qd)
+        vf = pi.f32_to_bits(rng.standard_normal((case.num_tokens, 2, D)), qd)
+        st, k_o, v_o, ks_o, vs_o = oracle.get().kv_append(case, kf, vf, qd)
+        assert st == 0
+        k2, v2, ks2, vs2 = _append_gpu(case, kf, vf, qd)
+        assert np.array_equal(k2, k_o) and np.array_equal(v2, v_o), k
+        assert np.array_equal(ks2, ks_o) and np.array_equal(vs2, vs_o), k
+        done = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+        done.k_cache, done.v_cache, done.k_scale_zp, done.v_scale_zp = k_o, v_o, ks_o, vs_o
+        _full(done, rounding_aware=True)
