@@ -66,6 +66,13 @@ def workloads():
         "swa_pair_global_L51200": lambda T: pi.config4(51200, window=0, T=T),
         "swa_pair_window1024_L32768": lambda T: pi.config4(32768, window=1024, T=T),
         "ragged8_bf16": lambda T: pi.config5(),
+        # batches of many sequences (fixed per-sequence segments: more
+        # sequences than workgroup slots per KV head): past_len log-uniform,
+        # shorter as the batch grows, T uniform in 1..4, bf16, 32 q / 8 KV
+        # heads, head_dim 128, 16-slot pages
+        "batch64_bf16": lambda T: pi.config5(num_seqs=64, lo=256, hi=4096, spare_blocks=8),
+        "batch512_bf16": lambda T: pi.config5(num_seqs=512, lo=64, hi=1024, spare_blocks=8),
+        "batch4096_bf16": lambda T: pi.config5(num_seqs=4096, lo=16, hi=256, spare_blocks=8),
     }
 
 

@@ -150,7 +150,8 @@ typedef struct pa_verify_params {
                                   Sizes the kernel's row blocks (G * bound rows, in blocks
                                   of 16), so pass the real bound (the draft length) */
   void* workspace;             /* device scratch >= pa_verify_workspace_bytes; its first 4 bytes
-                                  are the sticky device status word: zero them once at allocation */
+                                  are the sticky device status word: zero them once at allocation
+                                  (the rest is rewritten by every call) */
   size_t workspace_bytes;
   void* stream;                /* hipStream_t to enqueue on; NULL = the null stream */
   void* prof_event_begin;      /* optional hipEvent_t stamped when the segment kernel starts */

@@ -37,14 +37,11 @@ __global__ __launch_bounds__(kWave) void pa_combine(CombineArgs a) {
   }
   const int lane = threadIdx.x & (kWave - 1);
   const int col = slice * kWave + lane;
-  const int n = pair / a.Hq;
   const int S = a.seg.S;
 
-  // subsequence_begins, 64 entries per lane step: its first chunk goes out
-  // with the partial loads
-  const int nseq = a.seg.num_seqs;
-  const int sb_next = lane < nseq ? a.seg.sb[lane + 1] : 0;
-  const int sb_this = lane < nseq ? a.seg.sb[lane] : 0;
+  // the segment kernel's verdict on subsequence_begins (one word per
+  // wavefront of its workgroup 0): it goes out with the partial loads
+  const int sb_bad = lane < a.seg.sb_words ? a.seg.sb_check[lane] : 0;
 
   // Every segment of a valid sequence wrote its (m, l) (empty ones as
   // (-inf, 0)); a segment in which the row saw no key left its O unwritten,
@@ -105,27 +102,9 @@ __global__ __launch_bounds__(kWave) void pa_combine(CombineArgs a) {
   }
 
   // subsequence_begins must start at 0, never decrease and end at
-  // num_tokens; then token n belongs to the first s with n < sb[s + 1].  A
+  // num_tokens; then every token belongs to exactly one sequence.  A
   // sequence that breaks the rest of the contract left NaN in its partials.
-  bool ok = true;
-  int s = -1;
-  {
-    ok &= !__any(lane < nseq && sb_this > sb_next);
-    ok &= __builtin_amdgcn_readlane(sb_this, 0) == 0;
-    if (nseq <= kWave) ok &= __builtin_amdgcn_readlane(sb_next, nseq - 1) == a.seg.num_tokens;
-    const unsigned long long hit = __ballot(lane < nseq && n < sb_next);
-    if (hit) s = __builtin_ctzll(hit);
-  }
-  for (int b = kWave; b < nseq; b += kWave) {                 // more than 64 sequences
-    const int k = b + lane;
-    const int nx = k < nseq ? a.seg.sb[k + 1] : 0;
-    const int th = k < nseq ? a.seg.sb[k] : 0;
-    ok &= !__any(k < nseq && th > nx);
-    if (b + kWave >= nseq) ok &= __builtin_amdgcn_readlane(nx, nseq - 1 - b) == a.seg.num_tokens;
-    const unsigned long long hit = __ballot(k < nseq && n < nx);
-    if (s < 0 && hit) s = b + __builtin_ctzll(hit);
-  }
-  ok &= s >= 0;
+  const bool ok = !__any(sb_bad != 0);
   const bool bad = __any(nan_seen) || !ok;
   if (bad && threadIdx.x == 0) atomicExch(a.seg.status, kDeviceContract);
   float res[CPL];

@@ -37,6 +37,10 @@ struct SegmentArgs {
   float* ws_o;                       // [num_tokens, Hq, S, D] unnormalised partial outputs
   float* ws_ml;                      // [num_tokens, Hq, S, 2] (max in log2 units, sum)
   int32_t* status;                   // sticky device status word
+  // [sb_words] one word per wavefront of segment workgroup 0, nonzero when
+  // subsequence_begins breaks its contract (read by the combine kernel)
+  int32_t* sb_check;
+  int32_t sb_words;
   int32_t num_seqs, num_tokens, Hq, Hkv, G;
   int32_t num_blocks, mbps, window, max_ctx;
   int32_t max_q;                     // bound on T_s the host planned for (<= kMaxT)
@@ -92,6 +96,13 @@ hipError_t launch_append(const AppendArgs& a, int q_dtype, int kv_dtype, int D, 
 // the seg_block_slots(bs)-entry LDS table.
 constexpr int max_steps_per_segment(int bs) { return (seg_block_slots(bs) - 2) * bs / kKeysPerStep; }
 
+// Work-list batches hold 2 .. kWlSeqs sequences: every wavefront keeps their
+// metadata in registers, kWlCached lane-strided groups of 64.
+constexpr int kWlCached = 4;
+constexpr int kWlSeqs = kWlCached * 64;
+// the work list's exact float ceiling division needs chunk sizes below 2^16
+static_assert(max_steps_per_segment(64) < 65536, "chunk sizes must stay below 2^16");
+
 // Combine grid: one 64-thread workgroup per (token, q head) row and 64-column
 // slice of it (same-box A/B, us per call: see the combine kernel).
 constexpr int combine_slices(int D) { return D / 64; }
@@ -103,11 +114,11 @@ constexpr int combine_slices(int D) { return D / 64; }
 // SIMDs per CU) and the wavefronts per workgroup.  Measured on MI355X at 32k
 // context:
 // head_dim 128 (16-bit) and u8 head_dim 256 run best as one 8-wavefront
-// workgroup per CU, two wavefronts per SIMD with one step each (C2 shape
-// 27.6 vs 28.2 µs per call for 4 wavefronts with two steps each; u8 21.4 vs
+// workgroup per CU, two wavefronts per SIMD with one step each (32 q / 8 KV
+// heads, T = 3: 27.6 vs 28.2 µs per call for 4 wavefronts with two steps each; u8 21.4 vs
 // 22.5 µs) — two workgroups of 4 instead would double the partials the
-// combine reads.  The same holds elsewhere (C2-shaped calls at 32k, µs per
-// call): head_dim 64 as two 8-wavefront workgroups per CU at four
+// combine reads.  The same holds elsewhere (32 q / 8 KV heads, T = 3, at
+// 32k, µs per call): head_dim 64 as two 8-wavefront workgroups per CU at four
 // wavefronts per SIMD, 17.4 vs 17.7 for four 4-wavefront ones (one
 // 16-wavefront one: 18.6); u8 head_dim 128 (16 q / 4 KV heads) as one
 // 8-wavefront workgroup at two per SIMD, 14.5 vs 15.4 for one 4-wavefront
@@ -133,7 +144,8 @@ struct SegConfig {
 // or head_dim 64 (16.54 -> 17.05).
 constexpr SegConfig seg_config(int kv_dtype, int D, int rb, int bs = 16) {
   // Pages of fewer than 16 slots: one 8-wavefront workgroup per CU as for
-  // 16-slot pages (C2 shape at 32k, us per call: 2 slots 29.8 vs 29.9 for two
+  // 16-slot pages (32 q / 8 KV heads, head_dim 128, T = 3 at 32k, us per
+  // call: 2 slots 29.8 vs 29.9 for two
   // 4-wavefront groups, 4 slots 27.6 vs 28.1, 8 slots 27.8 vs 28.0).
   if (bs < 16) return D >= 256 ? SegConfig{1, 1} : SegConfig{2, 1, 8};
   if (rb > 1) return (rb == 2 && D <= 128) || D <= 64 ? SegConfig{2, 1, 8} : SegConfig{1, 1};

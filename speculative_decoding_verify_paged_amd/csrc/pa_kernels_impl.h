@@ -308,87 +308,167 @@ struct SeqInfo {
 };
 
 // rows: stacked query rows the kernel instance holds (G * T must fit).
-__device__ __forceinline__ SeqInfo seq_info(const SegmentArgs& a, int s, int rows) {
+// b0, b1: subsequence_begins[s], [s + 1]; L: past_lens[s].
+__device__ __forceinline__ SeqInfo seq_decode(const SegmentArgs& a, int b0, int b1, int L, int rows) {
   SeqInfo q;
-  q.b0 = a.sb[s];
-  const int b1 = a.sb[s + 1];
-  q.T = b1 - q.b0;
-  q.L = a.past_lens[s];
-  q.ok = q.b0 >= 0 && b1 <= a.num_tokens && q.T >= 1 && q.T <= a.max_q && q.L >= 0 &&
-         (int64_t)q.L + q.T <= a.max_ctx && a.G * q.T <= rows;
-  q.ctx = q.L + q.T;
-  q.lo0 = a.window > 0 ? max(0, q.L + 1 - a.window) : 0;
+  q.b0 = b0;
+  q.T = b1 - b0;
+  q.L = L;
+  q.ok = b0 >= 0 && b1 <= a.num_tokens && q.T >= 1 && q.T <= a.max_q && L >= 0 &&
+         (int64_t)L + q.T <= a.max_ctx && a.G * q.T <= rows;
+  q.ctx = L + q.T;
+  q.lo0 = a.window > 0 ? max(0, L + 1 - a.window) : 0;
   q.base = (q.lo0 / kKeysPerStep) * kKeysPerStep;
   q.n_steps = q.ok ? (q.ctx - q.base + kKeysPerStep - 1) / kKeysPerStep : 0;
   return q;
 }
+__device__ __forceinline__ SeqInfo seq_info(const SegmentArgs& a, int s, int rows) {
+  return seq_decode(a, a.sb[s], a.sb[s + 1], a.past_lens[s], rows);
+}
+
+// ceil(n / c) for 0 <= n < 2^26 and 1 <= c < 2^16, exact; rc = rcp(c).  A
+// float estimate q0 of floor(m / c), m = n + c - 1, is within 60 of it; the
+// remainder m - q0 c (exact in float) then gives the rest to within one,
+// and one integer comparison settles it.
+__device__ __forceinline__ int ceil_div_small(int n, int c, float rc) {
+  const int m = n + c - 1;
+  int q = (int)((float)m * rc);
+  q += (int)floorf((float)(m - q * c) * rc);
+  const int r = m - q * c;
+  return q + (r >= c) - (r < 0);
+}
+
+// inclusive prefix sum over the 64 lanes: DPP row shifts inside each 16-lane
+// row, then the totals of the rows before it (read from lanes 15, 31, 47)
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (int)(threadIdx.x & (kWave - 1)) >> 4;
+  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
 
 // ---------------------------------------------------------------------------
-// Work list of a batch of several sequences.  Every sequence's steps are cut
-// into chunks of C steps; C is the smallest size (not below the host's steps
-// per segment, nor above what the LDS block-id table holds) whose chunks of
-// all sequences fit the target count of workgroups per KV head, so one round
-// of equal workgroups covers the batch however its lengths are spread.  A
-// sequence that breaks the contract gets one chunk (it writes NaN partials).
-// Computed redundantly and identically by every wavefront of every workgroup
-// from the sequence metadata.  Wave-wide.
+// Work list of a batch of 2 .. kWlSeqs sequences (the planner gives larger
+// batches, and any batch whose sequences outnumber the target, fixed
+// per-sequence segments: every sequence then has a chunk of its own
+// whatever the chunk size, which is what those segments are).  Every
+// sequence's steps are cut into chunks of C steps; C is the smallest size
+// (not below the host's steps per segment, nor above what the LDS block-id
+// table holds) whose chunks of all sequences fit the target count of
+// workgroups per KV head, so one round of equal workgroups covers the batch
+// however its lengths are spread.  A sequence that breaks the contract gets
+// one chunk (it writes NaN partials).  Every wavefront of every workgroup
+// loads the batch's metadata once into registers (lane-strided, one request
+// per array) and computes the same C from them.  Wave-wide.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int wl_steps(const SegmentArgs& a, int seq, int rows, bool& ok) {
-  const SeqInfo q = seq_info(a, seq, rows);
-  ok = q.ok;
-  return q.n_steps;
-}
-
-// A sequence for the work list: its step count, -1 if it breaks the
-// contract (one chunk), -2 past the end of the batch (no chunk).
-__device__ __forceinline__ int wl_code(const SegmentArgs& a, int seq, int rows) {
-  if (seq >= a.num_seqs) return -2;
-  bool ok;
-  const int st = wl_steps(a, seq, rows, ok);
-  return ok ? st : -1;
-}
-__device__ __forceinline__ int wl_items(int code, int C) {
-  return code >= 0 ? (code + C - 1) / C : code == -1 ? 1 : 0;
-}
-
-// The codes of the batch's first kWlCached * 64 sequences, lane-strided,
-// kept in registers: the chunk-size search scans them once per candidate.
-constexpr int kWlCached = 4;
 struct WorkList {
-  int code[kWlCached];
+  int code[kWlCached];                 // steps; -1 breaks the contract; -2 past the batch
+  int b0[kWlCached], b1[kWlCached], L[kWlCached];
+  int P;                               // 64-lane groups holding sequences (uniform)
 };
 __device__ __forceinline__ WorkList wl_load(const SegmentArgs& a, int rows) {
   const int lane = threadIdx.x & (kWave - 1);
   WorkList w;
+  w.P = min((a.num_seqs + kWave - 1) / kWave, kWlCached);
 #pragma unroll
-  for (int p = 0; p < kWlCached; ++p) w.code[p] = wl_code(a, p * kWave + lane, rows);
+  for (int p = 0; p < kWlCached; ++p) {
+    const int s = p * kWave + lane;
+    const bool in = p < w.P && s < a.num_seqs;
+    w.b0[p] = in ? a.sb[s] : 0;
+    w.b1[p] = in ? a.sb[s + 1] : 0;
+    w.L[p] = in ? a.past_lens[s] : 0;
+  }
+#pragma unroll
+  for (int p = 0; p < kWlCached; ++p) {
+    const SeqInfo q = seq_decode(a, w.b0[p], w.b1[p], w.L[p], rows);
+    w.code[p] = p * kWave + lane >= a.num_seqs ? -2 : q.ok ? q.n_steps : -1;
+  }
   return w;
+}
+__device__ __forceinline__ int wl_items(int code, int C, float rc) {
+  return code >= 0 ? ceil_div_small(code, C, rc) : code == -1 ? 1 : 0;
 }
 
 // chunks of all sequences for chunk size C
-__device__ __forceinline__ int wl_count(const SegmentArgs& a, int rows, int C, const WorkList& w) {
-  const int lane = threadIdx.x & (kWave - 1);
+__device__ __forceinline__ int wl_count(int C, const WorkList& w) {
+  const float rc = __builtin_amdgcn_rcpf((float)C);
   int n = 0;
 #pragma unroll
-  for (int p = 0; p < kWlCached; ++p) n += wl_items(w.code[p], C);
-  for (int b = kWlCached * kWave; b < a.num_seqs; b += kWave) n += wl_items(wl_code(a, b + lane, rows), C);
+  for (int p = 0; p < kWlCached; ++p)
+    if (p < w.P) n += wl_items(w.code[p], C, rc);
   return wave_sum_i32(n);
 }
 
-__device__ __forceinline__ int wl_chunk(const SegmentArgs& a, int rows, const WorkList& w) {
+// sum over aligned groups of g lanes (g a power of two, uniform), every lane
+// of a group left with its group's total
+__device__ __forceinline__ int lane_group_sum(int v, int g) {
+  if (g > 1) v += (int)dpp_u32<kDppXor1>((uint32_t)v);
+  if (g > 2) v += (int)dpp_u32<kDppXor2>((uint32_t)v);
+  if (g > 4) v += (int)dpp_u32<kDppHalfMirror>((uint32_t)v);
+  if (g > 8) v += (int)dpp_u32<kDppMirror>((uint32_t)v);
+  if (g > 16) {
+    uint32_t x = (uint32_t)v, y = x;
+    swap16(x, y);
+    v = (int)(x + y);
+  }
+  if (g > 32) {
+    uint32_t x = (uint32_t)v, y = x;
+    swap32(x, y);
+    v = (int)(x + y);
+  }
+  return v;
+}
+
+// The smallest C in [lo, hi] whose chunks number at most `target`, given
+// that C = hi's do, for a batch of 2 .. 64 sequences (sequence i's code in
+// lane i): the wavefront splits into groups of g lanes (the sequence count
+// rounded up to a power of two), each holding a copy of the codes and
+// testing one candidate, so each round cuts the range into 64 / g + 1
+// parts instead of two.
+__device__ __forceinline__ int wl_search_small(int lo, int hi, int target, int num_seqs, int code0) {
   const int lane = threadIdx.x & (kWave - 1);
+  const int lg = 32 - __clz(num_seqs - 1);                  // log2 g
+  const int g = 1 << lg;
+  const int k = lane >> lg;                                 // this lane's candidate
+  const int kn = kWave >> lg;                               // candidates per round
+  const int code = __shfl(code0, lane & (g - 1), kWave);
+  const float inv = 1.0f / (float)(kn + 1);
+  while (lo < hi) {
+    // kn non-decreasing candidates in [lo, hi - 1], about evenly spaced
+    const int span = hi - lo;
+    auto cand = [&](int kk) { return lo + min(span - 1, (int)((float)((kk + 1) * span) * inv)); };
+    const int c = cand(k);
+    const int n = lane_group_sum(wl_items(code, c, __builtin_amdgcn_rcpf((float)c)), g);
+    const unsigned long long fits = __ballot(n <= target && (lane & (g - 1)) == 0);
+    if (fits) {
+      // the first fitting candidate; the one before it (a smaller C) did not fit
+      const int kf = __builtin_ctzll(fits) >> lg;
+      const int c_hi = cand(kf);
+      if (kf > 0) lo = cand(kf - 1) + 1;
+      hi = c_hi;
+    } else {
+      lo = cand(kn - 1) + 1;
+    }
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int wl_chunk(const SegmentArgs& a, const WorkList& w) {
   long long total = 0;
   int longest = 1;
-  auto add = [&](int code) {
-    const int st = max(code, 0);
+#pragma unroll
+  for (int p = 0; p < kWlCached; ++p) {
+    const int st = max(w.code[p], 0);
     total += st;
     longest = max(longest, st);
-  };
-#pragma unroll
-  for (int p = 0; p < kWlCached; ++p) add(w.code[p]);
-  for (int b = kWlCached * kWave; b < a.num_seqs; b += kWave) add(wl_code(a, b + lane, rows));
-  // a lane's share of the total stays below 2^47 (at most 1024 sequences of
-  // at most 2^26 steps each): summed as 16-bit high and low parts, each of
+  }
+  // a lane's share of the total stays below 2^28 (kWlCached sequences of at
+  // most 2^26 steps each): summed as 16-bit high and low parts, each of
   // whose totals fits 32 bits
   {
     const int hi = wave_sum_i32((int)(total >> 16));
@@ -396,51 +476,53 @@ __device__ __forceinline__ int wl_chunk(const SegmentArgs& a, int rows, const Wo
     total = ((long long)hi << 16) + lo;
   }
   longest = wave_max_i32(longest);
-  const long long want = (total + a.target_items - 1) / a.target_items;
+  // ceil(total / target): total < 2^53 and the quotient lies at least
+  // 1 / target from an integer unless it is one, far more than its
+  // rounding error, so the ceiling of the double quotient is exact
+  const long long want = (long long)ceil((double)total / (double)a.target_items);
   int hi = max(1, min(longest, a.max_sps));               // a chunk's block ids fit LDS
   int lo = (int)min<long long>(max<long long>(a.steps_per_seg, want), hi);
   lo = max(lo, 1);
-  if (wl_count(a, rows, hi, w) > a.target_items) return hi;   // the fewest chunks possible
-  while (lo < hi) {                                         // smallest C that fits
+  if (wl_count(hi, w) > a.target_items) return hi;       // the fewest chunks possible
+  if (w.P == 1) return wl_search_small(lo, hi, a.target_items, a.num_seqs, w.code[0]);
+  while (lo < hi) {                                       // smallest C that fits
     const int mid = lo + (hi - lo) / 2;
-    if (wl_count(a, rows, mid, w) <= a.target_items) hi = mid; else lo = mid + 1;
+    if (wl_count(mid, w) <= a.target_items) hi = mid; else lo = mid + 1;
   }
   return lo;
 }
 
-// the sequence holding chunk number `item` (in sequence order), and the
-// chunk's index inside it; -1 when item is past the last chunk
-__device__ __forceinline__ int wl_find(const SegmentArgs& a, int rows, int C, int item, int& chunk,
-                                       const WorkList& w) {
+// The sequence holding chunk number `item` (in sequence order): its index,
+// the chunk's index inside it, the sequence's chunk count and metadata;
+// -1 when item is past the last chunk.
+struct WlHit {
+  int seq, chunk, items, b0, b1, L;
+};
+__device__ __forceinline__ WlHit wl_find(int C, int item, const WorkList& w) {
   const int lane = threadIdx.x & (kWave - 1);
+  const float rc = __builtin_amdgcn_rcpf((float)C);
+  WlHit h{-1, 0, 0, 0, 0, 0};
   int base = 0;
-  // one pass over sequences b .. b + 63: true when the chunk lies in it
-  auto pass = [&](int b, int code, int& seq) {
-    const int items = wl_items(code, C);
-    int inc = items;
-    for (int m = 1; m < kWave; m <<= 1) {
-      const int v = __shfl_up(inc, m, kWave);
-      if (lane >= m) inc += v;
-    }
+#pragma unroll
+  for (int p = 0; p < kWlCached; ++p) {
+    if (p >= w.P) break;                                  // uniform
+    const int items = wl_items(w.code[p], C, rc);
+    const int inc = wave_incl_scan(items);
     const int excl = inc - items;
     const unsigned long long hit = __ballot(item >= base + excl && item < base + inc);
     if (hit) {
       const int l = __builtin_ctzll(hit);
-      chunk = item - base - __shfl(excl, l, kWave);
-      seq = b + l;
-      return true;
+      h.seq = p * kWave + l;
+      h.chunk = item - base - __builtin_amdgcn_readlane(excl, l);
+      h.items = __builtin_amdgcn_readlane(items, l);
+      h.b0 = __builtin_amdgcn_readlane(w.b0[p], l);
+      h.b1 = __builtin_amdgcn_readlane(w.b1[p], l);
+      h.L = __builtin_amdgcn_readlane(w.L[p], l);
+      return h;
     }
-    base += __shfl(inc, kWave - 1, kWave);
-    return false;
-  };
-  int seq = -1;
-#pragma unroll
-  for (int p = 0; p < kWlCached; ++p)
-    if (pass(p * kWave, w.code[p], seq)) return seq;
-  for (int b = kWlCached * kWave; b < a.num_seqs; b += kWave)
-    if (pass(b, wl_code(a, b + lane, rows), seq)) return seq;
-  chunk = 0;
-  return -1;
+    base += __builtin_amdgcn_readlane(inc, kWave - 1);
+  }
+  return h;
 }
 
 // ---------------------------------------------------------------------------
@@ -516,12 +598,28 @@ void pa_segment(SegmentArgs a) {
   const int wave = threadIdx.x / kWave;
   const int n16 = lane & 15;          // stacked query row owned by this lane (in each row block)
   const int q4 = lane >> 4;           // lane group
+
+  // Workgroup 0 checks subsequence_begins as a whole (starts at 0, never
+  // decreases, ends at num_tokens): each wavefront writes its verdict on its
+  // share of the entries, every call, so the combine kernel reads NW words
+  // instead of scanning the batch.  The loads go out with the workgroup's
+  // own metadata loads.
+  static_assert(NW < 64, "one header word per wavefront");
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) {
+    bool bad = false;
+#pragma unroll 4
+    for (int i = threadIdx.x; i < a.num_seqs; i += NW * kWave) bad |= a.sb[i] > a.sb[i + 1];
+    if (threadIdx.x == 0) bad |= a.sb[0] != 0 || a.sb[a.num_seqs] != a.num_tokens;
+    const bool wave_bad = __any(bad);
+    if (lane == 0) a.sb_check[wave] = wave_bad ? 1 : 0;
+  }
   // Fixed segments (one sequence): grid (Hkv, num_seqs, S) with segment
   // j = S - 1 - blockIdx.z.  Work-list mode (a batch of several sequences):
   // grid (Hkv, 1, chunks), the sequence and steps of chunk blockIdx.z taken
   // from the work list.
   const int h = blockIdx.x;
   int s, j, st_begin, st_cap, wl_items = 0;
+  WlHit wl_hit{};
   if (!a.worklist) {
     s = blockIdx.y;
     j = a.S - 1 - (int)blockIdx.z;
@@ -531,12 +629,12 @@ void pa_segment(SegmentArgs a) {
     st_cap = (int)(((int64_t)(j + 1) * a.n_steps) / a.S);
   } else {
     const WorkList wl = wl_load(a, ROWS);
-    const int C = wl_chunk(a, ROWS, wl);
-    s = wl_find(a, ROWS, C, (int)blockIdx.z, j, wl);
+    const int C = wl_chunk(a, wl);
+    wl_hit = wl_find(C, (int)blockIdx.z, wl);
+    s = wl_hit.seq;
     if (s < 0) return;                                        // past the last chunk (uniform)
-    bool ok;
-    const int st = wl_steps(a, s, ROWS, ok);
-    wl_items = ok ? (st + C - 1) / C : 1;
+    j = wl_hit.chunk;
+    wl_items = wl_hit.items;
     st_begin = j * C;
     st_cap = st_begin + C;
   }
@@ -558,7 +656,8 @@ void pa_segment(SegmentArgs a) {
     spec_id[k] = x < spec_n ? bt_row[spec_lo + x] : 0;
   }
 
-  const SeqInfo si = seq_info(a, s, ROWS);
+  const SeqInfo si = a.worklist ? seq_decode(a, wl_hit.b0, wl_hit.b1, wl_hit.L, ROWS)
+                                : seq_info(a, s, ROWS);
   if (!si.ok) {
     // A sequence that breaks the contract: its partials for this segment
     // become NaN (for the tokens it claims that exist), so the combine turns

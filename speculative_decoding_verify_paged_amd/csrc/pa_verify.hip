@@ -127,17 +127,28 @@ int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_ve
   pl->grid[0] = p->num_kv_heads;
   pl->grid[1] = p->num_seqs;
   pl->grid[2] = (int32_t)S;
-  pl->worklist = p->num_seqs > 1 ? 1 : 0;
   pl->target_items = (int32_t)std::max<int64_t>(
       1, cdiv((int64_t)num_cus * pav::groups_per_cu(p->kv_dtype, p->head_dim, pl->row_blocks,
                                                     p->block_size), p->num_kv_heads));
+  // The work list pays where a few sequences of unequal length must share
+  // the GPU.  Every sequence has at least one chunk, so with more sequences
+  // than target_items the device's chunk size would be the longest
+  // sequence's (capped by the LDS table): chunks the same as the fixed
+  // per-sequence segments up to their cut points, at the cost of a scan
+  // over the batch in every workgroup.  Those batches, and any of more than
+  // kWlSeqs sequences, take the fixed segments.
+  pl->worklist = p->num_seqs > 1 && p->num_seqs <= std::min<int64_t>(pl->target_items, pav::kWlSeqs);
   if (pl->worklist) {
     // a ragged batch: one workgroup per work-list chunk, at most
-    // max(target, every sequence at its fewest chunks)
+    // max(target, every sequence at its fewest chunks); past the grid's z
+    // limit, fixed segments instead
     const int64_t most = std::max<int64_t>(pl->target_items, (int64_t)p->num_seqs * cdiv(n_steps, max_sps));
-    if (most > 65535) return PA_ERR_UNSUPPORTED;
-    pl->grid[1] = 1;
-    pl->grid[2] = (int32_t)most;
+    if (most > 65535) {
+      pl->worklist = 0;
+    } else {
+      pl->grid[1] = 1;
+      pl->grid[2] = (int32_t)most;
+    }
   }
   pl->block_threads = nw * 64;
   const int64_t rows = (int64_t)p->num_tokens * p->num_q_heads;
@@ -283,6 +294,8 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
   a.sb = sb;
   a.tree = static_cast<const uint32_t*>(p->tree_mask);
   a.status = reinterpret_cast<int32_t*>(ws);
+  a.sb_check = a.status + 1;                         // header words 1 .. waves_per_group
+  a.sb_words = pl.waves_per_group;
   a.ws_ml = reinterpret_cast<float*>(ws + 256);
   a.ws_o = reinterpret_cast<float*>(ws + 256 + ml_bytes);
   a.num_seqs = p->num_seqs;

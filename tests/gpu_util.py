@@ -65,6 +65,22 @@ def run_gpu(case: pi.Case, dev=None, *, num_segments=0, out=None, max_context_le
     return o
 
 
+def plan_of(case: pi.Case, max_query_len=None) -> dict:
+    """The library's launch plan for the case on the current device."""
+    import torch
+    import speculative_decoding_verify_paged_amd as pav
+    p = pav.make_params(num_seqs=case.num_seqs, num_tokens=case.num_tokens,
+                        num_q_heads=case.num_q_heads, num_kv_heads=case.num_kv_heads,
+                        head_dim=case.head_dim, block_size=case.block_size,
+                        num_blocks=case.num_blocks, max_blocks_per_seq=case.max_blocks_per_seq,
+                        q_dtype=case.q_dtype, kv_dtype=case.kv_dtype,
+                        sliding_window=case.sliding_window,
+                        max_query_len=max(case.Ts) if max_query_len is None else max_query_len,
+                        page_layout=getattr(case, "page_layout", 0))
+    cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    return pav.pa_verify_make_plan(p, case.max_context_len, cus)
+
+
 def to_f64(t) -> np.ndarray:
     import torch
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)

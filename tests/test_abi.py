@@ -227,11 +227,16 @@ def check_plan_covers(pl, max_ctx, window=0, nseq=1, hkv=8, bs=16, tq=4):
     lens = [(j + 1) * steps // S - j * steps // S for j in range(S)]
     assert sum(lens) == steps and min(lens) >= 1 and max(lens) - min(lens) <= 1
     assert pl["steps_per_segment"] == max(lens)
-    if nseq == 1:
-        assert pl["grid"] == [hkv, 1, S] and pl["worklist"] == 0
-    else:   # work list: one workgroup per chunk, at least one round of them
+    # the work list takes batches of 2 .. min(target_items, 256) sequences
+    # whose worst case fits the grid; the rest fixed per-sequence segments
+    if 1 < nseq <= min(pl["target_items"], 256) and pl["grid"][1] == 1:
+        # work list: one workgroup per chunk, at least one round of them
         assert pl["worklist"] == 1 and pl["grid"][:2] == [hkv, 1]
         assert pl["grid"][2] >= pl["target_items"]
+    else:
+        assert pl["grid"] == [hkv, nseq, S] and pl["worklist"] == 0
+        if 1 < nseq <= min(pl["target_items"], 256):       # fell back: chunks past the z limit
+            assert nseq * -(-steps // pl["max_steps_per_segment"]) > 65535
     assert pl["steps_per_segment"] <= pl["max_steps_per_segment"]
     assert pl["max_steps_per_segment"] * pl["keys_per_step"] // bs + 2 <= (2080 if bs == 1 else 1040)
 
@@ -254,12 +259,26 @@ def test_plan_ragged_batch_gives_the_longest_sequence_the_gpu():
     # the longest one alone covers the 256 workgroup slots
     pl = plan(32235, num_seqs=8, num_tokens=22, max_blocks_per_seq=2015, num_blocks=6000)
     check_plan_covers(pl, 32235, nseq=8)
-    assert pl["num_segments"] == 32
-    # a large batch is capped at 8 rounds of workgroups
+    assert pl["num_segments"] == 32 and pl["worklist"] == 1
+    # more sequences than workgroup slots per KV head: fixed per-sequence
+    # segments, capped at 8 rounds of workgroups
     pl = plan(32771, num_seqs=64, num_tokens=64 * 3, max_blocks_per_seq=2049, num_blocks=64 * 2049)
     check_plan_covers(pl, 32771, nseq=64)
-    assert pl["num_segments"] == 4
+    assert pl["num_segments"] == 4 and pl["worklist"] == 0
     assert pl["grid"][0] * pl["grid"][1] * pl["grid"][2] <= 8 * 256
+
+
+@pytest.mark.parametrize("nseq,hkv,expect", [
+    (2, 8, 1), (32, 8, 1), (33, 8, 0),          # target 256 / 8 = 32 workgroups per KV head
+    (256, 1, 1), (257, 1, 0),                   # target 256, and the 256 sequences of registers
+    (4096, 8, 0),
+])
+def test_plan_work_list_only_for_small_batches(nseq, hkv, expect):
+    pl = plan(4099, num_seqs=nseq, num_tokens=nseq, num_q_heads=4 * hkv, num_kv_heads=hkv,
+              max_blocks_per_seq=257, num_blocks=257 * nseq)
+    assert pl["target_items"] == 256 // hkv
+    assert pl["worklist"] == expect
+    check_plan_covers(pl, 4099, nseq=nseq, hkv=hkv)
 
 
 @pytest.mark.parametrize("over,rb", [
@@ -309,14 +328,13 @@ def test_plan_grid_limits_are_reported():
     with pytest.raises(pav.PaVerifyError) as e:
         plan(big, block_size=1, max_blocks_per_seq=big, num_blocks=1 << 20)
     assert e.value.code == pav.PA_ERR_UNSUPPORTED
-    # a batch whose worst case needs more than 65535 work-list chunks
-    n = 3000
-    with pytest.raises(pav.PaVerifyError) as e:
-        plan(100_000, block_size=1, max_blocks_per_seq=100_000, num_blocks=1 << 20,
-             num_seqs=n, num_tokens=n)
-    assert e.value.code == pav.PA_ERR_UNSUPPORTED
-    # just inside the limits
-    pl = plan(100_000, block_size=1, max_blocks_per_seq=100_000, num_blocks=1 << 20,
-              num_seqs=600, num_tokens=600)
+    # a small batch whose worst case needs more than 65535 work-list chunks
+    # takes fixed segments instead
+    pl = plan(20_000_000, block_size=1, max_blocks_per_seq=20_000_000, num_blocks=1 << 20,
+              num_seqs=8, num_tokens=8)
     assert pl["max_steps_per_segment"] == 64
-    assert pl["grid"][2] == 600 * -(-3125 // 64) and pl["grid"][2] <= 65535
+    assert pl["worklist"] == 0 and pl["grid"] == [8, 8, -(-625_000 // 64)]
+    # just inside the work list's limit
+    pl = plan(200_000, block_size=1, max_blocks_per_seq=200_000, num_blocks=1 << 20,
+              num_seqs=8, num_tokens=8)
+    assert pl["worklist"] == 1 and pl["grid"] == [8, 1, 8 * -(-6250 // 64)]

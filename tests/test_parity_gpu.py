@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import pa_inputs as pi
-from gpu_util import (excess, max_err, run_gpu, to_f64, tol)
+from gpu_util import (excess, max_err, plan_of, run_gpu, to_f64, tol)
 from gpu_util import half_ulp as gpu_half_ulp
 
 pytestmark = pytest.mark.gpu
@@ -192,10 +192,10 @@ def test_small_ragged_batches():
 
 
 def test_work_list_shapes():
-    """Batches of several sequences take their steps from the device-side
-    work list: more than one 64-lane pass over the sequences, chunk sizes
-    capped by the block-id table (1-slot pages), more sequences than
-    workgroup slots, equal lengths, and one long sequence among many short."""
+    """Batches of several sequences: the device-side work list with more than
+    one 64-lane group of sequences, chunk sizes capped by the block-id table
+    (1-slot pages), equal lengths, and one long sequence among many short;
+    600 tiny sequences (more than the workgroup slots) as fixed segments."""
     rng = np.random.default_rng(191)
     shapes = [
         ("many150_bs16", [int(x) for x in rng.integers(0, 2000, 150)], 16, 64, pi.F16),
@@ -213,8 +213,8 @@ def test_work_list_shapes():
 
 
 def test_very_large_batches():
-    """Thousands of short sequences: the work list's scans over the batch
-    (many 64-lane passes) and grids of thousands of workgroups."""
+    """Thousands of short sequences: fixed per-sequence segments on grids of
+    thousands of workgroups."""
     rng = np.random.default_rng(197)
     for k, (n, Hkv, G) in enumerate([(3000, 16, 1), (20000, 2, 2)]):
         Ls = [int(x) for x in rng.integers(0, 40, n)]
@@ -222,6 +222,58 @@ def test_very_large_batches():
         case = pi.build_case([196, k], Ls, Ts, num_q_heads=G * Hkv, num_kv_heads=Hkv,
                              head_dim=64, block_size=16, q_dtype=pi.F16, kv_dtype=pi.F16,
                              spare_blocks=2, poison=True, name=f"batch{n}_H{Hkv}_G{G}")
+        _full(case, rounding_aware=True)
+
+
+def test_work_list_register_groups():
+    """Work-list batches of up to 256 sequences, whose metadata every
+    wavefront holds in four lane-strided register groups (65 sequences: a
+    second group; 200: a partial fourth; 256: all four), and 257 sequences,
+    one past them (fixed per-sequence segments)."""
+    rng = np.random.default_rng(211)
+    for k, (n, wl) in enumerate([(65, 1), (200, 1), (256, 1), (257, 0)]):
+        Ls = [int(x) for x in rng.integers(0, 900, n)]
+        Ts = [int(t) for t in rng.integers(1, 5, n)]
+        case = pi.build_case([210, k], Ls, Ts, num_q_heads=4, num_kv_heads=1, head_dim=64,
+                             block_size=16, q_dtype=pi.F16, kv_dtype=pi.F16, spare_blocks=3,
+                             poison=True, name=f"wl_groups{n}")
+        assert plan_of(case)["worklist"] == wl, n
+        _full(case, rounding_aware=True)
+
+
+def _fixed_batches():
+    rng = np.random.default_rng(223)
+    out = [pi.config5(rep=0, num_seqs=64, lo=64, hi=6000, poison=True)]
+    n = 40
+    Ls = [int(x) for x in rng.integers(0, 3000, n)]
+    Ts = [int(t) for t in rng.integers(1, 4, n)]
+    out.append(pi.build_case([222, 1], Ls, Ts, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                             block_size=16, q_dtype=pi.BF16, kv_dtype=pi.BF16, sliding_window=700,
+                             spare_blocks=4, poison=True, name="fixed_window40"))
+    n = 48
+    Ls = [int(x) for x in rng.integers(0, 2500, n)]
+    Ts = [int(t) for t in rng.integers(2, 9, n)]
+    out.append(pi.build_case([222, 2], Ls, Ts, num_q_heads=16, num_kv_heads=8, head_dim=128,
+                             block_size=16, q_dtype=pi.F16, kv_dtype=pi.F16, spare_blocks=4,
+                             poison=True, tree=True, name="fixed_tree48"))
+    n = 80
+    Ls = [int(x) for x in rng.integers(0, 2500, n)]
+    Ts = [int(t) for t in rng.integers(1, 5, n)]
+    out.append(pi.build_case([222, 3], Ls, Ts, num_q_heads=16, num_kv_heads=4, head_dim=128,
+                             block_size=16, q_dtype=pi.BF16, kv_dtype=pi.U8, spare_blocks=4,
+                             poison=True, name="fixed_u8_80"))
+    out.append(pi.with_layout(pi.config5(rep=1, num_seqs=40, lo=64, hi=4000), pi.PAGES_ROW_MAJOR))
+    return out
+
+
+def test_fixed_segment_batches():
+    """Batches of more sequences than the work list targets: fixed
+    per-sequence segments, several per sequence (most of a short sequence's
+    empty), for causal, sliding-window, tree and u8 layers and row-major
+    pages."""
+    for case in _fixed_batches():
+        pl = plan_of(case)
+        assert pl["worklist"] == 0 and pl["num_segments"] > 1, (case.name, pl)
         _full(case, rounding_aware=True)
 
 
@@ -318,6 +370,31 @@ def test_device_contract_violations_give_nan_and_status():
     assert pav.pa_verify_read_status() == pav.PA_ERR_DEVICE_CONTRACT
     assert np.all(np.isnan(got[2:]))
     assert np.max(np.abs(got[:2] - ref[:2])) <= 2e-3
+
+
+def test_begins_contract_violations_make_every_row_nan():
+    """subsequence_begins that does not start at 0, end at num_tokens and
+    never decrease leaves tokens no sequence (or two) claims: every output
+    row is NaN and the status is set, in work-list and fixed-segment
+    batches; the next valid call is clean."""
+    import speculative_decoding_verify_paged_amd as pav
+    base = pi.build_case([37], [300, 200, 100], [2, 3, 1], num_q_heads=8, num_kv_heads=2,
+                         head_dim=128, block_size=16, name="begins")
+    big = pi.config5(rep=3, num_seqs=40, lo=16, hi=200)
+    assert plan_of(base, max_query_len=4)["worklist"] == 1
+    assert plan_of(big)["worklist"] == 0
+    nb = list(big.subsequence_begins)
+    for case, sb in ((base, [1, 2, 5, 6]), (base, [0, 2, 5, 5]), (base, [0, 3, 2, 6]),
+                     (big, [1] + nb[1:]), (big, nb[:-1] + [nb[-1] - 1])):
+        bad = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+        bad.subsequence_begins = np.array(sb, np.int32)
+        got = to_f64(run_gpu(bad, max_query_len=4))
+        assert pav.pa_verify_read_status() == pav.PA_ERR_DEVICE_CONTRACT, sb
+        assert np.all(np.isnan(got)), sb
+    for case in (base, big):
+        got = to_f64(run_gpu(case, max_query_len=4))
+        assert pav.pa_verify_read_status() == pav.PA_OK
+        assert excess(case, got, oracle.forward(case)) <= 0.0
 
 
 def test_cached_workspace_growth_keeps_a_pending_status():

@@ -7,6 +7,8 @@ holds) whose chunks of all sequences number at most the target count; it
 launches one workgroup per chunk on a grid the host sized without seeing
 the lengths.  The model restates that rule; the test checks that every chunk
 fits the host's grid and the per-token partial slots, for random batches.
+Batches of more sequences than the target (or than 256) take fixed
+per-sequence segments instead.
 """
 import numpy as np
 import pytest
@@ -51,6 +53,14 @@ def test_worklist_chunks_fit_the_planned_grid(bs):
             params(num_seqs=n, num_tokens=int(Ts.sum()), num_q_heads=4 * hkv, num_kv_heads=hkv,
                    block_size=bs, max_blocks_per_seq=mbps, num_blocks=n * mbps, max_query_len=4),
             ctx, 256)
+        if not pl["worklist"]:
+            # more sequences than the target (every sequence has a chunk of its
+            # own) or than the registers hold, or a worst case past the grid's
+            # z limit: fixed per-sequence segments
+            assert (n > min(pl["target_items"], 256)
+                    or n * cdiv(pl["num_steps"], pl["max_steps_per_segment"]) > 65535)
+            assert pl["grid"] == [hkv, n, pl["num_segments"]]
+            continue
         assert pl["worklist"] == 1 and pl["grid"][:2] == [hkv, 1]
         max_sps = pl["max_steps_per_segment"]
         steps = [cdiv(L + int(t), 32) for L, t in zip(Ls, Ts)]
