@@ -83,7 +83,9 @@
  * Ownership and behaviour.  The library never allocates, frees or retains a
  * pointer past the call and never synchronises (except pa_verify_read_status).
  * A forward call enqueues exactly two kernels (segment kernel, then combine
- * kernel) on params->stream, so it can be captured in a HIP graph.  Calls are
+ * kernel; with one segment, the segment kernel writes the output and a
+ * check kernel takes the combine's place) on params->stream, so it can be
+ * captured in a HIP graph.  Calls are
  * stateless and thread-safe; calls that share one workspace must be ordered
  * on one stream.  No C++ exception crosses this ABI.
  *
@@ -177,11 +179,12 @@ typedef struct pa_verify_plan {
                                   covers steps [j*N/S, (j+1)*N/S) of num_steps = N */
   int32_t num_steps;           /* N: steps covering span */
   int32_t row_blocks;          /* 16-row blocks of stacked query rows the kernel is built with */
-  int32_t worklist;            /* 1 for a batch of several sequences: the grid is
-                                  (Hkv, 1, chunks) and each workgroup takes one chunk of a
-                                  work list the device builds from the sequence lengths
+  int32_t worklist;            /* 1 for a batch of 2 .. min(target_items, 256) sequences: the
+                                  grid is (Hkv, 1, chunks) and each workgroup takes one chunk
+                                  of a work list the device builds from the sequence lengths
                                   (chunk size chosen so the chunks fill one round of
-                                  target_items workgroups per KV head); 0: fixed segments */
+                                  target_items workgroups per KV head); 0: fixed segments,
+                                  also for larger batches (every sequence has its own) */
   int32_t target_items;        /* work-list chunks per KV head the chunk size aims at */
   int32_t keys_per_step;       /* keys one wavefront consumes per loop iteration */
   int32_t span;                /* bound on keys any one sequence's rows touch */
@@ -193,9 +196,13 @@ typedef struct pa_verify_plan {
   int32_t grid[3];             /* segment kernel grid: (Hkv, num_seqs, S), z = S-1-j; work
                                   list: (Hkv, 1, chunks) */
   int32_t block_threads;       /* segment kernel workgroup size */
-  int32_t combine_grid[3];     /* combine kernel grid */
-  int32_t combine_threads;     /* combine kernel workgroup size */
-  size_t workspace_bytes;      /* status word + per-token segment partials */
+  int32_t combine_grid[3];     /* combine kernel grid (direct: the check kernel's) */
+  int32_t combine_threads;     /* combine kernel workgroup size (direct: the check kernel's) */
+  size_t workspace_bytes;      /* status word + per-token segment partials (direct: 256) */
+  int32_t direct;              /* 1 when S == 1: the segment kernel normalises and writes the
+                                  output rows itself (no partials), and a check kernel that
+                                  turns every row NaN if subsequence_begins is broken runs
+                                  in the combine kernel's place */
 } pa_verify_plan;
 
 /* Fill *plan for params p, host scalar max_context_len (>= max_s L_s + T_s)

@@ -121,6 +121,32 @@ __global__ __launch_bounds__(kWave) void pa_combine(CombineArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Check kernel of a direct call (one segment, output written by the segment
+// kernel): when the segment kernel's workgroup 0 found subsequence_begins
+// broken, every output row becomes NaN and the status word is set, as the
+// combine kernel does; otherwise every wavefront exits after one load.
+// ---------------------------------------------------------------------------
+template <int OUT>
+__global__ __launch_bounds__(kFinishThreads) void pa_finish(CombineArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = lane < a.seg.sb_words ? a.seg.sb_check[lane] : 0;
+  if (!__any(w != 0)) return;                                 // uniform
+  if (blockIdx.x == 0 && threadIdx.x == 0) atomicExch(a.seg.status, kDeviceContract);
+  const uint32_t nan2 = OUT == kF16 ? 0x7E007E00u : 0x7FC07FC0u;
+  const size_t n = (size_t)a.num_tokens * a.Hq * a.head_dim / 2;   // 32-bit words of out
+  uint32_t* out = reinterpret_cast<uint32_t*>(a.out);
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    out[i] = nan2;
+}
+
+hipError_t launch_finish(const CombineArgs& a, int out_dtype, int threads, dim3 grid, hipStream_t st) {
+  if (threads != kFinishThreads) return hipErrorInvalidValue;
+  const void* fn = out_dtype == kF16 ? reinterpret_cast<const void*>(pa_finish<kF16>)
+                                     : reinterpret_cast<const void*>(pa_finish<kBF16>);
+  return launch_kernel(fn, grid, dim3(kFinishThreads), st, a);
+}
+
 template <int D>
 static hipError_t launch_combine_d(const CombineArgs& a, int out_dtype, dim3 grid, hipStream_t st) {
   const void* fn = out_dtype == kF16 ? reinterpret_cast<const void*>(pa_combine<D, kF16>)

@@ -50,6 +50,10 @@ struct SegmentArgs {
   int32_t max_sps;                   // most steps whose block ids fit the LDS table
   float scale_log2;                  // scale * log2(e)
   int32_t page_layout;               // kPagesTiled or kPagesRowMajor
+  // S == 1: the segment kernel normalises its rows and writes them to out
+  // ([num_tokens, Hq, D] in the q dtype) instead of partials
+  int32_t direct;
+  void* out;
 };
 
 struct AppendArgs {
@@ -77,6 +81,7 @@ struct CombineArgs {
   // whose L2 may still hold that KV head's partials from the segment kernel
   // (all of them when the XCD count divides Hkv).
   int32_t xcds;
+  int32_t head_dim;
 };
 
 // ev0/ev1: optional events timestamped by the segment kernel's own dispatch
@@ -90,6 +95,9 @@ hipError_t launch_segment_u8(const SegmentArgs& a, int q_dtype, int D, int bs, i
                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_combine(const CombineArgs& a, int out_dtype, int D, int threads, dim3 grid,
                           hipStream_t st);
+// After a direct segment kernel: turns every output row into NaN and sets
+// the status when the segment kernel found subsequence_begins broken.
+hipError_t launch_finish(const CombineArgs& a, int out_dtype, int threads, dim3 grid, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, int q_dtype, int kv_dtype, int D, hipStream_t st);
 // Most steps a segment or work-list chunk may span: its block ids (one more
 // for a step that starts inside a page, one more for the last page) must fit
@@ -106,6 +114,9 @@ static_assert(max_steps_per_segment(64) < 65536, "chunk sizes must stay below 2^
 // Combine grid: one 64-thread workgroup per (token, q head) row and 64-column
 // slice of it (same-box A/B, us per call: see the combine kernel).
 constexpr int combine_slices(int D) { return D / 64; }
+// The check kernel of direct calls: one 256-thread workgroup per CU.
+constexpr int kFinishGroups = 256;
+constexpr int kFinishThreads = 256;
 
 // Per (cache dtype, head_dim, row blocks, block size): wavefronts per SIMD
 // the segment kernel is compiled for (its register budget, no spills; each

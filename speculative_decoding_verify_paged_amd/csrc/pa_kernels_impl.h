@@ -658,13 +658,30 @@ void pa_segment(SegmentArgs a) {
 
   const SeqInfo si = a.worklist ? seq_decode(a, wl_hit.b0, wl_hit.b1, wl_hit.L, ROWS)
                                 : seq_info(a, s, ROWS);
+  // Direct calls (one segment): output rows [t0, t1) x this KV head's q
+  // heads become NaN (a sequence that breaks the contract, a row with no key)
+  auto nan_rows = [&](int t0, int t1) {
+    constexpr int V8 = D / 8;                                 // 16-byte stores per row
+    const u32x4 nan8 = QT == kF16 ? u32x4{0x7E007E00u, 0x7E007E00u, 0x7E007E00u, 0x7E007E00u}
+                                  : u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+    for (int x = threadIdx.x; x < (t1 - t0) * a.G * V8; x += NW * kWave) {
+      const int y = x / V8;
+      const size_t row = (size_t)(t0 + y / a.G) * a.Hq + h * a.G + y % a.G;
+      reinterpret_cast<u32x4*>(a.out)[row * V8 + x % V8] = nan8;
+    }
+  };
   if (!si.ok) {
     // A sequence that breaks the contract: its partials for this segment
     // become NaN (for the tokens it claims that exist), so the combine turns
-    // its rows into NaN without re-checking the sequence.
+    // its rows into NaN without re-checking the sequence; a direct call
+    // writes NaN rows.
     if (j == 0 && h == 0 && threadIdx.x == 0) atomicExch(a.status, kDeviceContract);
     const int t0 = min(max(si.b0, 0), a.num_tokens);
     const int t1 = min(max(si.b0 + si.T, t0), a.num_tokens);
+    if (a.direct) {
+      nan_rows(t0, t1);
+      return;
+    }
     // work-list mode: the sequence's only chunk marks all its slots
     const int nj = a.worklist ? a.S : 1;
     for (int x = threadIdx.x; x < (t1 - t0) * a.G * nj; x += NW * kWave) {
@@ -691,7 +708,13 @@ void pa_segment(SegmentArgs a) {
   const int st_end = min(si.n_steps, st_cap);
   if (st_begin >= st_end) {
     // no key of this sequence falls in segment j: an empty partial, so the
-    // combine can read all S partials without knowing the sequence
+    // combine can read all S partials without knowing the sequence (a
+    // direct call's only segment: rows with no key, NaN as the combine
+    // would make them)
+    if (a.direct) {
+      nan_rows(si.b0, si.b0 + T);
+      return;
+    }
     if (threadIdx.x < R) {
       const int r = threadIdx.x;
       const size_t row = ((size_t)(si.b0 + r % T) * a.Hq + h * a.G + r / T) * a.S + j;
@@ -1516,6 +1539,34 @@ void pa_segment(SegmentArgs a) {
     const int rt = si.b0 + r % T;
     const int rh = h * a.G + r / T;
     const size_t row = ((size_t)rt * a.Hq + rh) * a.S + j;   // partials are per token
+    if (a.direct) {
+      // the one segment: the normalised row (NaN for a row with no key,
+      // 0 / 0, as the combine would make it)
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      float lsum = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float f = __builtin_amdgcn_exp2f(s_m[w][r] - M);
+          acc += f * *reinterpret_cast<const f32x4*>(&s_o[w][r][c4]);
+          lsum += f * s_l[w][r];
+        }
+      }
+      u32x2 packed;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float x0 = bad ? NAN : acc[2 * e] / lsum, x1 = bad ? NAN : acc[2 * e + 1] / lsum;
+        if constexpr (QT == kF16) {
+          packed[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x0) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x1) << 16);
+        } else {
+          packed[e] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x0) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x1) << 16);
+        }
+      }
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + ((size_t)rt * a.Hq + rh) * D + c4) = packed;
+      continue;
+    }
     if (M == -INFINITY) {                                     // no key of this row here
       if (c4 == 0) {
         a.ws_ml[row * 2 + 0] = bad ? NAN : -INFINITY;

@@ -152,12 +152,16 @@ int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_ve
   }
   pl->block_threads = nw * 64;
   const int64_t rows = (int64_t)p->num_tokens * p->num_q_heads;
-  pl->combine_grid[0] = (int32_t)(rows * pav::combine_slices(p->head_dim));
+  // One segment: nothing to combine.  The segment kernel writes the output
+  // rows (no partials) and a check kernel of kFinishGroups workgroups
+  // follows it in the combine's place.
+  pl->direct = S == 1 ? 1 : 0;
+  pl->combine_grid[0] = pl->direct ? pav::kFinishGroups : (int32_t)(rows * pav::combine_slices(p->head_dim));
   pl->combine_grid[1] = 1;
   pl->combine_grid[2] = 1;
-  pl->combine_threads = 64;
-  const size_t ml_bytes = (size_t)rows * S * 2 * sizeof(float);
-  const size_t o_bytes = (size_t)rows * S * p->head_dim * sizeof(float);
+  pl->combine_threads = pl->direct ? pav::kFinishThreads : 64;
+  const size_t ml_bytes = pl->direct ? 0 : (size_t)rows * S * 2 * sizeof(float);
+  const size_t o_bytes = pl->direct ? 0 : (size_t)rows * S * p->head_dim * sizeof(float);
   pl->workspace_bytes = 256 + ((ml_bytes + 255) / 256) * 256 + o_bytes;
   return PA_OK;
 }
@@ -282,7 +286,7 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
 
   char* ws = static_cast<char*>(ws_base);
   const size_t rows = (size_t)p->num_tokens * p->num_q_heads;
-  const size_t ml_bytes = ((rows * pl.num_segments * 2 * sizeof(float) + 255) / 256) * 256;
+  const size_t ml_bytes = pl.direct ? 0 : ((rows * pl.num_segments * 2 * sizeof(float) + 255) / 256) * 256;
   pav::SegmentArgs a;
   a.q = q;
   a.k = k;
@@ -316,6 +320,8 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
   a.max_sps = pav::max_steps_per_segment(p->block_size);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.page_layout = p->page_layout;
+  a.direct = pl.direct;
+  a.out = out;
 
   hipStream_t st = static_cast<hipStream_t>(p->stream);
   hipEvent_t e0 = static_cast<hipEvent_t>(p->prof_event_begin);
@@ -347,7 +353,11 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
     b = t;
   }
   c.xcds = g > 1 ? g : 0;
-  e = pav::launch_combine(c, p->q_dtype, p->head_dim, pl.combine_threads, dim3(pl.combine_grid[0]), st);
+  c.head_dim = p->head_dim;
+  if (pl.direct)
+    e = pav::launch_finish(c, p->q_dtype, pl.combine_threads, dim3(pl.combine_grid[0]), st);
+  else
+    e = pav::launch_combine(c, p->q_dtype, p->head_dim, pl.combine_threads, dim3(pl.combine_grid[0]), st);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -296,6 +296,21 @@ def test_plan_row_blocks(over, rb):
     assert pl["row_blocks"] == rb
 
 
+def test_plan_direct_output_for_one_segment():
+    # one segment per sequence (large batches, tiny contexts, or forced):
+    # the segment kernel writes the output, no partials, a check kernel of
+    # 256 x 256 threads in the combine's place
+    for pl in (plan(257, num_seqs=600, num_tokens=600, max_blocks_per_seq=17, num_blocks=600 * 17),
+               plan(30, num_tokens=3, max_blocks_per_seq=2, num_blocks=2),
+               plan(16000, num_segments=1)):
+        assert pl["num_segments"] == 1 and pl["direct"] == 1
+        assert pl["workspace_bytes"] == 256
+        assert pl["combine_grid"] == [256, 1, 1] and pl["combine_threads"] == 256
+    pl = plan(32771)
+    assert pl["num_segments"] > 1 and pl["direct"] == 0
+    assert pl["combine_grid"][0] == 3 * 32 * 2 and pl["combine_threads"] == 64
+
+
 def test_plan_window_and_forced_segments():
     pl = plan(51202, num_q_heads=32, num_kv_heads=16, head_dim=256, block_size=64,
               num_blocks=801, max_blocks_per_seq=801, sliding_window=1024, num_tokens=2,

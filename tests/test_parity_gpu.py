@@ -277,6 +277,87 @@ def test_fixed_segment_batches():
         _full(case, rounding_aware=True)
 
 
+def _direct_batches():
+    rng = np.random.default_rng(229)
+    out = []
+
+    def add(k, n, lo, hi, tlo, thi, **kw):
+        Ls = [int(x) for x in rng.integers(lo, hi, n)]
+        Ts = [int(t) for t in rng.integers(tlo, thi + 1, n)]
+        out.append(pi.build_case([228, k], Ls, Ts, spare_blocks=4, poison=True, **kw))
+
+    add(0, 300, 0, 300, 1, 4, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+        q_dtype=pi.F16, kv_dtype=pi.F16, name="direct_f16_d128")
+    add(1, 200, 0, 900, 1, 3, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+        q_dtype=pi.BF16, kv_dtype=pi.BF16, sliding_window=64, name="direct_bf16_window64")
+    add(2, 400, 0, 300, 1, 4, num_q_heads=16, num_kv_heads=4, head_dim=256, block_size=16,
+        q_dtype=pi.F16, kv_dtype=pi.U8, name="direct_u8_d256")
+    add(3, 200, 0, 300, 2, 8, num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=16,
+        q_dtype=pi.F16, kv_dtype=pi.F16, tree=True, name="direct_tree")
+    add(4, 300, 0, 200, 1, 8, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+        q_dtype=pi.BF16, kv_dtype=pi.BF16, name="direct_two_row_blocks")
+    add(6, 300, 0, 200, 1, 4, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=4,
+        q_dtype=pi.BF16, kv_dtype=pi.BF16, name="direct_bs4")
+    add(5, 400, 0, 250, 1, 4, num_q_heads=32, num_kv_heads=8, head_dim=64, block_size=16,
+        q_dtype=pi.F16, kv_dtype=pi.F16, name="direct_d64")
+    out.append(pi.with_layout(out[0], pi.PAGES_ROW_MAJOR))
+    return out
+
+
+def test_direct_output_batches():
+    """One segment per sequence (batches of hundreds of short sequences):
+    the segment kernel writes the normalised rows itself and a check kernel
+    runs in the combine's place; causal, sliding-window, u8, tree, two row
+    blocks, head_dim 64, 4-slot pages and row-major pages."""
+    for case in _direct_batches():
+        pl = plan_of(case)
+        assert pl["direct"] == 1 and pl["num_segments"] == 1, (case.name, pl)
+        _full(case, rounding_aware=True)
+
+
+def test_direct_output_contract_violations():
+    """Direct calls keep the contract: a sequence that breaks it (T above
+    max_query_len, a block id out of range) has NaN rows and the others are
+    untouched; subsequence_begins that leaves a token unclaimed makes every
+    row NaN (the check kernel); each sets the status; a clean call after."""
+    import speculative_decoding_verify_paged_amd as pav
+    case = _direct_batches()[0]
+    ref = oracle.forward(case)
+    sb = case.subsequence_begins
+    Ts = case.Ts
+    assert plan_of(case, max_query_len=3)["direct"] == 1
+    # T = 4 rows under max_query_len 3
+    got = to_f64(run_gpu(case, max_query_len=3))
+    assert pav.pa_verify_read_status() == pav.PA_ERR_DEVICE_CONTRACT
+    long_rows = np.zeros(case.num_tokens, bool)
+    for s, T in enumerate(Ts):
+        if T > 3:
+            long_rows[sb[s]:sb[s + 1]] = True
+    assert long_rows.any() and (~long_rows).any()
+    assert np.all(np.isnan(got[long_rows]))
+    assert excess(case, got[~long_rows], ref[~long_rows]) <= 0.0
+    # a used block id out of range in sequence 7
+    bad = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+    bt = case.block_tables.copy()
+    bt[7, 0] = case.num_blocks + 3
+    bad.block_tables = bt
+    got = to_f64(run_gpu(bad))
+    assert pav.pa_verify_read_status() == pav.PA_ERR_DEVICE_CONTRACT
+    assert np.all(np.isnan(got[sb[7]:sb[8]]))
+    keep = np.ones(case.num_tokens, bool)
+    keep[sb[7]:sb[8]] = False
+    assert excess(case, got[keep], ref[keep]) <= 0.0
+    # token 0 claimed by no sequence
+    bad = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+    bad.subsequence_begins = np.concatenate([[1], sb[1:]]).astype(np.int32)
+    got = to_f64(run_gpu(bad, max_query_len=4))
+    assert pav.pa_verify_read_status() == pav.PA_ERR_DEVICE_CONTRACT
+    assert np.all(np.isnan(got))
+    got = to_f64(run_gpu(case))
+    assert pav.pa_verify_read_status() == pav.PA_OK
+    assert excess(case, got, ref) <= 0.0
+
+
 @pytest.mark.parametrize("S", [1, 2, 7, 0, 10 ** 6])
 def test_segment_count_invariance(S):
     case = pi.config2(8192, 3)
@@ -488,10 +569,13 @@ def test_graph_capture_replays_match_eager():
     from gpu_util import to_device
     import speculative_decoding_verify_paged_amd as pav
     # fixed segments, a sliding window, a work-list batch, 1-slot pages
-    # (LDS reordering), a tree and the u8 entry point
+    # (LDS reordering), a tree, the u8 entry point and a one-segment batch
+    # (direct output and the check kernel)
     cases = [pi.config2(8192, 3, rep=7), pi.config4(4096, window=1024, rep=7),
              pi.config5(rep=7, lo=1, hi=3000), pi.config2(2048, 3, rep=7, block_size=1),
-             pi.config2(2048, 4, rep=7, tree=True), pi.config3(2048, 3, rep=7)]
+             pi.config2(2048, 4, rep=7, tree=True), pi.config3(2048, 3, rep=7),
+             pi.config5(rep=7, num_seqs=300, lo=8, hi=200, spare_blocks=4)]
+    assert plan_of(cases[-1])["direct"] == 1
     devs = [to_device(c) for c in cases]
     outs = [torch.empty_like(d["q"]) for d in devs]
 
