@@ -1278,8 +1278,9 @@ void pa_segment(SegmentArgs a) {
   };
 
   // -------------------------------------------------------------------------
-  // Half-step path (HR > 0, 16-slot pages): the wavefront's steps are taken
-  // one sub-tile (16 keys) at a time through a ring of HR register sets, and
+  // Half-step path (HR > 0, 16-slot pages): the wavefront's share of the
+  // segment is taken one sub-tile (16 keys) at a time through a ring of HR
+  // register sets, and
   // the loads of half-step j + HR are issued as soon as half-step j has been
   // computed, so loads stay in flight while the wavefront computes.  Half-
   // steps past the wavefront's last are still issued (the count of
@@ -1459,23 +1460,27 @@ void pa_segment(SegmentArgs a) {
   };
 
   if constexpr (HR > 0 && BS >= 16) {
-    // the wavefront's half-steps j = 0 .. nh - 1: step st_begin + wave +
-    // (j / 2) * NW, sub-tile j % 2
-    const int first = st_begin + wave;
-    const int nh = first < st_end ? 2 * ((st_end - 1 - first) / NW + 1) : 0;
+    // The segment's half-steps k = 0 .. 2 (st_end - st_begin) - 1 (sub-tile
+    // k % 2 of step st_begin + k / 2) go to the wavefronts round-robin: this
+    // one's j-th is k = wave + j NW.  A segment one step longer than a
+    // multiple of NW (the T new keys past a round context) then gives that
+    // step's halves to two wavefronts instead of a whole step to one.
+    const int nseg = 2 * max(st_end - st_begin, 0);
+    const int nh = wave < nseg ? (nseg - 1 - wave) / NW + 1 : 0;
+    auto hst = [&](int j) { return st_begin + ((wave + j * NW) >> 1); };
+    auto htau = [&](int j) { return (wave + j * NW) & 1; };
     if (nh > 0) {
       Half ring[HR];
 #pragma unroll
-      for (int i = 0; i < HR; ++i)
-        load_half(first + (i >> 1) * NW, i & 1, ring[i], i < nh, i == 0);
+      for (int i = 0; i < HR; ++i) load_half(hst(i), htau(i), ring[i], i < nh, i == 0);
       finish_q();
       for (int j0 = 0; j0 < nh; j0 += HR) {
 #pragma unroll
         for (int i = 0; i < HR; ++i) {
           const int j = j0 + i;
-          if (j < nh) compute_half(first + (j >> 1) * NW, j & 1, ring[i]);
+          if (j < nh) compute_half(hst(j), htau(j), ring[i]);
           const int jn = j + HR;
-          load_half(first + (jn >> 1) * NW, jn & 1, ring[i], jn < nh, false);
+          load_half(hst(jn), htau(jn), ring[i], jn < nh, false);
         }
       }
     }
