@@ -275,8 +275,13 @@ int pa_verify_forward_u8(const void* q, const uint8_t* k_cache, const uint8_t* v
  * word at the head of p->workspace (>= 4 bytes); not max_context_len.
  * Device-side contract violations (as for the forward call, with positions
  * bounded by max_blocks_per_seq * block_size) set the status word and write
- * nothing for that token.  Enqueues one kernel; enqueue it before the forward
- * call on the same stream. */
+ * nothing for that token.  subsequence_begins is checked as a whole by one
+ * wavefront (a broken one sets the status word); each token is looked up as
+ * the last s with subsequence_begins[s] <= token and written only if that
+ * sequence's own checks pass, so a broken array can at most fill new-token
+ * slots inside the block tables (the forward call then gives NaN rows).
+ * Enqueues one kernel; enqueue it before the forward call on the same
+ * stream. */
 int pa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                  const int32_t* block_tables, const int32_t* past_lens,
                  const int32_t* subsequence_begins, const pa_verify_params* p);

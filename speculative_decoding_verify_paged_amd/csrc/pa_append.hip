@@ -52,26 +52,42 @@ __global__ __launch_bounds__(kWave) void pa_append(AppendArgs a) {
   const int lane = threadIdx.x;
   const int n = blockIdx.x, g = blockIdx.y, kv = blockIdx.z;
 
-  // the token's sequence, and subsequence_begins checked on the way (as the
-  // combine kernel does): it starts at 0, never decreases, ends at num_tokens
-  bool ok = true;
-  int s = -1;
-  for (int b = 0; b < a.num_seqs; b += kWave) {
-    const int k = b + lane;
-    const int nx = k < a.num_seqs ? a.sb[k + 1] : 0;
-    const int th = k < a.num_seqs ? a.sb[k] : 0;
-    ok &= !__any(k < a.num_seqs && th > nx);
-    if (b == 0) ok &= __builtin_amdgcn_readlane(th, 0) == 0;
-    if (b + kWave >= a.num_seqs) ok &= __builtin_amdgcn_readlane(nx, a.num_seqs - 1 - b) == a.num_tokens;
-    const unsigned long long hit = __ballot(k < a.num_seqs && n < nx);
-    if (s < 0 && hit) s = b + __builtin_ctzll(hit);
+  // One wavefront checks subsequence_begins as a whole (starts at 0, never
+  // decreases, ends at num_tokens) and sets the status if it is broken; the
+  // others take it as sorted.
+  if (n == 0 && g == 0 && kv == 0) {
+    bool bad = false;
+    for (int k = lane; k < a.num_seqs; k += kWave) bad |= a.sb[k] > a.sb[k + 1];
+    if (lane == 0) bad |= a.sb[0] != 0 || a.sb[a.num_seqs] != a.num_tokens;
+    if (__any(bad) && lane == 0) atomicExch(a.status, kDeviceContract);
   }
-  ok &= s >= 0;
+  // The token's sequence: the last s with sb[s] <= n, narrowed 64 entries
+  // at a time (one load per lane and round: two rounds up to 4096
+  // sequences).  Whatever the array holds, a token is written only for an s
+  // with sb[s] <= n < sb[s + 1] whose own checks below pass: a position of
+  // that sequence's new tokens, inside its block table.
+  int lo = 0, cnt = a.num_seqs;                               // candidates sb[lo .. lo + cnt)
+  int s = -1;
+  while (true) {
+    const int stride = cnt > kWave ? (cnt + kWave - 1) / kWave : 1;
+    const int k = lo + lane * stride;
+    const bool le = lane * stride < cnt && a.sb[k] <= n;
+    const unsigned long long m = __ballot(le);
+    if (!m) break;                                            // n below every candidate
+    const int l = 63 - __builtin_clzll(m);
+    if (stride == 1) {
+      s = lo + l;
+      break;
+    }
+    lo += l * stride;
+    cnt = min(stride, cnt - l * stride);
+  }
+  bool ok = s >= 0;
   int blk = 0, slot = 0;
   if (ok) {
     const int b0 = a.sb[s], T = a.sb[s + 1] - b0, L = a.past_lens[s];
     const int pos = L + (n - b0);
-    ok = T >= 1 && T <= a.max_q && L >= 0 && (int64_t)pos < (int64_t)a.mbps * a.bs;
+    ok = n < b0 + T && T >= 1 && T <= a.max_q && L >= 0 && (int64_t)pos < (int64_t)a.mbps * a.bs;
     if (ok) {
       blk = a.bt[(size_t)s * a.mbps + pos / a.bs];
       slot = pos % a.bs;

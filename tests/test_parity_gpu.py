@@ -780,6 +780,43 @@ def test_append_16bit_restores_the_cache_bit_for_bit():
         assert np.array_equal(k2, case.k_cache) and np.array_equal(v2, case.v_cache), k
 
 
+def test_append_large_batches():
+    """Appends for batches whose token-to-sequence search takes one, two and
+    three 64-way rounds (40, 300 and 5000 sequences) restore a blanked f16
+    cache bit for bit; the u8 append of 300 sequences matches the oracle's
+    bit for bit."""
+    import speculative_decoding_verify_paged_amd as pav
+    from oracle_pins import _blank_new_tokens
+    rng = np.random.default_rng(47)
+    for k, n in enumerate((40, 300, 5000)):
+        Ls = [int(x) for x in rng.integers(0, 100, n)]
+        Ts = [int(x) for x in rng.integers(1, 5, n)]
+        case = pi.build_case([935, k], Ls, Ts, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                             block_size=16, q_dtype=pi.F16, kv_dtype=pi.F16, spare_blocks=1)
+        kn, vn, blank = _blank_new_tokens(case, rng)
+        k2, v2, _, _ = _append_gpu(blank, kn, vn, pi.F16)
+        assert pav.pa_verify_read_status() == pav.PA_OK
+        assert np.array_equal(k2, case.k_cache) and np.array_equal(v2, case.v_cache), n
+    Ls = [int(x) for x in rng.integers(0, 100, 300)]
+    Ts = [int(x) for x in rng.integers(1, 5, 300)]
+    case = pi.build_case([936], Ls, Ts, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                         block_size=16, q_dtype=pi.BF16, kv_dtype=pi.U8, spare_blocks=1)
+    shape = (case.num_tokens, case.num_kv_heads, case.head_dim)
+    kn = pi.f32_to_bits(rng.standard_normal(shape).astype(np.float32), pi.BF16)
+    vn = pi.f32_to_bits(rng.standard_normal(shape).astype(np.float32), pi.BF16)
+    st, k_ref, v_ref, ksz_ref, vsz_ref = oracle.get().kv_append(case, kn, vn, pi.BF16)
+    assert st == oracle.OK
+    k2, v2, ksz2, vsz2 = _append_gpu(case, kn, vn, pi.BF16)
+    assert pav.pa_verify_read_status() == pav.PA_OK
+    assert np.array_equal(k2, k_ref) and np.array_equal(v2, v_ref)
+    assert np.array_equal(ksz2, ksz_ref) and np.array_equal(vsz2, vsz_ref)
+    # subsequence_begins not starting at 0: the status is set
+    bad = pi.Case(**{f: getattr(case, f) for f in case.__dataclass_fields__})
+    bad.subsequence_begins = np.concatenate([[1], case.subsequence_begins[1:]]).astype(np.int32)
+    _append_gpu(bad, kn, vn, pi.BF16, max_query_len=4)
+    assert pav.pa_verify_read_status() == pav.PA_ERR_DEVICE_CONTRACT
+
+
 def test_append_u8_matches_the_oracle_bit_for_bit():
     rng = np.random.default_rng(42)
     for k, (qd, D, bs, Ls, Ts) in enumerate([(pi.F16, 256, 16, [32768], [3]),
