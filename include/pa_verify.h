@@ -203,6 +203,9 @@ typedef struct pa_verify_plan {
                                   output rows itself (no partials), and a check kernel that
                                   turns every row NaN if subsequence_begins is broken runs
                                   in the combine kernel's place */
+  int32_t small_groups;        /* for a direct call over short contexts (one row block, tiled
+                                  pages of >= 16 slots): the segment workgroups' wavefronts,
+                                  2 up to 16 steps, 4 up to 48 (more of them per CU); else 0 */
 } pa_verify_plan;
 
 /* Fill *plan for params p, host scalar max_context_len (>= max_s L_s + T_s)

@@ -63,7 +63,7 @@ class PaVerifyPlan(ctypes.Structure):
         ("grid", ctypes.c_int32 * 3),
         ("block_threads", ctypes.c_int32), ("combine_grid", ctypes.c_int32 * 3),
         ("combine_threads", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
-        ("direct", ctypes.c_int32),
+        ("direct", ctypes.c_int32), ("small_groups", ctypes.c_int32),
     ]
 
     def as_dict(self):

@@ -54,6 +54,7 @@ struct SegmentArgs {
   // ([num_tokens, Hq, D] in the q dtype) instead of partials
   int32_t direct;
   void* out;
+  int32_t small_groups;              // host dispatch only: 0, or the waves of the small-workgroup instance
 };
 
 struct AppendArgs {
@@ -163,6 +164,23 @@ constexpr SegConfig seg_config(int kv_dtype, int D, int rb, int bs = 16) {
   if (kv_dtype == kU8)
     return D >= 256 ? SegConfig{2, 1, 8, kHalfRingU8} : D >= 128 ? SegConfig{2, 1, 8} : SegConfig{4, 4};
   return D >= 256 ? SegConfig{1, 1} : D >= 128 ? SegConfig{2, 1, 8, 2} : SegConfig{4, 2, 8};
+}
+// One-segment calls over short contexts (every workgroup one short
+// sequence, most of an 8-wavefront workgroup idle): workgroups of 2 or 4
+// wavefronts at the same wavefronts per SIMD, so more of them are in
+// flight per CU.  One row block, tiled pages of 16 or more slots.  Same-box
+// A/B, graph-replayed us per call, 4096 sequences of 16..256 keys (at most
+// 9 steps) / 512 of 64..1024 (33 steps): 8 wavefronts 652 / 157.6, four 365
+// / 129.7, two 331 / 136.3, one 330 / 143.8.  Two up to kSmallSplitSteps
+// steps, four up to kSmallMaxSteps.
+constexpr int kSmallSplitSteps = 16;
+constexpr int kSmallMaxSteps = 48;
+constexpr int small_waves(int n_steps) {
+  return n_steps <= kSmallSplitSteps ? 2 : n_steps <= kSmallMaxSteps ? 4 : 0;
+}
+constexpr SegConfig seg_config_small(int kv_dtype, int D, int bs, int nw) {
+  const SegConfig c = seg_config(kv_dtype, D, 1, bs);
+  return SegConfig{c.waves_per_simd, 4 * c.waves_per_simd / nw, nw, c.half_ring};
 }
 constexpr int groups_per_cu(int kv_dtype, int D, int rb, int bs) {
   return seg_config(kv_dtype, D, rb, bs).groups_per_cu;

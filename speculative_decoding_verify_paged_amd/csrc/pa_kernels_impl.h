@@ -1602,9 +1602,9 @@ void pa_segment(SegmentArgs a) {
 // Launchers: one instance per (q dtype, cache dtype, D, block size, row
 // blocks); each pa_segment_*.hip instantiates one cache dtype.
 // ---------------------------------------------------------------------------
-template <int QT, int KV, int D, int BS, int RB, int PL>
+template <int QT, int KV, int D, int BS, int RB, int PL, int SMALL = 0>
 hipError_t launch_seg(const SegmentArgs& a, dim3 grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  constexpr SegConfig c = seg_config(KV, D, RB, BS);
+  constexpr SegConfig c = SMALL ? seg_config_small(KV, D, BS, SMALL) : seg_config(KV, D, RB, BS);
   static_assert(c.waves_per_group <= 4 * c.waves_per_simd, "a workgroup must fit on one CU");
   // the half-step path reads tiled pages only
   constexpr int HR = PL == kPagesTiled ? c.half_ring : 0;
@@ -1617,7 +1617,12 @@ template <int QT, int KV, int D, int BS, int PL>
 hipError_t dispatch_rb(const SegmentArgs& a, int rb, dim3 grid, hipStream_t st, hipEvent_t e0,
                        hipEvent_t e1) {
   switch (rb) {
-    case 1: return launch_seg<QT, KV, D, BS, 1, PL>(a, grid, st, e0, e1);
+    case 1:
+      if constexpr (BS >= 16 && PL == kPagesTiled) {
+        if (a.small_groups == 2) return launch_seg<QT, KV, D, BS, 1, PL, 2>(a, grid, st, e0, e1);
+        if (a.small_groups == 4) return launch_seg<QT, KV, D, BS, 1, PL, 4>(a, grid, st, e0, e1);
+      }
+      return launch_seg<QT, KV, D, BS, 1, PL>(a, grid, st, e0, e1);
     case 2:
       if constexpr (BS >= 16 && max_row_blocks(KV, D) >= 2) return launch_seg<QT, KV, D, BS, 2, PL>(a, grid, st, e0, e1);
       break;

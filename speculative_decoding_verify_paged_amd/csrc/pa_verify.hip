@@ -156,6 +156,13 @@ int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_ve
   // rows (no partials) and a check kernel of kFinishGroups workgroups
   // follows it in the combine's place.
   pl->direct = S == 1 ? 1 : 0;
+  // one-segment calls over short contexts: the small-workgroup instance
+  pl->small_groups = pl->direct && pl->row_blocks == 1 && bs >= 16 && p->page_layout == PA_PAGES_TILED
+                         ? pav::small_waves((int)n_steps) : 0;
+  if (pl->small_groups) {
+    pl->waves_per_group = pl->small_groups;
+    pl->block_threads = pl->small_groups * 64;
+  }
   pl->combine_grid[0] = pl->direct ? pav::kFinishGroups : (int32_t)(rows * pav::combine_slices(p->head_dim));
   pl->combine_grid[1] = 1;
   pl->combine_grid[2] = 1;
@@ -322,6 +329,7 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
   a.page_layout = p->page_layout;
   a.direct = pl.direct;
   a.out = out;
+  a.small_groups = pl.small_groups;
 
   hipStream_t st = static_cast<hipStream_t>(p->stream);
   hipEvent_t e0 = static_cast<hipEvent_t>(p->prof_event_begin);

@@ -307,8 +307,24 @@ def test_plan_direct_output_for_one_segment():
         assert pl["workspace_bytes"] == 256
         assert pl["combine_grid"] == [256, 1, 1] and pl["combine_threads"] == 256
     pl = plan(32771)
-    assert pl["num_segments"] > 1 and pl["direct"] == 0
+    assert pl["num_segments"] > 1 and pl["direct"] == 0 and pl["small_groups"] == 0
     assert pl["combine_grid"][0] == 3 * 32 * 2 and pl["combine_threads"] == 64
+
+
+def test_plan_small_groups_for_short_direct_batches():
+    big = dict(num_seqs=600, num_tokens=600, max_blocks_per_seq=200, num_blocks=600 * 200)
+    pl = plan(257, **big)                                   # 9 steps: 2-wavefront workgroups
+    assert pl["direct"] == 1 and pl["small_groups"] == 2
+    assert pl["waves_per_group"] == 2 and pl["block_threads"] == 128
+    assert plan(16 * 32, **big)["small_groups"] == 2
+    pl = plan(16 * 32 + 1, **big)                           # 17 steps: 4 wavefronts
+    assert pl["small_groups"] == 4 and pl["waves_per_group"] == 4 and pl["block_threads"] == 256
+    assert plan(48 * 32, **big)["small_groups"] == 4
+    assert plan(48 * 32 + 1, **big)["small_groups"] == 0      # 49 steps: the usual workgroups
+    assert plan(257, page_layout=pav.PA_PAGES_ROW_MAJOR, **big)["small_groups"] == 0
+    assert plan(257, block_size=8, **big)["small_groups"] == 0
+    pl = plan(257, max_query_len=8, **dict(big, num_tokens=1200))     # two row blocks
+    assert pl["row_blocks"] == 2 and pl["small_groups"] == 0
 
 
 def test_plan_window_and_forced_segments():

@@ -300,6 +300,11 @@ def _direct_batches():
         q_dtype=pi.BF16, kv_dtype=pi.BF16, name="direct_bs4")
     add(5, 400, 0, 250, 1, 4, num_q_heads=32, num_kv_heads=8, head_dim=64, block_size=16,
         q_dtype=pi.F16, kv_dtype=pi.F16, name="direct_d64")
+    # contexts of 17..48 steps: the 4-wavefront small-workgroup instance
+    add(7, 300, 0, 1200, 1, 4, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+        q_dtype=pi.F16, kv_dtype=pi.F16, name="direct_f16_up_to_38_steps")
+    add(8, 400, 0, 1000, 1, 3, num_q_heads=16, num_kv_heads=4, head_dim=256, block_size=32,
+        q_dtype=pi.BF16, kv_dtype=pi.U8, name="direct_u8_up_to_32_steps")
     out.append(pi.with_layout(out[0], pi.PAGES_ROW_MAJOR))
     return out
 
@@ -308,11 +313,16 @@ def test_direct_output_batches():
     """One segment per sequence (batches of hundreds of short sequences):
     the segment kernel writes the normalised rows itself and a check kernel
     runs in the combine's place; causal, sliding-window, u8, tree, two row
-    blocks, head_dim 64, 4-slot pages and row-major pages."""
+    blocks, head_dim 64, 4-slot pages and row-major pages, in 2- and
+    4-wavefront workgroups (contexts up to 16 and 48 steps) and the usual
+    ones."""
+    small = {}
     for case in _direct_batches():
         pl = plan_of(case)
         assert pl["direct"] == 1 and pl["num_segments"] == 1, (case.name, pl)
+        small[pl["small_groups"]] = small.get(pl["small_groups"], 0) + 1
         _full(case, rounding_aware=True)
+    assert set(small) == {0, 2, 4}, small           # both small-workgroup sizes and the usual
 
 
 def test_direct_output_contract_violations():
