@@ -133,11 +133,12 @@ __global__ __launch_bounds__(kFinishThreads) void pa_finish(CombineArgs a) {
   const int w = lane < a.seg.sb_words ? a.seg.sb_check[lane] : 0;
   if (!__any(w != 0)) return;                                 // uniform
   if (blockIdx.x == 0 && threadIdx.x == 0) atomicExch(a.seg.status, kDeviceContract);
-  const uint32_t nan2 = OUT == kF16 ? 0x7E007E00u : 0x7FC07FC0u;
-  const size_t n = (size_t)a.num_tokens * a.Hq * a.head_dim / 2;   // 32-bit words of out
-  uint32_t* out = reinterpret_cast<uint32_t*>(a.out);
+  // element stores: out need only be 2-byte aligned (an error path)
+  const uint16_t nan1 = OUT == kF16 ? 0x7E00u : 0x7FC0u;
+  const size_t n = (size_t)a.num_tokens * a.Hq * a.head_dim;
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    out[i] = nan2;
+    out[i] = nan1;
 }
 
 hipError_t launch_finish(const CombineArgs& a, int out_dtype, int threads, dim3 grid, hipStream_t st) {

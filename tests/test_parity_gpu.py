@@ -660,6 +660,35 @@ def test_misaligned_views_are_refused_and_out_is_untouched():
     assert max_err(got, oracle.forward(case)) <= tol(case)
 
 
+def test_out_at_two_byte_alignment():
+    """out need only be 2-byte aligned: a view 2 bytes past a 16-byte boundary
+    gets the aligned call's result bit for bit, for the combine kernel and
+    for direct one-segment calls (rows written by the segment kernel, NaN
+    rows of a violation, the check kernel's NaN fill), and the elements
+    around it stay untouched."""
+    import torch
+    import speculative_decoding_verify_paged_amd as pav
+    from gpu_util import to_device
+    direct = _direct_batches()[0]
+    bad_seq = pi.Case(**{f: getattr(direct, f) for f in direct.__dataclass_fields__})
+    bt = direct.block_tables.copy()
+    bt[5, 0] = direct.num_blocks + 1
+    bad_seq.block_tables = bt
+    bad_sb = pi.Case(**{f: getattr(direct, f) for f in direct.__dataclass_fields__})
+    bad_sb.subsequence_begins = np.concatenate([[1], direct.subsequence_begins[1:]]).astype(np.int32)
+    for case in (pi.config2(2048, 3, rep=5), direct, bad_seq, bad_sb):
+        dev = to_device(case)
+        q = dev["q"]
+        aligned = run_gpu(case, dev, max_query_len=4)
+        st = pav.pa_verify_read_status()
+        buf = torch.full((q.numel() + 2,), 5.0, dtype=q.dtype, device=q.device)
+        out = buf[1:-1].view(q.shape)                        # 2 bytes past a 16-byte boundary
+        run_gpu(case, dev, out=out, max_query_len=4)
+        assert pav.pa_verify_read_status() == st, case.name
+        assert np.array_equal(to_f64(out), to_f64(aligned), equal_nan=True), case.name
+        assert float(buf[0]) == 5.0 and float(buf[-1]) == 5.0, case.name
+
+
 # ---------------------------------------------------------------------------
 # More than 16 stacked rows (several 16-row MFMA blocks) and tree verify
 # ---------------------------------------------------------------------------
