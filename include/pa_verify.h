@@ -71,9 +71,9 @@
  *                [num_seqs] == num_tokens
  *
  * Alignment (the kernels use 16-byte vector accesses).  Forward calls: q,
- * k_cache, v_cache, k_scale_zp, v_scale_zp and the workspace 16-byte
- * aligned; out 2 bytes; block_tables, past_lens, subsequence_begins and
- * tree_mask 4 bytes.  Append calls: the new K/V rows, the caches and the
+ * out, k_cache, v_cache, k_scale_zp, v_scale_zp and the workspace 16-byte
+ * aligned; block_tables, past_lens, subsequence_begins and tree_mask 4
+ * bytes.  Append calls: the new K/V rows, the caches and the
  * scale/zero-point arrays 2 bytes (the u8 caches 1), the int32 arrays and the
  * workspace 4 bytes.  A misaligned pointer is PA_ERR_INVALID_ARG (a
  * misaligned workspace PA_ERR_WORKSPACE), returned before anything is

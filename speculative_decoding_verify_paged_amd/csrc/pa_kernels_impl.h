@@ -660,9 +660,6 @@ void pa_segment(SegmentArgs a) {
                                 : seq_info(a, s, ROWS);
   // Direct calls (one segment): output rows [t0, t1) x this KV head's q
   // heads become NaN (a sequence that breaks the contract, a row with no key)
-  // (out need only be 2-byte aligned: vector stores when it is 16-byte
-  // aligned, element stores otherwise)
-  const bool out16 = (reinterpret_cast<uintptr_t>(a.out) & 15) == 0;
   auto nan_rows = [&](int t0, int t1) {
     constexpr int V8 = D / 8;                                 // 16-byte pieces per row
     const uint16_t nan1 = QT == kF16 ? 0x7E00u : 0x7FC0u;
@@ -672,12 +669,7 @@ void pa_segment(SegmentArgs a) {
       const int y = x / V8;
       const size_t row = (size_t)(t0 + y / a.G) * a.Hq + h * a.G + y % a.G;
       uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + row * D + (x % V8) * 8;
-      if (out16) {
-        *reinterpret_cast<u32x4*>(dst) = nan8;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dst[e] = nan1;
-      }
+      *reinterpret_cast<u32x4*>(dst) = nan8;
     }
   };
   if (!si.ok) {
@@ -1580,12 +1572,7 @@ void pa_segment(SegmentArgs a) {
         }
       }
       uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((size_t)rt * a.Hq + rh) * D + c4;
-      if (out16) {
-        *reinterpret_cast<u32x2*>(dst) = packed;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[e] = (uint16_t)(packed[e / 2] >> (16 * (e % 2)));
-      }
+      *reinterpret_cast<u32x2*>(dst) = packed;
       continue;
     }
     if (M == -INFINITY) {                                     // no key of this row here

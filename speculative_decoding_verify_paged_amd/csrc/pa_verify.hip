@@ -269,7 +269,7 @@ int run(const void* q, const void* k, const void* v, const void* ksz, const void
   if (!q || !k || !v || !bt || !past_lens || !sb || !out) return PA_ERR_INVALID_ARG;
   if (u8_entry && (!ksz || !vsz)) return PA_ERR_INVALID_ARG;
   // the widths the kernels access these with
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 2) ||
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
       !aligned(bt, 4) || !aligned(past_lens, 4) || !aligned(sb, 4) || !aligned(p->tree_mask, 4))
     return PA_ERR_INVALID_ARG;
   if (u8_entry && (!aligned(ksz, 16) || !aligned(vsz, 16))) return PA_ERR_INVALID_ARG;

@@ -174,8 +174,9 @@ def test_misaligned_pointers_are_rejected_before_any_launch():
         args[k] = FAKE + off
         assert L.pa_verify_forward(*args, 32771, 0.1, FAKE, ctypes.byref(params())) \
             == pav.PA_ERR_INVALID_ARG, k
-    assert L.pa_verify_forward(*[FAKE] * 6, 32771, 0.1, FAKE + 1, ctypes.byref(params())) \
-        == pav.PA_ERR_INVALID_ARG                                          # out: 2 B
+    for off in (2, 8):                                                 # out: 16 B
+        assert L.pa_verify_forward(*[FAKE] * 6, 32771, 0.1, FAKE + off, ctypes.byref(params())) \
+            == pav.PA_ERR_INVALID_ARG, off
     assert call(params(tree_mask=FAKE + 2)) == pav.PA_ERR_INVALID_ARG
     assert call(params(workspace=FAKE + 8, workspace_bytes=1 << 30)) == pav.PA_ERR_WORKSPACE
     u8 = ctypes.byref(params(kv_dtype=pav.PA_U8, head_dim=256, num_q_heads=16, num_kv_heads=4))

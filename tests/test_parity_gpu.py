@@ -305,6 +305,9 @@ def _direct_batches():
         q_dtype=pi.F16, kv_dtype=pi.F16, name="direct_f16_up_to_38_steps")
     add(8, 400, 0, 1000, 1, 3, num_q_heads=16, num_kv_heads=4, head_dim=256, block_size=32,
         q_dtype=pi.BF16, kv_dtype=pi.U8, name="direct_u8_up_to_32_steps")
+    # 8 sequences of at most 32 keys: a work-list batch with one segment
+    add(9, 8, 0, 29, 1, 4, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+        q_dtype=pi.BF16, kv_dtype=pi.BF16, name="direct_work_list_8_short")
     out.append(pi.with_layout(out[0], pi.PAGES_ROW_MAJOR))
     return out
 
@@ -316,13 +319,15 @@ def test_direct_output_batches():
     blocks, head_dim 64, 4-slot pages and row-major pages, in 2- and
     4-wavefront workgroups (contexts up to 16 and 48 steps) and the usual
     ones."""
-    small = {}
+    small, worklist = {}, 0
     for case in _direct_batches():
         pl = plan_of(case)
         assert pl["direct"] == 1 and pl["num_segments"] == 1, (case.name, pl)
         small[pl["small_groups"]] = small.get(pl["small_groups"], 0) + 1
+        worklist += pl["worklist"]
         _full(case, rounding_aware=True)
     assert set(small) == {0, 2, 4}, small           # both small-workgroup sizes and the usual
+    assert worklist == 1
 
 
 def test_direct_output_contract_violations():
@@ -660,33 +665,27 @@ def test_misaligned_views_are_refused_and_out_is_untouched():
     assert max_err(got, oracle.forward(case)) <= tol(case)
 
 
-def test_out_at_two_byte_alignment():
-    """out need only be 2-byte aligned: a view 2 bytes past a 16-byte boundary
-    gets the aligned call's result bit for bit, for the combine kernel and
-    for direct one-segment calls (rows written by the segment kernel, NaN
-    rows of a violation, the check kernel's NaN fill), and the elements
-    around it stay untouched."""
+def test_misaligned_out_is_refused():
+    """out must be 16-byte aligned like q (the segment kernel of a
+    one-segment call writes the rows with vector stores): a view 2 or 8
+    bytes past a 16-byte boundary is refused before anything runs, for the
+    combine and the direct path, and the memory stays untouched."""
     import torch
     import speculative_decoding_verify_paged_amd as pav
     from gpu_util import to_device
-    direct = _direct_batches()[0]
-    bad_seq = pi.Case(**{f: getattr(direct, f) for f in direct.__dataclass_fields__})
-    bt = direct.block_tables.copy()
-    bt[5, 0] = direct.num_blocks + 1
-    bad_seq.block_tables = bt
-    bad_sb = pi.Case(**{f: getattr(direct, f) for f in direct.__dataclass_fields__})
-    bad_sb.subsequence_begins = np.concatenate([[1], direct.subsequence_begins[1:]]).astype(np.int32)
-    for case in (pi.config2(2048, 3, rep=5), direct, bad_seq, bad_sb):
+    for case in (pi.config2(2048, 3, rep=5), _direct_batches()[0]):
         dev = to_device(case)
         q = dev["q"]
-        aligned = run_gpu(case, dev, max_query_len=4)
-        st = pav.pa_verify_read_status()
-        buf = torch.full((q.numel() + 2,), 5.0, dtype=q.dtype, device=q.device)
-        out = buf[1:-1].view(q.shape)                        # 2 bytes past a 16-byte boundary
-        run_gpu(case, dev, out=out, max_query_len=4)
-        assert pav.pa_verify_read_status() == st, case.name
-        assert np.array_equal(to_f64(out), to_f64(aligned), equal_nan=True), case.name
-        assert float(buf[0]) == 5.0 and float(buf[-1]) == 5.0, case.name
+        for off in (1, 4):                                   # elements: 2 and 8 bytes
+            buf = torch.full((q.numel() + 8,), 5.0, dtype=q.dtype, device=q.device)
+            out = buf[off:off + q.numel()].view(q.shape)
+            with pytest.raises(pav.PaVerifyError) as e:
+                run_gpu(case, dev, out=out, max_query_len=4)
+            assert e.value.code == pav.PA_ERR_INVALID_ARG
+            torch.cuda.synchronize()
+            assert bool(torch.all(buf == 5.0)), (case.name, off)
+        got = to_f64(run_gpu(case, dev, max_query_len=4))  # an aligned out still runs
+        assert excess(case, got, oracle.forward(case)) <= 0.0
 
 
 # ---------------------------------------------------------------------------

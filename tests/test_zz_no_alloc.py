@@ -25,10 +25,13 @@ def test_noalloc_matches_the_workspace_call_on_calls_in_a_row():
     entry point, so the outputs agree bit for bit."""
     import torch
     import speculative_decoding_verify_paged_amd as pav
+    # the last, a batch of 300 short sequences, is a one-segment call (direct
+    # output, only the scratch's header)
     cases = [pi.config5(rep=3, lo=100, hi=20000, poison=True),
              pi.config2(32768, 4, rep=3),
              pi.config4(3000, window=1024, rep=2, poison=True),
-             pi.config2(2048, 1, rep=4)]
+             pi.config2(2048, 1, rep=4),
+             pi.config5(rep=4, num_seqs=300, lo=8, hi=200, spare_blocks=4)]
     sizes = []
     for case in cases:
         dev = to_device(case)
