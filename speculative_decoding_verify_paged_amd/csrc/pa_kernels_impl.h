@@ -3,16 +3,19 @@
 //
 // Two kernels per call:
 //   1. pa_segment: one workgroup per (KV segment j, KV head, sequence) — for
-//      a batch of several sequences, per (work-list chunk, KV head), a chunk
-//      being a run of one sequence's steps whose size the device picks from
-//      the lengths so the chunks fill one round of workgroups.  Its
-//      wavefronts stream the segment's K/V page tiles straight from HBM into
-//      MFMA operand registers, each tile read once for all G*T stacked query
-//      rows of the GQA group, and keep an online softmax.  The workgroup
-//      merges its wavefronts in LDS and writes one partial (O, m, l) per query
-//      row to the workspace, indexed per token.
+//      a small batch (2..256 sequences, no more than the workgroup slots per
+//      KV head), per (work-list chunk, KV head), a chunk being a run of one
+//      sequence's steps whose size the device picks from the lengths so the
+//      chunks fill one round of workgroups.  Its wavefronts stream the
+//      segment's K/V page tiles straight from HBM into MFMA operand
+//      registers, each tile read once for all G*T stacked query rows of the
+//      GQA group, and keep an online softmax.  The workgroup merges its
+//      wavefronts in LDS and writes one partial (O, m, l) per query row to
+//      the workspace, indexed per token — or, with one segment, the
+//      normalised output row itself.
 //   2. pa_combine: log-sum-exp merge of the segment partials of each
-//      (token, q head) row, cast to the output dtype.
+//      (token, q head) row, cast to the output dtype (pa_finish instead for
+//      one segment: only the check of subsequence_begins).
 //
 // Why segments: a verify call at batch 1 has only num_kv_heads independent
 // KV streams; a kernel that gives each one workgroup idles almost all of the
@@ -32,7 +35,10 @@
 //   V: [d/32][(slot%16)/4][d%16][(d%32)/16][slot%4]
 //                                               (u8: [d/64][(slot%16)/4][d%16][(d%64)/16][slot%4])
 // Pages of 1, 2, 4 or 8 slots hold K row-major [slot][d] and V d-major
-// [d][slot]; each lane gathers its own operand pieces from them.
+// [d][slot]; each lane gathers its own operand pieces from them.  With
+// page_layout = kPagesRowMajor every page is [slot][d] for K and V; the
+// wavefronts read whole page rows and reorder them into operand order
+// through LDS.
 //
 // Data path of one wavefront step (32 keys = two sub-tiles, stacked rows
 // r = g*T + i padded to 16):
@@ -43,8 +49,10 @@
 //                                           A = half of each sub-tile's V load,
 //                                           B = the S^T accumulators after exp
 //                                           (bf16: hi + lo parts)
-// Every lane owns one stacked row r = lane % 16 in all three products, so the
-// softmax state and its rescale never leave the lane.
+// The half-step path takes one sub-tile (16 keys) at a time, PV as
+// v_mfma_f32_16x16x16 over its keys.  Every lane owns one stacked row
+// r = lane % 16 in all three products, so the softmax state and its rescale
+// never leave the lane.
 #pragma once
 
 #include <hip/hip_ext.h>
@@ -613,10 +621,10 @@ void pa_segment(SegmentArgs a) {
     const bool wave_bad = __any(bad);
     if (lane == 0) a.sb_check[wave] = wave_bad ? 1 : 0;
   }
-  // Fixed segments (one sequence): grid (Hkv, num_seqs, S) with segment
-  // j = S - 1 - blockIdx.z.  Work-list mode (a batch of several sequences):
-  // grid (Hkv, 1, chunks), the sequence and steps of chunk blockIdx.z taken
-  // from the work list.
+  // Fixed segments (one sequence, or a batch of more sequences than the
+  // work list takes): grid (Hkv, num_seqs, S) with segment j = S - 1 -
+  // blockIdx.z.  Work-list mode (a small batch): grid (Hkv, 1, chunks), the
+  // sequence and steps of chunk blockIdx.z taken from the work list.
   const int h = blockIdx.x;
   int s, j, st_begin, st_cap, wl_items = 0;
   WlHit wl_hit{};
