@@ -148,12 +148,13 @@ class Runner:
         """µs per call with the `steps` calls captured in one HIP graph and
         replayed: device time per call, host launch overhead excluded (a
         serving engine replays the verify forward from a graph).  Each timed
-        replay is enqueued right behind an untimed replay of a second graph of
-        the same calls, so the timed calls start on a busy GPU.  A timed
-        replay still carries a fixed cost of its own on the device (~19 us
-        on MI355X: the timing events and the graph's start and end), which
-        adds ~0.9 us per call at steps = 20 and ~0.1 us at the default 200.
-        Median and all values over `repeats` replays."""
+        replay is enqueued right behind untimed replays of a second graph of
+        the same calls, at least ~100 calls of them, so the timed calls start
+        on a busy GPU and the host has enqueued them before it idles.  A
+        timed replay still carries a fixed cost of its own on the device
+        (~7 us on MI355X: the timing events and the graph's start and end),
+        ~0.35 us per call at steps = 20.  Median and all values over
+        `repeats` replays."""
         import torch
         for i in range(warmup):
             self.call(i)
@@ -172,9 +173,11 @@ class Runner:
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         per_call = []
+        lead = -(-100 // steps)                         # untimed replays ahead of the timed one
         for r in range(repeats):
             torch.cuda.synchronize()
-            g_lead.replay()                             # untimed, keeps the GPU busy
+            for _ in range(lead):
+                g_lead.replay()                         # untimed, keeps the GPU busy
             t0.record()
             g.replay()
             t1.record()
@@ -217,7 +220,7 @@ class Runner:
 def time_append(case, steps, warmup, repeats):
     """µs per pa_kv_append(_u8) call writing the case's T new tokens (values
     drawn once, stored in the q dtype), graph-replayed like the forward (the
-    timed replay right behind an untimed one)."""
+    timed replay right behind untimed ones)."""
     import numpy as np
     import torch
     import speculative_decoding_verify_paged_amd as pav
@@ -253,9 +256,11 @@ def time_append(case, steps, warmup, repeats):
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     per = []
+    lead = -(-100 // steps)
     for _ in range(repeats):
         torch.cuda.synchronize()
-        g_lead.replay()                                 # untimed, keeps the GPU busy
+        for _ in range(lead):
+            g_lead.replay()                             # untimed, keeps the GPU busy
         e0.record()
         g.replay()
         e1.record()
