@@ -62,7 +62,7 @@
  *                Measured on MI355X, us per call tiled vs row-major: 32k
  *                context, 32 q / 8 KV heads, head_dim 128, f16: 26.2 vs 27.8;
  *                bf16 head_dim 256 (16 KV heads): 84.8 vs 102.9; ragged bf16
- *                batch: 64.1 vs 69.3; u8 head_dim 256: 20.8 vs 51.3.
+ *                batch: 64.1 vs 69.3; u8 head_dim 256: 20.7 vs 26.7.
  *  k_scale_zp,   [num_blocks, Hkv, block_size, 2]     f16 (scale, zero_point) per
  *  v_scale_zp    token per KV head, u8 variant only; dequant = (u - zp) * scale
  *  block_tables  [num_seqs, max_blocks_per_seq] int32 physical block ids

@@ -154,7 +154,7 @@ struct SegConfig {
 // 16-bit head_dim 128, ragged batch 64.19 -> 63.85, 32k 26.20 -> 26.13.  Not
 // at 16-bit head_dim 256 (window layer 8.63 -> 10.12, global 83.98 -> 84.69)
 // or head_dim 64 (16.54 -> 17.05).
-constexpr SegConfig seg_config(int kv_dtype, int D, int rb, int bs = 16) {
+constexpr SegConfig seg_config_tiled(int kv_dtype, int D, int rb, int bs) {
   // Pages of fewer than 16 slots: one 8-wavefront workgroup per CU as for
   // 16-slot pages (32 q / 8 KV heads, head_dim 128, T = 3 at 32k, us per
   // call: 2 slots 29.8 vs 29.9 for two
@@ -178,12 +178,19 @@ constexpr int kSmallMaxSteps = 48;
 constexpr int small_waves(int n_steps) {
   return n_steps <= kSmallSplitSteps ? 2 : n_steps <= kSmallMaxSteps ? 4 : 0;
 }
+// Row-major pages stage every step through LDS on the full-step path; at
+// u8 head_dim 256 that path at two wavefronts per SIMD spills 368-484 B per
+// lane, so there it runs one wavefront per SIMD with the whole register file.
+constexpr SegConfig seg_config(int kv_dtype, int D, int rb, int bs = 16, int pl = kPagesTiled) {
+  return pl == kPagesRowMajor && kv_dtype == kU8 && D >= 256 && bs >= 16 ? SegConfig{1, 1}
+                                                                         : seg_config_tiled(kv_dtype, D, rb, bs);
+}
 constexpr SegConfig seg_config_small(int kv_dtype, int D, int bs, int nw) {
   const SegConfig c = seg_config(kv_dtype, D, 1, bs);
   return SegConfig{c.waves_per_simd, 4 * c.waves_per_simd / nw, nw, c.half_ring};
 }
-constexpr int groups_per_cu(int kv_dtype, int D, int rb, int bs) {
-  return seg_config(kv_dtype, D, rb, bs).groups_per_cu;
+constexpr int groups_per_cu(int kv_dtype, int D, int rb, int bs, int pl = kPagesTiled) {
+  return seg_config(kv_dtype, D, rb, bs, pl).groups_per_cu;
 }
 // Row blocks built per (cache dtype, head_dim): each adds D/4 accumulator
 // and D/8 query registers per lane and 16 * (D + 4) * 16 B of LDS; these are

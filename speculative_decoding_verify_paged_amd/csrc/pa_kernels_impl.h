@@ -1615,7 +1615,7 @@ void pa_segment(SegmentArgs a) {
 // ---------------------------------------------------------------------------
 template <int QT, int KV, int D, int BS, int RB, int PL, int SMALL = 0>
 hipError_t launch_seg(const SegmentArgs& a, dim3 grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  constexpr SegConfig c = SMALL ? seg_config_small(KV, D, BS, SMALL) : seg_config(KV, D, RB, BS);
+  constexpr SegConfig c = SMALL ? seg_config_small(KV, D, BS, SMALL) : seg_config(KV, D, RB, BS, PL);
   static_assert(c.waves_per_group <= 4 * c.waves_per_simd, "a workgroup must fit on one CU");
   // the half-step path reads tiled pages only
   constexpr int HR = PL == kPagesTiled ? c.half_ring : 0;

@@ -107,7 +107,8 @@ int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_ve
     // batch 1, and in a ragged batch the longest sequence is not left to a
     // few CUs), but at most kMaxRounds rounds of workgroups in all.
     const int64_t groups =
-        (int64_t)num_cus * pav::groups_per_cu(p->kv_dtype, p->head_dim, row_blocks(p), p->block_size);
+        (int64_t)num_cus * pav::groups_per_cu(p->kv_dtype, p->head_dim, row_blocks(p), p->block_size,
+                                              p->page_layout);
     const int64_t pairs = (int64_t)p->num_kv_heads * p->num_seqs;
     S = cdiv(groups, p->num_kv_heads);
     S = std::min(S, std::max<int64_t>(cdiv(groups, pairs), kMaxRounds * groups / pairs));
@@ -121,7 +122,8 @@ int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_ve
   pl->row_blocks = row_blocks(p);
   pl->keys_per_step = kKeysPerStep;
   pl->span = (int32_t)span;
-  const int nw = pav::seg_config(p->kv_dtype, p->head_dim, pl->row_blocks, p->block_size).waves_per_group;
+  const int nw = pav::seg_config(p->kv_dtype, p->head_dim, pl->row_blocks, p->block_size, p->page_layout)
+                     .waves_per_group;
   pl->waves_per_group = nw;
   pl->max_steps_per_segment = (int32_t)max_sps;
   pl->grid[0] = p->num_kv_heads;
@@ -129,7 +131,7 @@ int make_plan(const pa_verify_params* p, int32_t max_ctx, int32_t num_cus, pa_ve
   pl->grid[2] = (int32_t)S;
   pl->target_items = (int32_t)std::max<int64_t>(
       1, cdiv((int64_t)num_cus * pav::groups_per_cu(p->kv_dtype, p->head_dim, pl->row_blocks,
-                                                    p->block_size), p->num_kv_heads));
+                                                    p->block_size, p->page_layout), p->num_kv_heads));
   // The work list pays where a few sequences of unequal length must share
   // the GPU.  Every sequence has at least one chunk, so with more sequences
   // than target_items the device's chunk size would be the longest
