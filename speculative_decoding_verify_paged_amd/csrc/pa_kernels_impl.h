@@ -370,9 +370,9 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // table holds) whose chunks of all sequences fit the target count of
 // workgroups per KV head, so one round of equal workgroups covers the batch
 // however its lengths are spread.  A sequence that breaks the contract gets
-// one chunk (it writes NaN partials).  Every wavefront of every workgroup
-// loads the batch's metadata once into registers (lane-strided, one request
-// per array) and computes the same C from them.  Wave-wide.
+// one chunk (it writes NaN partials).  Wavefront 0 of every workgroup loads
+// the batch's metadata once into registers (lane-strided, one request per
+// array) and computes C and the workgroup's chunk from them.  Wave-wide.
 // ---------------------------------------------------------------------------
 struct WorkList {
   int code[kWlCached];                 // steps; -1 breaks the contract; -2 past the batch
@@ -636,9 +636,27 @@ void pa_segment(SegmentArgs a) {
     st_begin = (int)(((int64_t)j * a.n_steps) / a.S);
     st_cap = (int)(((int64_t)(j + 1) * a.n_steps) / a.S);
   } else {
-    const WorkList wl = wl_load(a, ROWS);
-    const int C = wl_chunk(a, wl);
-    wl_hit = wl_find(C, (int)blockIdx.z, wl);
+    // wavefront 0 alone searches (its SIMD partner waits at the barrier
+    // instead of competing for issue slots with the same work) and hands
+    // the chunk to the others through LDS
+    __shared__ int s_wl[7];
+    if (wave == 0) {
+      const WorkList wl = wl_load(a, ROWS);
+      const int C = wl_chunk(a, wl);
+      const WlHit hit = wl_find(C, (int)blockIdx.z, wl);
+      if (lane == 0) {
+        s_wl[0] = hit.seq;
+        s_wl[1] = hit.chunk;
+        s_wl[2] = hit.items;
+        s_wl[3] = hit.b0;
+        s_wl[4] = hit.b1;
+        s_wl[5] = hit.L;
+        s_wl[6] = C;
+      }
+    }
+    __syncthreads();
+    wl_hit = WlHit{s_wl[0], s_wl[1], s_wl[2], s_wl[3], s_wl[4], s_wl[5]};
+    const int C = s_wl[6];
     s = wl_hit.seq;
     if (s < 0) return;                                        // past the last chunk (uniform)
     j = wl_hit.chunk;
