@@ -507,7 +507,6 @@ struct WlHit {
   int seq, chunk, items, b0, b1, L;
 };
 __device__ __forceinline__ WlHit wl_find(int C, int item, const WorkList& w) {
-  const int lane = threadIdx.x & (kWave - 1);
   const float rc = __builtin_amdgcn_rcpf((float)C);
   WlHit h{-1, 0, 0, 0, 0, 0};
   int base = 0;
